@@ -1,0 +1,165 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) routed, block-quantized MoE expert layer.
+ *
+ * The layer, as the pages describe it:
+ *   [LR] "QwenのMoEルーターを観測してホットエキスパートを先読みしても速くならなかった"
+ *        (lilting.ch). Section "ルーターをフックする" (hooking the router): the router
+ *        is a gate linear, a precise softmax and a top-k. Section
+ *        "事前ウォームアップとmmapキャッシュを比べる": expert weights are one stacked
+ *        (experts, output_dims, input_dims) array, and gather_qmm multiplies by
+ *        the experts named in rhs_indices.
+ *   [QK] "鳴かぬなら、カスタムカーネル、ほととぎす" (qiita.com, john-rocky).
+ *        Section 1: an MoE token runs only its top-k experts, so decode should
+ *        read only those experts' weights. Section 4: the routed expert ids are
+ *        a kernel input and index the weight reads, so unrouted experts are never
+ *        fetched. Section 6: weights are symmetric linear int8 with one scale per
+ *        32 K elements ("sym8"). Section 7: gate and up share the token, while
+ *        the down projection of each slot takes that expert's own gated
+ *        activation.
+ *
+ * Conventions, common to every entry point:
+ *   - Array arguments are DEVICE pointers to memory the caller owns. The library
+ *     keeps no pointer after a call returns. The moe_experts struct itself is
+ *     read on the host, during the call only.
+ *   - Every call is asynchronous on `stream`, a hipStream_t passed as void*
+ *     (NULL means the default stream). No call synchronises, allocates device
+ *     memory or copies device data to the host.
+ *   - Arguments are checked on the host before any launch. A failed check
+ *     returns an error and launches nothing. moe_last_error() then describes it,
+ *     per calling thread.
+ *   - Scratch memory comes from the caller: `ws` must hold at least
+ *     moe_workspace_bytes(...) bytes, aligned to 256 bytes. Calls that share a
+ *     workspace must be ordered, for example on one stream.
+ *   - Layouts are row-major and C-contiguous. Device arrays must be 16-byte
+ *     aligned.
+ *   - Codes: sym8 stores one int8 two's-complement code per byte, in K order.
+ *     int4 stores two codes per byte: the even K index in the low nibble, the
+ *     odd one in the high nibble, each a two's-complement nibble in [-7, 7].
+ *     Scales are IEEE binary16 bit patterns, one per 32 consecutive K elements
+ *     of a row. A weight is code * scale.
+ *   - Limits: 1 <= T <= 65536; 32 <= H <= 4096 and 32 <= I <= 4096, both
+ *     multiples of 32; 1 <= E <= 1024; 1 <= k <= min(E, 16).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null pointer, a shape outside the limits, misalignment */
+  MOE_ERR_UNSUPPORTED = 2,  /* unknown dtype, codec or flag */
+  MOE_ERR_WORKSPACE = 3,    /* ws too small, or not 256-byte aligned */
+  MOE_ERR_HIP = 4           /* a HIP launch failed; moe_last_error() names it */
+} moe_status;
+
+/* Activation element type of x. */
+typedef enum { MOE_F32 = 0, MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
+
+/* Weight codec [QK §6, §3/§7]: sym8 codes lie in [-127, 127], int4 codes in [-7, 7]. */
+typedef enum { MOE_Q_SYM8 = 0, MOE_Q_INT4 = 1 } moe_qscheme;
+
+enum {
+  /* Renormalise the k gates of each token so they sum to one. */
+  MOE_FLAG_RENORM = 1u,
+  /* Expert-path selection; with neither bit set the library chooses.
+   * GATHER: gathered matvec kernels. GEMM: grouped MFMA GEMM (x bf16/f16 only). */
+  MOE_FLAG_PATH_GATHER = 2u,
+  MOE_FLAG_PATH_GEMM = 4u
+};
+
+/* Stacked experts [LR "事前ウォームアップとmmapキャッシュを比べる"]:
+ *   w_gate_up: [E][2I][H] codes (int4: [E][2I][H/2] bytes). Rows 0..I-1 of an
+ *              expert are the gate projection and rows I..2I-1 the up projection.
+ *   s_gate_up: [E][2I][H/32] binary16 scales.
+ *   w_down:    [E][H][I] codes (int4: [E][H][I/2] bytes).
+ *   s_down:    [E][H][I/32] binary16 scales.                                  */
+typedef struct moe_experts {
+  int32_t E, H, I;
+  int32_t scheme;           /* moe_qscheme */
+  const void* w_gate_up;
+  const uint16_t* s_gate_up;
+  const void* w_down;
+  const uint16_t* s_down;
+} moe_experts;
+
+/* Bytes of workspace that moe_route, moe_gather_qmm_forward and
+ * moe_layer_forward need for these sizes, with any flags. Returns 0 when the
+ * sizes are outside the limits. */
+size_t moe_workspace_bytes(int32_t T, int32_t E, int32_t H, int32_t I, int32_t k, int32_t scheme);
+
+/* Router [LR "ルーターをフックする"]: logits = x R^T in fp32, a softmax over the E
+ * experts and the top k.
+ *   x:         [T][H] activations of type xtype.
+ *   router_w:  [E][H] fp32.
+ *   topk_idx:  out [T][k] int32. Expert ids by descending logit, ties to the
+ *              lower id.
+ *   topk_gate: out [T][k] fp32. Softmax probability of each chosen expert,
+ *              divided by their sum when flags has MOE_FLAG_RENORM. */
+moe_status moe_route(const void* x, int32_t xtype, int32_t T, int32_t H, const float* router_w,
+                     int32_t E, int32_t k, uint32_t flags, int32_t* topk_idx, float* topk_gate,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Token-by-expert grouping of the T*k assignments f = t*k + s of topk_idx.
+ * This is the step that lets a batch read each routed expert once.
+ *   counts:  out [E]     assignments per expert.
+ *   offsets: out [E+1]   exclusive prefix sum of counts.
+ *   perm:    out [T*k]   flat ids ordered by expert, then by f.
+ *   uniq:    out [E]     experts with counts > 0, ascending. Entries past
+ *                        *n_uniq are unspecified.
+ *   n_uniq:  out [1]     number of such experts.
+ * topk_idx entries must lie in [0, E); the caller guarantees this. No workspace
+ * is needed beyond `ws` of moe_workspace_bytes(T, E, 32, 32, k, 0) bytes. */
+moe_status moe_group(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int32_t* uniq, int32_t* n_uniq,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Gathered quantized expert layer, the routed-only gather_qmm [QK §4, §7;
+ * LR "事前ウォームアップとmmapキャッシュを比べる"]. For each token t and slot s,
+ * with e = topk_idx[t][s]:
+ *   u = W_gu[e] x_t (2I values); h = silu(u[0:I]) * u[I:2I], where
+ *   silu(z) = z / (1 + exp(-z)); ys = W_d[e] h.
+ * Only the weights of experts named in topk_idx are read.
+ *   topk_gate: [T][k] fp32. With it, y is [T][H] = sum_s gate[t][s] * ys, in
+ *              slot order. With topk_gate == NULL, y is [T][k][H], the per-slot ys.
+ *   topk_idx:  entries must lie in [0, E). The caller guarantees this; it is
+ *              not checked on the device.
+ *   flags:     MOE_FLAG_PATH_* bits select the path; other bits are ignored. */
+moe_status moe_gather_qmm_forward(const void* x, int32_t xtype, int32_t T, const moe_experts* ex,
+                                  int32_t k, const int32_t* topk_idx, const float* topk_gate,
+                                  float* y, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/* Whole expert layer: moe_route, then moe_gather_qmm_forward on its output.
+ *   y:             out [T][H] fp32.
+ *   topk_idx_out:  out [T][k], or NULL.
+ *   topk_gate_out: out [T][k], or NULL.                                        */
+moe_status moe_layer_forward(const void* x, int32_t xtype, int32_t T, const float* router_w,
+                             const moe_experts* ex, int32_t k, uint32_t flags, float* y,
+                             int32_t* topk_idx_out, float* topk_gate_out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Block quantiser for the codecs above [QK §6]: w [rows][K] fp32 to codes and
+ * scales. Per block of 32: s = binary16(amax / qmax), with the division in
+ * fp32, rounded to nearest even and saturated at the largest finite value;
+ * then q = clamp(rint(w / s), -qmax, qmax) in fp32, or q = 0 when s == 0.
+ *   codes:  out [rows][K] (sym8) or [rows][K/2] (int4) bytes.
+ *   scales: out [rows][K/32] binary16.
+ * K must be a positive multiple of 32. Non-finite inputs give unspecified codes. */
+moe_status moe_quantize(const float* w, int64_t rows, int32_t K, int32_t scheme, void* codes,
+                        uint16_t* scales, void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_str(moe_status s);
+
+/* Detail of the last error returned to the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

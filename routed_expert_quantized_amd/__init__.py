@@ -1,0 +1,246 @@
+"""Python binding of libmoe.so, the MI355X (gfx950) routed block-quantized MoE layer.
+
+This module only marshals arguments: it turns torch device tensors into
+pointers, allocates outputs and workspace through torch, and calls the C ABI
+declared in include/moe.h. Every step of the layer runs in the library's HIP
+kernels. There is no fallback: if libmoe.so is missing or the GPU is absent,
+the calls raise.
+
+Entry points mirror the C names: moe_route, moe_group, moe_gather_qmm_forward,
+moe_layer_forward, moe_quantize, moe_workspace_bytes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_F16, MOE_BF16 = 0, 1, 2
+MOE_Q_SYM8, MOE_Q_INT4 = 0, 1
+MOE_FLAG_RENORM, MOE_FLAG_PATH_GATHER, MOE_FLAG_PATH_GEMM = 1, 2, 4
+
+# Every function the header declares; the library must export all of them.
+EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_group", "moe_gather_qmm_forward", "moe_layer_forward",
+           "moe_quantize", "moe_status_str", "moe_last_error")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed: status {status} ({detail})")
+        self.status = status
+
+
+class _Experts(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("scheme", ctypes.c_int32),
+                ("w_gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (built in-tree by routed_expert_quantized_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m routed_expert_quantized_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, U32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+        E = ctypes.POINTER(_Experts)
+        sigs = {
+            "moe_workspace_bytes": ([I32, I32, I32, I32, I32, I32], SZ),
+            "moe_route": ([P, I32, I32, I32, P, I32, I32, U32, P, P, P, SZ, P], ctypes.c_int),
+            "moe_group": ([P, I32, I32, I32, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+            "moe_gather_qmm_forward": ([P, I32, I32, E, I32, P, P, P, U32, P, SZ, P], ctypes.c_int),
+            "moe_layer_forward": ([P, I32, I32, P, E, I32, U32, P, P, P, P, SZ, P], ctypes.c_int),
+            "moe_quantize": ([P, I64, I32, I32, P, P, P], ctypes.c_int),
+            "moe_status_str": ([ctypes.c_int], ctypes.c_char_p),
+            "moe_last_error": ([], ctypes.c_char_p),
+        }
+        for name, (args, res) in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(fn, status, lib().moe_last_error().decode())
+
+
+def _xtype(x: torch.Tensor) -> int:
+    return {torch.float32: MOE_F32, torch.float16: MOE_F16, torch.bfloat16: MOE_BF16}[x.dtype]
+
+
+def _p(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _device_tensor(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class Experts:
+    """Packed experts on the device (layout in include/moe.h).
+
+    w_gate_up uint8 [E][2I][H] (int4: [E][2I][H/2]); s_gate_up int16/uint16 bits [E][2I][H/32];
+    w_down uint8 [E][H][I] (int4: [E][H][I/2]); s_down [E][H][I/32]."""
+    E: int
+    H: int
+    I: int
+    scheme: int
+    w_gate_up: torch.Tensor
+    s_gate_up: torch.Tensor
+    w_down: torch.Tensor
+    s_down: torch.Tensor
+
+    def c(self) -> _Experts:
+        for n in ("w_gate_up", "s_gate_up", "w_down", "s_down"):
+            _device_tensor(getattr(self, n), n)
+        return _Experts(self.E, self.H, self.I, self.scheme, self.w_gate_up.data_ptr(), self.s_gate_up.data_ptr(),
+                        self.w_down.data_ptr(), self.s_down.data_ptr())
+
+    @property
+    def expert_bytes(self) -> int:
+        """Bytes of one expert's codes and scales."""
+        cpb = 32 if self.scheme == MOE_Q_SYM8 else 16
+        return 3 * self.H * self.I // 32 * (cpb + 2)
+
+
+class Workspace:
+    """A growable 256-byte-aligned device scratch buffer (torch caching allocator)."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes + 256:
+            self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        off = (-self.buf.data_ptr()) % 256
+        return self.buf[off:off + max(nbytes, 1)]
+
+
+_default_ws: dict = {}
+
+
+def _ws(ws: Workspace | None, nbytes: int, device) -> torch.Tensor:
+    if ws is None:
+        key = str(device)
+        ws = _default_ws.setdefault(key, Workspace(device))
+    return ws.get(nbytes)
+
+
+def moe_workspace_bytes(T: int, E: int, H: int, I: int, k: int, scheme: int) -> int:
+    return int(lib().moe_workspace_bytes(T, E, H, I, k, scheme))
+
+
+def moe_quantize(w: torch.Tensor, scheme: int, stream=None):
+    """Quantise fp32 w[..., K] per block of 32 along K. Returns (codes uint8, scales int16 bits)."""
+    _device_tensor(w, "w")
+    assert w.dtype == torch.float32
+    K = w.shape[-1]
+    rows = w.numel() // K
+    cb = K if scheme == MOE_Q_SYM8 else K // 2
+    codes = torch.empty(w.shape[:-1] + (cb,), dtype=torch.uint8, device=w.device)
+    scales = torch.empty(w.shape[:-1] + (K // 32,), dtype=torch.int16, device=w.device)
+    _check("moe_quantize", lib().moe_quantize(_p(w), rows, K, scheme, _p(codes), _p(scales), _stream(stream)))
+    return codes, scales
+
+
+def moe_route(x: torch.Tensor, router_w: torch.Tensor, k: int, flags: int = MOE_FLAG_RENORM,
+              ws: Workspace | None = None, stream=None):
+    """Router: returns (topk_idx int32 [T][k], topk_gate fp32 [T][k])."""
+    _device_tensor(x, "x")
+    _device_tensor(router_w, "router_w")
+    T, H = x.shape
+    E = router_w.shape[0]
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    gate = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    nb = moe_workspace_bytes(T, E, H, 32, k, MOE_Q_SYM8)
+    w = _ws(ws, nb, x.device)
+    _check("moe_route", lib().moe_route(_p(x), _xtype(x), T, H, _p(router_w), E, k, flags, _p(idx), _p(gate),
+                                        _p(w), w.numel(), _stream(stream)))
+    return idx, gate
+
+
+def moe_group(topk_idx: torch.Tensor, E: int, ws: Workspace | None = None, stream=None):
+    """Token-by-expert grouping: returns (counts [E], offsets [E+1], perm [T*k], uniq [E], n_uniq [1])."""
+    _device_tensor(topk_idx, "topk_idx")
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    uniq = torch.empty(E, dtype=torch.int32, device=dev)
+    n_uniq = torch.empty(1, dtype=torch.int32, device=dev)
+    nb = moe_workspace_bytes(T, E, 32, 32, k, MOE_Q_SYM8)
+    w = _ws(ws, nb, dev)
+    _check("moe_group", lib().moe_group(_p(topk_idx), T, k, E, _p(counts), _p(offsets), _p(perm), _p(uniq),
+                                        _p(n_uniq), _p(w), w.numel(), _stream(stream)))
+    return counts, offsets, perm, uniq, n_uniq
+
+
+def moe_gather_qmm_forward(x: torch.Tensor, ex: Experts, topk_idx: torch.Tensor, topk_gate: torch.Tensor | None,
+                           flags: int = 0, ws: Workspace | None = None, stream=None, out: torch.Tensor | None = None):
+    """Routed-only expert layer on given routing. y [T][H], or [T][k][H] when topk_gate is None."""
+    _device_tensor(x, "x")
+    _device_tensor(topk_idx, "topk_idx")
+    T, k = topk_idx.shape
+    shape = (T, ex.H) if topk_gate is not None else (T, k, ex.H)
+    y = out if out is not None else torch.empty(shape, dtype=torch.float32, device=x.device)
+    nb = moe_workspace_bytes(T, ex.E, ex.H, ex.I, k, ex.scheme)
+    w = _ws(ws, nb, x.device)
+    c = ex.c()
+    _check("moe_gather_qmm_forward",
+           lib().moe_gather_qmm_forward(_p(x), _xtype(x), T, ctypes.byref(c), k, _p(topk_idx), _p(topk_gate), _p(y),
+                                        flags, _p(w), w.numel(), _stream(stream)))
+    return y
+
+
+def moe_layer_forward(x: torch.Tensor, router_w: torch.Tensor, ex: Experts, k: int, flags: int = MOE_FLAG_RENORM,
+                      ws: Workspace | None = None, stream=None, out: torch.Tensor | None = None,
+                      return_routing: bool = True):
+    """Router + routed-only experts. Returns y [T][H] (and topk_idx, topk_gate)."""
+    _device_tensor(x, "x")
+    _device_tensor(router_w, "router_w")
+    T = x.shape[0]
+    y = out if out is not None else torch.empty((T, ex.H), dtype=torch.float32, device=x.device)
+    idx = gate = None
+    if return_routing:
+        idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        gate = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    nb = moe_workspace_bytes(T, ex.E, ex.H, ex.I, k, ex.scheme)
+    w = _ws(ws, nb, x.device)
+    c = ex.c()
+    _check("moe_layer_forward",
+           lib().moe_layer_forward(_p(x), _xtype(x), T, _p(router_w), ctypes.byref(c), k, flags, _p(y), _p(idx),
+                                   _p(gate), _p(w), w.numel(), _stream(stream)))
+    return (y, idx, gate) if return_routing else y
+
+
+def quantize_experts(w_gate_up: torch.Tensor, w_down: torch.Tensor, scheme: int, stream=None) -> Experts:
+    """Quantise fp32 device weights w_gate_up [E][2I][H], w_down [E][H][I] with the library's kernel."""
+    E, I2, H = w_gate_up.shape
+    cgu, sgu = moe_quantize(w_gate_up, scheme, stream)
+    cd, sd = moe_quantize(w_down, scheme, stream)
+    return Experts(E, H, I2 // 2, scheme, cgu, sgu, cd, sd)

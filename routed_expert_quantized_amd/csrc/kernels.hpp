@@ -1,0 +1,55 @@
+// kernels.hpp — launch wrappers of the gfx950 kernels, called by the C ABI layer.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 16;
+constexpr int kTiledLogitsMinT = 128;  // from this many tokens the router logits run as a tiled GEMM
+
+// Device buffers of the token-by-expert grouping.
+struct GroupBufs {
+  uint64_t* mask;    // [ceil(T/64)][E]
+  int32_t* base;     // [ceil(T/64)][E]
+  int32_t* counts;   // [E]
+  int32_t* offsets;  // [E+1]
+  int32_t* perm;     // [T*k]
+  int32_t* uniq;     // [E]
+  int32_t* n_uniq;   // [1]
+};
+
+// Experts as the kernels see them (byte pointers, decoded struct).
+struct ExpertsDev {
+  int E, H, I, scheme;
+  const uint8_t* wgu;
+  const uint16_t* sgu;
+  const uint8_t* wd;
+  const uint16_t* sd;
+};
+
+hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R, int E, float* logits,
+                         hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int renorm, int32_t* idx, float* gate,
+                       int32_t* idx2, float* gate2, hipStream_t s);
+hipError_t launch_group(const int32_t* idx, int T, int k, int E, const GroupBufs& g, hipStream_t s);
+
+// Single-token decode: gate/up + SwiGLU into h[k][I], then down + combine.
+// With logits != nullptr the routing is computed from them inside the gate/up
+// kernel (and written to idx_ws/gate_ws and the optional user copies); otherwise
+// idx/gate are read from idx_in/gate_in.
+hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int k, int renorm,
+                            const float* logits, const int32_t* idx_in, const float* gate_in,
+                            int32_t* idx_ws, float* gate_ws, int32_t* idx_user, float* gate_user,
+                            float* h, float* y, hipStream_t s);
+
+// Grouped decode for T > 1 (after launch_group): h[T*k][I], ys[T*k][H], y.
+hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsDev& ex, int k,
+                                 const GroupBufs& g, const float* gate, float* h, float* ys, float* y,
+                                 hipStream_t s);
+
+hipError_t launch_quantize(const float* w, int64_t rows, int K, int scheme, uint8_t* codes, uint16_t* scales,
+                           hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,268 @@
+// moe_api.cpp — host side of the C ABI declared in include/moe.h: argument
+// checks, workspace layout and kernel dispatch. No allocation, no host sync.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.hpp"
+#include "moe.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Scratch regions inside the caller's workspace, each 256-byte aligned.
+struct Layout {
+  size_t logits, idx, gate, mask, base, counts, offsets, perm, uniq, n_uniq, h, ys, total;
+};
+
+Layout layout(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const size_t o = off;
+    off += ((size_t)bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const int64_t C = (T + 63) / 64;
+  L.logits = take(T * E * 4);
+  L.idx = take(T * k * 4);
+  L.gate = take(T * k * 4);
+  L.mask = take(C * E * 8);
+  L.base = take(C * E * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.perm = take(T * k * 4);
+  L.uniq = take(E * 4);
+  L.n_uniq = take(4);
+  L.h = take(T * k * I * 4);
+  L.ys = take(T > 1 ? T * k * H * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+moe::GroupBufs group_bufs(void* ws, const Layout& L) {
+  return moe::GroupBufs{at<uint64_t>(ws, L.mask), at<int32_t>(ws, L.base), at<int32_t>(ws, L.counts),
+                        at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm), at<int32_t>(ws, L.uniq),
+                        at<int32_t>(ws, L.n_uniq)};
+}
+
+bool shape_ok(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
+  return T >= 1 && T <= 65536 && E >= 1 && E <= moe::kMaxE && H >= 32 && H <= 4096 && H % 32 == 0 &&
+         I >= 32 && I <= 4096 && I % 32 == 0 && k >= 1 && k <= std::min<int64_t>(E, moe::kMaxK);
+}
+
+moe_status check_shape(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
+  if (T < 1 || T > 65536) return fail(MOE_ERR_INVALID_ARG, "T=%lld outside [1, 65536]", (long long)T);
+  if (E < 1 || E > moe::kMaxE) return fail(MOE_ERR_INVALID_ARG, "E=%lld outside [1, %d]", (long long)E, moe::kMaxE);
+  if (H < 32 || H > 4096 || H % 32)
+    return fail(MOE_ERR_INVALID_ARG, "H=%lld must be a multiple of 32 in [32, 4096]", (long long)H);
+  if (I < 32 || I > 4096 || I % 32)
+    return fail(MOE_ERR_INVALID_ARG, "I=%lld must be a multiple of 32 in [32, 4096]", (long long)I);
+  if (k < 1 || k > std::min<int64_t>(E, moe::kMaxK))
+    return fail(MOE_ERR_INVALID_ARG, "k=%lld outside [1, min(E, %d)]", (long long)k, moe::kMaxK);
+  return MOE_OK;
+}
+
+moe_status check_ws(void* ws, size_t ws_bytes, const Layout& L) {
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace pointer is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, L.total);
+  return MOE_OK;
+}
+
+moe_status check_x(const void* x, int32_t xtype) {
+  if (!x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
+  if (xtype < MOE_F32 || xtype > MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "unknown activation type %d", xtype);
+  if (!aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x is not 16-byte aligned");
+  return MOE_OK;
+}
+
+moe_status check_experts(const moe_experts* ex, moe::ExpertsDev* d) {
+  if (!ex) return fail(MOE_ERR_INVALID_ARG, "experts struct is NULL");
+  if (ex->scheme != MOE_Q_SYM8 && ex->scheme != MOE_Q_INT4)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown weight codec %d", ex->scheme);
+  if (!ex->w_gate_up || !ex->s_gate_up || !ex->w_down || !ex->s_down)
+    return fail(MOE_ERR_INVALID_ARG, "an expert weight or scale pointer is NULL");
+  if (!aligned(ex->w_gate_up, 16) || !aligned(ex->w_down, 16) || !aligned(ex->s_gate_up, 2) ||
+      !aligned(ex->s_down, 2))
+    return fail(MOE_ERR_INVALID_ARG, "expert codes must be 16-byte aligned and scales 2-byte aligned");
+  *d = moe::ExpertsDev{ex->E, ex->H, ex->I, ex->scheme, static_cast<const uint8_t*>(ex->w_gate_up), ex->s_gate_up,
+                       static_cast<const uint8_t*>(ex->w_down), ex->s_down};
+  return MOE_OK;
+}
+
+// Expert stage shared by moe_gather_qmm_forward and moe_layer_forward.
+moe_status run_experts(const void* x, int32_t xtype, int32_t T, const moe::ExpertsDev& d, int32_t k,
+                       const int32_t* idx, const float* gate, float* y, uint32_t flags, void* ws,
+                       const Layout& L, hipStream_t s) {
+  if (flags & MOE_FLAG_PATH_GEMM)
+    return fail(MOE_ERR_UNSUPPORTED, "the grouped MFMA GEMM path is not available in this build");
+  float* h = at<float>(ws, L.h);
+  if (T == 1)
+    return hip_status(moe::launch_decode_t1(x, xtype, d, k, 0, nullptr, idx, gate, nullptr, nullptr, nullptr,
+                                            nullptr, h, y, s),
+                      "decode (one token)");
+  const moe::GroupBufs g = group_bufs(ws, L);
+  hipError_t e = moe::launch_group(idx, T, k, d.E, g, s);
+  if (e != hipSuccess) return hip_status(e, "grouping");
+  return hip_status(moe::launch_decode_grouped(x, xtype, T, d, k, g, gate, h, at<float>(ws, L.ys), y, s),
+                    "decode (grouped)");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(int32_t T, int32_t E, int32_t H, int32_t I, int32_t k, int32_t scheme) {
+  if (!shape_ok(T, E, H, I, k) || (scheme != MOE_Q_SYM8 && scheme != MOE_Q_INT4)) return 0;
+  return layout(T, E, H, I, k).total;
+}
+
+moe_status moe_route(const void* x, int32_t xtype, int32_t T, int32_t H, const float* router_w, int32_t E,
+                     int32_t k, uint32_t flags, int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
+                     void* stream) {
+  moe_status st;
+  if ((st = check_x(x, xtype))) return st;
+  if ((st = check_shape(T, E, H, 32, k))) return st;
+  if (!router_w || !topk_idx || !topk_gate) return fail(MOE_ERR_INVALID_ARG, "router_w, topk_idx or topk_gate is NULL");
+  if (!aligned(router_w, 16)) return fail(MOE_ERR_INVALID_ARG, "router_w is not 16-byte aligned");
+  if (flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_PATH_GATHER | MOE_FLAG_PATH_GEMM))
+    return fail(MOE_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  const Layout L = layout(T, E, H, 32, k);
+  if ((st = check_ws(ws, ws_bytes, L))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logits = at<float>(ws, L.logits);
+  hipError_t e = moe::launch_logits(x, xtype, T, H, router_w, E, logits, s);
+  if (e != hipSuccess) return hip_status(e, "router logits");
+  return hip_status(moe::launch_topk(logits, T, E, k, (flags & MOE_FLAG_RENORM) ? 1 : 0, topk_idx, topk_gate,
+                                     nullptr, nullptr, s),
+                    "top-k");
+}
+
+moe_status moe_group(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t* counts, int32_t* offsets,
+                     int32_t* perm, int32_t* uniq, int32_t* n_uniq, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st;
+  if ((st = check_shape(T, E, 32, 32, k))) return st;
+  if (!topk_idx || !counts || !offsets || !perm || !uniq || !n_uniq)
+    return fail(MOE_ERR_INVALID_ARG, "a grouping pointer is NULL");
+  const Layout L = layout(T, E, 32, 32, k);
+  if ((st = check_ws(ws, ws_bytes, L))) return st;
+  moe::GroupBufs g = group_bufs(ws, L);
+  g.counts = counts;
+  g.offsets = offsets;
+  g.perm = perm;
+  g.uniq = uniq;
+  g.n_uniq = n_uniq;
+  return hip_status(moe::launch_group(topk_idx, T, k, E, g, static_cast<hipStream_t>(stream)), "grouping");
+}
+
+moe_status moe_gather_qmm_forward(const void* x, int32_t xtype, int32_t T, const moe_experts* ex, int32_t k,
+                                  const int32_t* topk_idx, const float* topk_gate, float* y, uint32_t flags,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  moe_status st;
+  moe::ExpertsDev d;
+  if ((st = check_x(x, xtype))) return st;
+  if ((st = check_experts(ex, &d))) return st;
+  if ((st = check_shape(T, d.E, d.H, d.I, k))) return st;
+  if (!topk_idx || !y) return fail(MOE_ERR_INVALID_ARG, "topk_idx or y is NULL");
+  if (!aligned(y, 16)) return fail(MOE_ERR_INVALID_ARG, "y is not 16-byte aligned");
+  if ((flags & MOE_FLAG_PATH_GATHER) && (flags & MOE_FLAG_PATH_GEMM))
+    return fail(MOE_ERR_INVALID_ARG, "both path flags are set");
+  if (flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_PATH_GATHER | MOE_FLAG_PATH_GEMM))
+    return fail(MOE_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  const Layout L = layout(T, d.E, d.H, d.I, k);
+  if ((st = check_ws(ws, ws_bytes, L))) return st;
+  return run_experts(x, xtype, T, d, k, topk_idx, topk_gate, y, flags, ws, L, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_layer_forward(const void* x, int32_t xtype, int32_t T, const float* router_w, const moe_experts* ex,
+                             int32_t k, uint32_t flags, float* y, int32_t* topk_idx_out, float* topk_gate_out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  moe_status st;
+  moe::ExpertsDev d;
+  if ((st = check_x(x, xtype))) return st;
+  if ((st = check_experts(ex, &d))) return st;
+  if ((st = check_shape(T, d.E, d.H, d.I, k))) return st;
+  if (!router_w || !y) return fail(MOE_ERR_INVALID_ARG, "router_w or y is NULL");
+  if (!aligned(router_w, 16) || !aligned(y, 16))
+    return fail(MOE_ERR_INVALID_ARG, "router_w and y must be 16-byte aligned");
+  if ((flags & MOE_FLAG_PATH_GATHER) && (flags & MOE_FLAG_PATH_GEMM))
+    return fail(MOE_ERR_INVALID_ARG, "both path flags are set");
+  if (flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_PATH_GATHER | MOE_FLAG_PATH_GEMM))
+    return fail(MOE_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  const Layout L = layout(T, d.E, d.H, d.I, k);
+  if ((st = check_ws(ws, ws_bytes, L))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int renorm = (flags & MOE_FLAG_RENORM) ? 1 : 0;
+  float* logits = at<float>(ws, L.logits);
+  int32_t* idx = at<int32_t>(ws, L.idx);
+  float* gate = at<float>(ws, L.gate);
+  hipError_t e = moe::launch_logits(x, xtype, T, d.H, router_w, d.E, logits, s);
+  if (e != hipSuccess) return hip_status(e, "router logits");
+  if (T == 1 && !(flags & MOE_FLAG_PATH_GEMM))
+    return hip_status(moe::launch_decode_t1(x, xtype, d, k, renorm, logits, nullptr, nullptr, idx, gate,
+                                            topk_idx_out, topk_gate_out, at<float>(ws, L.h), y, s),
+                      "decode (one token)");
+  e = moe::launch_topk(logits, T, d.E, k, renorm, idx, gate, topk_idx_out, topk_gate_out, s);
+  if (e != hipSuccess) return hip_status(e, "top-k");
+  return run_experts(x, xtype, T, d, k, idx, gate, y, flags, ws, L, s);
+}
+
+moe_status moe_quantize(const float* w, int64_t rows, int32_t K, int32_t scheme, void* codes, uint16_t* scales,
+                        void* stream) {
+  if (!w || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "w, codes or scales is NULL");
+  if (rows < 0 || K <= 0 || K % 32) return fail(MOE_ERR_INVALID_ARG, "rows=%lld, K=%d: K must be a positive multiple of 32", (long long)rows, K);
+  if (scheme != MOE_Q_SYM8 && scheme != MOE_Q_INT4) return fail(MOE_ERR_UNSUPPORTED, "unknown weight codec %d", scheme);
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 2))
+    return fail(MOE_ERR_INVALID_ARG, "w and codes must be 16-byte aligned, scales 2-byte aligned");
+  return hip_status(moe::launch_quantize(w, rows, K, scheme, static_cast<uint8_t*>(codes), scales,
+                                         static_cast<hipStream_t>(stream)),
+                    "quantize");
+}
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/moe.h declares, sizes workspaces, and rejects bad arguments on the host
+before any launch (no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routed_expert_quantized_amd as rq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rq.LIB_PATH):
+        from routed_expert_quantized_amd import build
+        build.build()
+    return rq.lib()
+
+
+def test_exports_every_declared_function(L):
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", header))
+    assert declared == set(rq.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.moe_status_str(s)
+    assert L.moe_status_str(99) == b"unknown status"
+
+
+def test_workspace_bytes(L):
+    n1 = L.moe_workspace_bytes(1, 256, 2048, 512, 8, rq.MOE_Q_SYM8)
+    n64 = L.moe_workspace_bytes(64, 512, 2048, 512, 10, rq.MOE_Q_INT4)
+    assert n1 > 0 and n64 > n1 and n1 % 256 == 0
+    # h for T*k*I fp32 and ys for T*k*H fp32 at least
+    assert n64 >= 64 * 10 * (512 + 2048) * 4
+    for bad in [(0, 256, 2048, 512, 8, 0), (1, 2048, 2048, 512, 8, 0), (1, 256, 2000, 512, 8, 0),
+                (1, 256, 2048, 500, 8, 0), (1, 256, 2048, 512, 17, 0), (1, 4, 256, 128, 5, 0),
+                (1, 256, 8192, 512, 8, 0), (1, 256, 2048, 512, 8, 7)]:
+        assert L.moe_workspace_bytes(*bad) == 0, bad
+
+
+def _route(L, **kw):
+    a = dict(x=FAKE, xt=rq.MOE_F16, T=1, H=2048, R=FAKE, E=256, k=8, flags=1, idx=FAKE, gate=FAKE, ws=FAKE,
+             nws=1 << 30)
+    a.update(kw)
+    return L.moe_route(a["x"], a["xt"], a["T"], a["H"], a["R"], a["E"], a["k"], a["flags"], a["idx"], a["gate"],
+                       a["ws"], a["nws"], None)
+
+
+def test_route_validation(L):
+    assert _route(L, x=None) == rq.MOE_ERR_INVALID_ARG
+    assert b"x is NULL" in L.moe_last_error()
+    assert _route(L, xt=7) == rq.MOE_ERR_UNSUPPORTED
+    assert _route(L, T=0) == rq.MOE_ERR_INVALID_ARG
+    assert _route(L, H=2040) == rq.MOE_ERR_INVALID_ARG
+    assert _route(L, k=0) == rq.MOE_ERR_INVALID_ARG
+    assert _route(L, k=17, E=256) == rq.MOE_ERR_INVALID_ARG
+    assert _route(L, k=9, E=8) == rq.MOE_ERR_INVALID_ARG
+    assert _route(L, E=1025) == rq.MOE_ERR_INVALID_ARG
+    assert _route(L, R=None) == rq.MOE_ERR_INVALID_ARG
+    assert _route(L, x=ctypes.c_void_p(0x10008)) == rq.MOE_ERR_INVALID_ARG
+    assert _route(L, flags=0x80) == rq.MOE_ERR_UNSUPPORTED
+    assert _route(L, nws=1024) == rq.MOE_ERR_WORKSPACE
+    assert b"needed" in L.moe_last_error()
+    assert _route(L, ws=None) == rq.MOE_ERR_WORKSPACE
+    assert _route(L, ws=ctypes.c_void_p(0x10010)) == rq.MOE_ERR_WORKSPACE
+
+
+def _experts(scheme=rq.MOE_Q_SYM8, E=256, H=2048, I=512, ptr=FAKE):
+    return rq._Experts(E, H, I, scheme, ptr.value if ptr is not None else None, FAKE.value, FAKE.value, FAKE.value)
+
+
+def test_gather_and_layer_validation(L):
+    ex = _experts()
+
+    def gather(x=FAKE, xt=rq.MOE_F16, T=1, e=ex, k=8, idx=FAKE, gate=FAKE, y=FAKE, flags=0, ws=FAKE, nws=1 << 30):
+        return L.moe_gather_qmm_forward(x, xt, T, ctypes.byref(e) if e is not None else None, k, idx, gate, y,
+                                        flags, ws, nws, None)
+
+    assert gather(e=None) == rq.MOE_ERR_INVALID_ARG
+    assert gather(e=_experts(scheme=3)) == rq.MOE_ERR_UNSUPPORTED
+    assert gather(e=_experts(ptr=None)) == rq.MOE_ERR_INVALID_ARG
+    assert gather(e=_experts(ptr=ctypes.c_void_p(0x10004))) == rq.MOE_ERR_INVALID_ARG
+    assert gather(e=_experts(I=100)) == rq.MOE_ERR_INVALID_ARG
+    assert gather(e=_experts(H=8192)) == rq.MOE_ERR_INVALID_ARG
+    assert gather(idx=None) == rq.MOE_ERR_INVALID_ARG
+    assert gather(y=None) == rq.MOE_ERR_INVALID_ARG
+    assert gather(flags=rq.MOE_FLAG_PATH_GATHER | rq.MOE_FLAG_PATH_GEMM) == rq.MOE_ERR_INVALID_ARG
+    assert gather(flags=0x100) == rq.MOE_ERR_UNSUPPORTED
+    assert gather(nws=4096) == rq.MOE_ERR_WORKSPACE
+    need = L.moe_workspace_bytes(64, 256, 2048, 512, 8, 0)
+    assert gather(T=64, nws=need - 1) == rq.MOE_ERR_WORKSPACE
+
+    def layer(x=FAKE, R=FAKE, e=ex, k=8, flags=1, y=FAKE, nws=1 << 30):
+        return L.moe_layer_forward(x, rq.MOE_F16, 1, R, ctypes.byref(e), k, flags, y, None, None, FAKE, nws, None)
+
+    assert layer(R=None) == rq.MOE_ERR_INVALID_ARG
+    assert layer(y=None) == rq.MOE_ERR_INVALID_ARG
+    assert layer(k=300) == rq.MOE_ERR_INVALID_ARG
+    assert layer(nws=16) == rq.MOE_ERR_WORKSPACE
+    assert layer(flags=0x40) == rq.MOE_ERR_UNSUPPORTED
+
+
+def test_group_and_quantize_validation(L):
+    assert L.moe_group(None, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == rq.MOE_ERR_INVALID_ARG
+    assert L.moe_group(FAKE, 4, 9, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == rq.MOE_ERR_INVALID_ARG
+    assert L.moe_group(FAKE, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None) == rq.MOE_ERR_WORKSPACE
+    assert L.moe_quantize(FAKE, 4, 48, 0, FAKE, FAKE, None) == rq.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize(FAKE, 4, 64, 2, FAKE, FAKE, None) == rq.MOE_ERR_UNSUPPORTED
+    assert L.moe_quantize(None, 4, 64, 0, FAKE, FAKE, None) == rq.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize(FAKE, -1, 64, 0, FAKE, FAKE, None) == rq.MOE_ERR_INVALID_ARG

@@ -1,0 +1,161 @@
+"""Parity of the HIP path against the oracle, element by element, through the C ABI.
+
+Contract: router indices and grouping bit-exact; quantiser codes and scales
+bit-exact; gates within 1e-5 absolute; layer outputs within 1e-3 of the
+output norm per token (fp32 accumulation on the GPU, fp64 in the oracle).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routed_expert_quantized_amd as rq
+import synth
+from tests.cases import GATE_ATOL, Y_REL_NORM, enforce_gap, rel_inf_err, rel_norm_err
+from tests.gpu_cases import device_pool, oracle_compact, remap, to_dev_x
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rq.lib()  # raises if the HIP library is missing
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- quantiser
+@pytest.mark.parametrize("scheme", [rq.MOE_Q_SYM8, rq.MOE_Q_INT4])
+def test_quantize_bit_exact(scheme):
+    g = np.random.default_rng(100 + scheme)
+    w = (g.standard_normal((300, 512)) * 0.02).astype(np.float32)
+    w[0] = 0.0                              # zero blocks: scale 0, codes 0
+    w[1, :32] = 1e-9                        # scale underflows to a subnormal / zero
+    w[2] = g.standard_normal(512).astype(np.float32) * 1e4   # large values
+    w[3, :32] = np.arange(32, dtype=np.float32) - 16          # exact grid with ties
+    w[4, :32] = 70000.0 * 127               # scale saturates at 65504
+    codes, scales = rq.moe_quantize(torch.from_numpy(w).cuda(), scheme)
+    rc, rs = oracle.quantize(w, scheme)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), rs)
+
+
+# ---------------------------------------------------------------- router
+ROUTE_CASES = [("tiny", None), ("decode40", None), ("batched_int4", None), ("large_int4", None),
+               ("prefill", None), ("prefill", 130), ("batched_int4", 3)]
+
+
+@pytest.mark.parametrize("name,T", ROUTE_CASES)
+@pytest.mark.parametrize("renorm", [True, False])
+def test_route_parity(name, T, renorm):
+    w = synth.WORKLOADS[name]
+    li = enforce_gap(w, synth.draw_layer(w, seed=0, T=T, with_experts=False), seed=0, layer=0)
+    say(f"route {name} T={li.x.shape[0]} renorm={renorm}")
+    flags = rq.MOE_FLAG_RENORM if renorm else 0
+    idx, gate = rq.moe_route(to_dev_x(li.x, w.xtype), torch.from_numpy(li.R).cuda(), w.k, flags)
+    ridx, rgate = oracle.route(li.x, li.R, w.k, flags=oracle.RENORM if renorm else 0, bf16=w.xtype == synth.BF16)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
+
+
+def test_route_many_experts_and_max_k():
+    g = np.random.default_rng(7)
+    for T, H, E, k in [(5, 256, 1000, 16), (2, 64, 1024, 3), (4, 32, 16, 16), (1, 4096, 64, 1)]:
+        x = g.standard_normal((T, H)).astype(np.float32)
+        R = (g.standard_normal((E, H)) * 0.3).astype(np.float32)
+        w = synth.Workload("adhoc", T=T, H=H, E=E, k=k, I=32, scheme=0, xtype=synth.F32)
+        li = enforce_gap(w, synth.LayerInputs(x, x.copy(), R, None, None), seed=7, layer=T)
+        idx, gate = rq.moe_route(torch.from_numpy(li.x).cuda(), torch.from_numpy(R).cuda(), k)
+        ridx, rgate = oracle.route(li.x, R, k)
+        assert np.array_equal(idx.cpu().numpy(), ridx), (T, H, E, k)
+        assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
+
+
+# ---------------------------------------------------------------- grouping
+@pytest.mark.parametrize("T,k,E", [(1, 8, 256), (63, 10, 512), (64, 10, 512), (65, 3, 8), (16, 10, 512),
+                                   (2048, 8, 256), (300, 16, 1024), (5, 4, 4)])
+def test_group_bit_exact(T, k, E):
+    g = np.random.default_rng(T * 31 + k)
+    idx = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    counts, offsets, perm, uniq, n = rq.moe_group(torch.from_numpy(idx).cuda(), E)
+    rc, ro, rp, ru = oracle.group(idx, E)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(perm.cpu().numpy(), rp)
+    nu = int(n.cpu()[0])
+    assert nu == len(ru) and np.array_equal(uniq.cpu().numpy()[:nu], ru)
+
+
+# ---------------------------------------------------------------- gathered experts, small shapes
+SMALL = [(1, 6, 96, 64, 3), (1, 16, 256, 128, 4), (5, 6, 96, 64, 3), (37, 9, 160, 96, 4), (3, 2, 4096, 4096, 2),
+         (2, 16, 64, 32, 16)]
+
+
+@pytest.mark.parametrize("T,E,H,I,k", SMALL)
+@pytest.mark.parametrize("scheme", [rq.MOE_Q_SYM8, rq.MOE_Q_INT4])
+@pytest.mark.parametrize("xtype", [synth.F32, synth.F16, synth.BF16])
+def test_gather_parity_small(T, E, H, I, k, scheme, xtype):
+    say(f"gather T={T} E={E} H={H} I={I} k={k} scheme={scheme} xtype={xtype}")
+    g = np.random.default_rng(T + E + H + I + k + 10 * scheme + xtype)
+    wgu = (g.standard_normal((E, 2 * I, H)) * 0.02).astype(np.float32)
+    wd = (g.standard_normal((E, H, I)) * 0.02).astype(np.float32)
+    x32 = g.standard_normal((T, H)).astype(np.float32)
+    x = synth.encode_x(x32, xtype)
+    idx = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    gate = g.random((T, k)).astype(np.float32)
+    ex = rq.quantize_experts(torch.from_numpy(wgu).cuda(), torch.from_numpy(wd).cuda(), scheme)
+    rex = oracle.quantize_experts(wgu, wd, scheme)
+    xd = to_dev_x(x, xtype)
+    bf16 = xtype == synth.BF16
+    y = rq.moe_gather_qmm_forward(xd, ex, torch.from_numpy(idx).cuda(), torch.from_numpy(gate).cuda())
+    ref = oracle.gather_forward(x, rex, idx, gate, bf16=bf16)
+    assert rel_norm_err(y.cpu().numpy(), ref) <= Y_REL_NORM
+    ys = rq.moe_gather_qmm_forward(xd, ex, torch.from_numpy(idx).cuda(), None)
+    rys = oracle.gather_forward(x, rex, idx, None, bf16=bf16)
+    assert rel_norm_err(ys.cpu().numpy(), rys) <= Y_REL_NORM
+
+
+# ---------------------------------------------------------------- whole layer at the workloads' sizes
+LAYER_CASES = [("tiny", None, None), ("decode40", None, None), ("batched_int4", None, 16), ("large_int4", None, 6),
+               ("prefill", None, 12), ("batched_int4", 7, None)]
+
+
+@pytest.mark.parametrize("name,T,sample", LAYER_CASES)
+def test_layer_parity(name, T, sample):
+    w = synth.WORKLOADS[name]
+    li = enforce_gap(w, synth.draw_layer(w, seed=0, layer=0, T=T, with_experts=False), seed=0, layer=0)
+    bf16 = w.xtype == synth.BF16
+    ridx, rgate = oracle.route(li.x, li.R, w.k, bf16=bf16)
+    routed = np.unique(ridx)
+    say(f"layer {name} T={li.x.shape[0]} unique experts={len(routed)}")
+    ex = device_pool(w, 0, 0, routed)
+    y, idx, gate = rq.moe_layer_forward(to_dev_x(li.x, w.xtype), torch.from_numpy(li.R).cuda(), ex, w.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
+    yn = y.cpu().numpy()
+    assert np.isfinite(yn).all()   # unrouted experts carry NaN scales
+    Tn = li.x.shape[0]
+    toks = np.arange(Tn) if sample is None or sample >= Tn else np.random.default_rng(1).choice(Tn, sample, replace=False)
+    rex, m = oracle_compact(w, 0, 0, np.unique(ridx[toks]))
+    ref = oracle.gather_forward(np.ascontiguousarray(li.x[toks]), rex, remap(ridx[toks], m), rgate[toks], bf16=bf16)
+    err, inf = rel_norm_err(yn[toks], ref), rel_inf_err(yn[toks], ref)
+    say(f"  rel_norm_err={err:.3e} rel_inf_err={inf:.3e}")
+    assert err <= Y_REL_NORM
+
+
+def test_layer_is_deterministic():
+    w = synth.WORKLOADS["batched_int4"]
+    li = enforce_gap(w, synth.draw_layer(w, seed=3, with_experts=False), seed=3, layer=0)
+    ridx, _ = oracle.route(li.x, li.R, w.k)
+    ex = device_pool(w, 3, 0, np.unique(ridx))
+    xd, Rd = to_dev_x(li.x, w.xtype), torch.from_numpy(li.R).cuda()
+    a = rq.moe_layer_forward(xd, Rd, ex, w.k)[0].clone()
+    b = rq.moe_layer_forward(xd, Rd, ex, w.k)[0]
+    assert torch.equal(a, b)
