@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed, block-quantized MoE expert layer on one MI355X.
+
+Default workload (decode40): single-token decode through 40 stacked MoE
+layers, H=2048, E=256, top-8, I=512, sym8 experts with fp16 block scales, x
+fp16, fresh activations on each of 512 steps. A step is one token through
+all 40 layers: per layer, router, gathered gate/up + SwiGLU, per-slot down and
+gate-weighted combine. Each step is a captured HIP graph. Inputs and all
+40 layers' weights (34 GB) are resident in HBM before timing starts.
+
+Prints one JSON line: the contract fields, plus the dominant kernel's
+roofline (live HIP-event durations) and the CPU oracle's rate on a bounded
+sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode40]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "MoE-layer decode tokens/s + achieved HBM GB/s on routed bytes (1 MI355X)"
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "routed_expert_quantized_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode40")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=8, help="layer copies cycled for single-layer workloads")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--timer-steps", type=int, default=16, help="steps of the per-kernel event timing pass")
+    return ap.parse_args()
+
+
+def expert_bytes(w) -> int:
+    per_block = 32 if w.scheme == 0 else 16
+    return 3 * w.H * w.I // 32 * (per_block + 2)
+
+
+def gate_up_bytes(w) -> int:
+    per_block = 32 if w.scheme == 0 else 16
+    return 2 * w.I * w.H // 32 * (per_block + 2)
+
+
+def build_layers(w, nl, seed, rq, synth, torch):
+    """nl layers of device experts (quantised on the device) and host-drawn routers."""
+    pools, routers = [], []
+    for l in range(nl):
+        E, H, I = w.E, w.H, w.I
+        cbh = H if w.scheme == 0 else H // 2
+        cbi = I if w.scheme == 0 else I // 2
+        wgu = torch.empty((E, 2 * I, cbh), dtype=torch.uint8, device="cuda")
+        sgu = torch.empty((E, 2 * I, H // 32), dtype=torch.int16, device="cuda")
+        wd = torch.empty((E, H, cbi), dtype=torch.uint8, device="cuda")
+        sd = torch.empty((E, H, I // 32), dtype=torch.int16, device="cuda")
+        chunk = max(1, (256 << 20) // (3 * H * I * 4))
+        for e0, a, b in synth.torch_expert_chunks(w, seed, l, chunk, "cuda"):
+            c = a.shape[0]
+            ca, sa = rq.moe_quantize(a, w.scheme)
+            cb, sb = rq.moe_quantize(b, w.scheme)
+            wgu[e0:e0 + c], sgu[e0:e0 + c], wd[e0:e0 + c], sd[e0:e0 + c] = ca, sa, cb, sb
+            del a, b, ca, sa, cb, sb
+        pools.append(rq.Experts(E, H, I, w.scheme, wgu, sgu, wd, sd))
+        li = synth.draw_layer(w, seed=seed, layer=l, T=1, with_experts=False)
+        routers.append(torch.from_numpy(li.R).cuda())
+        if (l + 1) % 10 == 0:
+            log(f"  built {l + 1}/{nl} layers")
+    torch.cuda.synchronize()
+    return pools, routers
+
+
+def to_dev(x, xtype, torch):
+    import numpy as np
+    if xtype == 2:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def cpu_baseline(w, seed, seconds):
+    """The oracle, timed on this host on a bounded sample: one token per layer
+    for successive layers of the same workload (router + gathered experts).
+    Expert draws and quantisation happen before the clock starts."""
+    import numpy as np
+    import oracle
+    import synth
+    n_sample = min(w.layers, 8) if w.T == 1 else 2
+    t_sample = min(w.T, 16)
+    samples = []
+    for l in range(n_sample):
+        li = synth.draw_layer(w, seed=seed, layer=l, T=1, with_experts=False)
+        x = np.ascontiguousarray(synth.draw_step_x(w, seed, l)[:t_sample])
+        idx, _ = oracle.route(x, li.R, w.k, bf16=w.xtype == synth.BF16)
+        used = np.unique(idx)
+        wgu, wd = synth.draw_experts(seed, w.wid, l, used, w.H, w.I, w.weight_std)
+        samples.append((x, li.R, oracle.quantize_experts(wgu, wd, w.scheme), {int(e): i for i, e in enumerate(used)}))
+    t0 = time.perf_counter()
+    n_tok = 0
+    n_layers = 0
+    while True:
+        for x, R, ex, m in samples:
+            idx, gate = oracle.route(x, R, w.k, bf16=w.xtype == synth.BF16)
+            cidx = np.vectorize(lambda e: m[int(e)])(idx).astype(np.int32)
+            oracle.gather_forward(x, ex, cidx, gate, bf16=w.xtype == synth.BF16)
+            n_tok += x.shape[0]
+            n_layers += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n_tok / dt, "unit": "tokens/s (per layer)", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{len(samples)} layers x {t_sample} token(s) of {w.name}, {n_layers} layer calls in {dt:.1f} s "
+                      f"(fp64 oracle: router + gathered experts; weight draws and quantisation untimed)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the layer is built and measured on a single MI355X "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import routed_expert_quantized_amd as rq
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    K = args.steps if args.steps is not None else (512 if w.T == 1 else 64)
+    W = args.warmup if args.warmup is not None else 32
+    multi = w.layers > 1
+    nl = w.layers if multi else args.copies
+    log(f"workload {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} scheme={w.scheme} layers={nl}")
+    rq.lib()
+    t_setup = time.perf_counter()
+    pools, routers = build_layers(w, nl, args.seed, rq, synth, torch)
+    nx = w.steps if w.steps > 1 else 8
+    xs = torch.stack([to_dev(synth.draw_step_x(w, args.seed, s), w.xtype, torch) for s in range(nx)])
+    xbuf = torch.empty_like(xs[0])
+    ys = [torch.empty((w.T, w.H), dtype=torch.float32, device="cuda") for _ in range(nl)]
+    ws = rq.Workspace()
+    ws.get(rq.moe_workspace_bytes(w.T, w.E, w.H, w.I, w.k, w.scheme))
+    log(f"setup {time.perf_counter() - t_setup:.1f} s, pool {sum(p.w_gate_up.numel() + p.w_down.numel() for p in pools) / 1e9:.1f} GB codes")
+
+    layers_per_step = nl if multi else 1
+
+    def run_layers(step):
+        ls = range(nl) if multi else [step % nl]
+        for l in ls:
+            rq.moe_layer_forward(xbuf, routers[l], pools[l], w.k, rq.MOE_FLAG_RENORM, ws=ws, out=ys[l],
+                                 return_routing=False)
+
+    # eager warm-up (also checks every call succeeds)
+    xbuf.copy_(xs[0])
+    for s in range(2):
+        run_layers(s)
+    torch.cuda.synchronize()
+
+    graphs = []
+    if not args.no_graph:
+        ngraph = 1 if multi else nl
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        torch.cuda.current_stream().wait_stream(side)
+        for gi in range(ngraph):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_layers(gi)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def step(s):
+        xbuf.copy_(xs[s % nx])
+        if graphs:
+            graphs[0 if multi else s % nl].replay()
+        else:
+            run_layers(s)
+
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for s in range(K):
+        step(W + s)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    elapsed_ms = ev0.elapsed_time(ev1)
+    log(f"timed {K} steps: {elapsed_ms:.2f} ms (wall {wall * 1e3:.2f} ms)")
+
+    # realized unique experts per layer call (routing recomputed after the clock stops)
+    uniq_counts = []
+    for s in range(min(K, 64)):
+        ss = W + s
+        x = xs[ss % nx]
+        for l in (range(nl) if multi else [ss % nl]):
+            idx, _ = rq.moe_route(x, routers[l], w.k, rq.MOE_FLAG_RENORM)
+            uniq_counts.append(len(torch.unique(idx)))
+    uniq_mean = float(np.mean(uniq_counts))
+    layer_calls = K * layers_per_step
+    t_layer_s = elapsed_ms * 1e-3 / layer_calls
+    routed_bytes = uniq_mean * expert_bytes(w)
+    routed_gbps = routed_bytes / t_layer_s / 1e9
+    tokens_per_s_layer = w.T / t_layer_s
+
+    # per-kernel durations: eager pass with HIP events around every launch
+    def timed_kernel(kid, n_steps):
+        with rq.KernelTimer(kid, n_steps * layers_per_step + 8) as t:
+            for s in range(n_steps):
+                xbuf.copy_(xs[s % nx])
+                run_layers(s)
+        torch.cuda.synchronize()
+        return float(np.mean(t.ms)) * 1e3 if t.ms else None  # microseconds
+
+    gu_us = timed_kernel(rq.MOE_KERNEL_GATE_UP, args.timer_steps)
+    dn_us = timed_kernel(rq.MOE_KERNEL_DOWN, args.timer_steps)
+    rt_us = timed_kernel(rq.MOE_KERNEL_ROUTE_LOGITS, args.timer_steps)
+    # algorithmic bytes of one launch of the dominant kernel
+    xbytes = w.T * w.H * (4 if w.xtype == 0 else 2)
+    # gathered gate/up: routed gate/up codes + scales, x, router logits (single token,
+    # where the top-k runs inside this kernel) and the fp32 SwiGLU output
+    gu_alg = uniq_mean * gate_up_bytes(w) + xbytes + w.T * w.k * w.I * 4 + (w.E * 4 if w.T == 1 else 0)
+    kname = "gathered gate/up + SwiGLU" + (" (with the top-k)" if w.T == 1 else " (grouped)")
+    achieved = gu_alg / (gu_us * 1e-6) / 1e9
+
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", f"traffic_gate_up_{w.name}.json")
+    sha = kernel_source_sha()
+    if os.path.exists(tf):
+        with open(tf) as f:
+            tj = json.load(f)
+        if tj.get("kernel_source_sha") == sha:
+            traffic = tj.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s_layer, 1),
+        "unit": "tokens/s per MoE layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(elapsed_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
+                   "codec": "sym8" if w.scheme == 0 else "int4",
+                   "x": {0: "f32", 1: "f16", 2: "bf16"}[w.xtype], "layers_per_step": layers_per_step,
+                   "layer_copies": nl, "fresh_x": nx, "graph": not args.no_graph},
+        "us_per_layer": round(t_layer_s * 1e6, 3),
+        "step_tokens_per_s": round(w.T / (elapsed_ms * 1e-3 / K), 1),
+        "routed_bytes_per_layer": int(routed_bytes),
+        "unique_experts_per_layer": round(uniq_mean, 2),
+        "routed_hbm_gbps": round(routed_gbps, 1),
+        "routed_hbm_frac": round(routed_gbps / HBM_PEAK_GBPS, 4),
+        "kernel_us": {"gate_up": round(gu_us, 3), "down": round(dn_us, 3), "route_logits": round(rt_us, 3)},
+        "roofline": {"kernel": kname, "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(gu_alg), "avg_launch_us": round(gu_us, 3)},
+        "kernel_source_sha": sha,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,8 +22,9 @@
  *     keeps no pointer after a call returns. The moe_experts struct itself is
  *     read on the host, during the call only.
  *   - Every call is asynchronous on `stream`, a hipStream_t passed as void*
- *     (NULL means the default stream). No call synchronises, allocates device
- *     memory or copies device data to the host.
+ *     (NULL means the default stream). No call allocates device memory or
+ *     copies device data to the host, and none synchronises except the
+ *     benchmark timer's moe_timer_read.
  *   - Arguments are checked on the host before any launch. A failed check
  *     returns an error and launches nothing. moe_last_error() then describes it,
  *     per calling thread.
@@ -113,8 +114,9 @@ moe_status moe_route(const void* x, int32_t xtype, int32_t T, int32_t H, const f
  *   uniq:    out [E]     experts with counts > 0, ascending. Entries past
  *                        *n_uniq are unspecified.
  *   n_uniq:  out [1]     number of such experts.
- * topk_idx entries must lie in [0, E); the caller guarantees this. No workspace
- * is needed beyond `ws` of moe_workspace_bytes(T, E, 32, 32, k, 0) bytes. */
+ * topk_idx entries must lie in [0, E) and the k ids of one token must be
+ * distinct, as moe_route produces them; the caller guarantees both. `ws` must
+ * hold moe_workspace_bytes(T, E, 32, 32, k, 0) bytes. */
 moe_status moe_group(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t* counts,
                      int32_t* offsets, int32_t* perm, int32_t* uniq, int32_t* n_uniq,
                      void* ws, size_t ws_bytes, void* stream);
@@ -127,8 +129,9 @@ moe_status moe_group(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, i
  * Only the weights of experts named in topk_idx are read.
  *   topk_gate: [T][k] fp32. With it, y is [T][H] = sum_s gate[t][s] * ys, in
  *              slot order. With topk_gate == NULL, y is [T][k][H], the per-slot ys.
- *   topk_idx:  entries must lie in [0, E). The caller guarantees this; it is
- *              not checked on the device.
+ *   topk_idx:  entries must lie in [0, E), and the k ids of one token must be
+ *              distinct, as moe_route produces them. The caller guarantees
+ *              both; they are not checked on the device.
  *   flags:     MOE_FLAG_PATH_* bits select the path; other bits are ignored. */
 moe_status moe_gather_qmm_forward(const void* x, int32_t xtype, int32_t T, const moe_experts* ex,
                                   int32_t k, const int32_t* topk_idx, const float* topk_gate,
@@ -152,6 +155,30 @@ moe_status moe_layer_forward(const void* x, int32_t xtype, int32_t T, const floa
  * K must be a positive multiple of 32. Non-finite inputs give unspecified codes. */
 moe_status moe_quantize(const float* w, int64_t rows, int32_t K, int32_t scheme, void* codes,
                         uint16_t* scales, void* stream);
+
+/* Benchmark support: per-launch kernel durations from HIP events.
+ * moe_timer_start arms a timer for the next `capacity` launches of one kernel
+ * family (MOE_KERNEL_*), on any stream; those launches go through
+ * hipExtLaunchKernel with a start and a stop event. moe_timer_read waits for
+ * the recorded launches (a host synchronisation, the only one in this
+ * library), writes up to `capacity` durations in milliseconds to the host
+ * array `ms`, stores how many were recorded in *count and disarms the timer.
+ * Global state: not thread-safe, and not for launches under graph capture.
+ * capacity must lie in [1, 1 << 20]. */
+enum {
+  MOE_KERNEL_ROUTE_LOGITS = 0,  /* router logits (GEMV or tiled GEMM) */
+  MOE_KERNEL_TOPK = 1,          /* one-wave top-k */
+  MOE_KERNEL_GROUP = 2,         /* token-by-expert grouping (three kernels) */
+  MOE_KERNEL_GATE_UP = 3,       /* gathered gate/up + SwiGLU (one token or grouped) */
+  MOE_KERNEL_DOWN = 4,          /* gathered per-slot down (+ combine for one token) */
+  MOE_KERNEL_COMBINE = 5,       /* gate-weighted combine (T > 1) */
+  MOE_KERNEL_GEMM_GATE_UP = 6,  /* grouped MFMA GEMM, gate/up + SwiGLU */
+  MOE_KERNEL_GEMM_DOWN = 7,     /* grouped MFMA GEMM, down */
+  MOE_KERNEL_QUANTIZE = 8,      /* block quantiser */
+  MOE_KERNEL_COUNT = 9
+};
+moe_status moe_timer_start(int32_t kernel, int32_t capacity);
+moe_status moe_timer_read(float* ms, int32_t capacity, int32_t* count);
 
 /* Static description of a status code. */
 const char* moe_status_str(moe_status s);

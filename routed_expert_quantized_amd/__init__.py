@@ -27,7 +27,10 @@ MOE_FLAG_RENORM, MOE_FLAG_PATH_GATHER, MOE_FLAG_PATH_GEMM = 1, 2, 4
 
 # Every function the header declares; the library must export all of them.
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_group", "moe_gather_qmm_forward", "moe_layer_forward",
-           "moe_quantize", "moe_status_str", "moe_last_error")
+           "moe_quantize", "moe_timer_start", "moe_timer_read", "moe_status_str", "moe_last_error")
+
+(MOE_KERNEL_ROUTE_LOGITS, MOE_KERNEL_TOPK, MOE_KERNEL_GROUP, MOE_KERNEL_GATE_UP, MOE_KERNEL_DOWN, MOE_KERNEL_COMBINE,
+ MOE_KERNEL_GEMM_GATE_UP, MOE_KERNEL_GEMM_DOWN, MOE_KERNEL_QUANTIZE) = range(9)
 
 
 class MoeError(RuntimeError):
@@ -61,6 +64,8 @@ def lib() -> ctypes.CDLL:
             "moe_gather_qmm_forward": ([P, I32, I32, E, I32, P, P, P, U32, P, SZ, P], ctypes.c_int),
             "moe_layer_forward": ([P, I32, I32, P, E, I32, U32, P, P, P, P, SZ, P], ctypes.c_int),
             "moe_quantize": ([P, I64, I32, I32, P, P, P], ctypes.c_int),
+            "moe_timer_start": ([I32, I32], ctypes.c_int),
+            "moe_timer_read": ([P, I32, P], ctypes.c_int),
             "moe_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "moe_last_error": ([], ctypes.c_char_p),
         }
@@ -236,6 +241,27 @@ def moe_layer_forward(x: torch.Tensor, router_w: torch.Tensor, ex: Experts, k: i
            lib().moe_layer_forward(_p(x), _xtype(x), T, _p(router_w), ctypes.byref(c), k, flags, _p(y), _p(idx),
                                    _p(gate), _p(w), w.numel(), _stream(stream)))
     return (y, idx, gate) if return_routing else y
+
+
+class KernelTimer:
+    """Durations of the next `capacity` launches of one kernel family (HIP events).
+
+    Use around eager (not graph-captured) calls: `with KernelTimer(MOE_KERNEL_GATE_UP, n) as t: ...`,
+    then t.ms holds the per-launch durations in milliseconds."""
+
+    def __init__(self, kernel: int, capacity: int):
+        self.kernel, self.capacity, self.ms = kernel, capacity, []
+
+    def __enter__(self):
+        _check("moe_timer_start", lib().moe_timer_start(self.kernel, self.capacity))
+        return self
+
+    def __exit__(self, *exc):
+        buf = (ctypes.c_float * self.capacity)()
+        n = ctypes.c_int32(0)
+        _check("moe_timer_read", lib().moe_timer_read(buf, self.capacity, ctypes.byref(n)))
+        self.ms = list(buf[: n.value])
+        return False
 
 
 def quantize_experts(w_gate_up: torch.Tensor, w_down: torch.Tensor, scheme: int, stream=None) -> Experts:

@@ -35,10 +35,6 @@ static void with_xtype(int xt, F&& f) {
   else f(IC<MOE_BF16>{});
 }
 
-template <int SCHEME>
-__host__ __device__ constexpr int64_t row_bytes(int K) {
-  return SCHEME == MOE_Q_SYM8 ? (int64_t)K : (int64_t)K / 2;
-}
 
 // ------------------------------------------------------------------ T = 1
 // Grid: k slots x blocks_per_slot. A wave computes RP (gate row n, up row I+n)
@@ -55,31 +51,33 @@ __global__ __launch_bounds__(256) void k_gate_up_t1(const void* __restrict__ x, 
                                                     float* __restrict__ h, int blocks_per_slot) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int slot = blockIdx.x / blocks_per_slot, blk = blockIdx.x % blocks_per_slot;
+  const int H = ex.H, I = ex.I, NB = H / 32;
+  // Every load below is unconditional (block and row indices are clamped in
+  // bounds, surplus lanes get a zero scale) so the scheduler can issue them all
+  // before the arithmetic.
+  // activations do not depend on the routing: load them first
+  XReg<SCHEME, XT> xr[NBJ];
+#pragma unroll
+  for (int j = 0; j < NBJ; ++j) load_xreg<SCHEME, XT>(xr[j], x, 0, min(lane + 64 * j, NB - 1));
+  __builtin_amdgcn_sched_barrier(0);
   int e;
   if constexpr (FROM_LOGITS) {
+    // A workgroup of slot s needs only the first s+1 rounds; the first
+    // workgroup of the last slot runs all k, computes the gates and publishes
+    // the routing for the down kernel and the caller.
     int my_idx;
     float my_gate;
-    wave_topk<VPL>(logits, ex.E, k, renorm != 0, my_idx, my_gate);
-    if (blockIdx.x == 0 && wave == 0 && lane < k) {
+    const bool publisher = blockIdx.x == (k - 1) * blocks_per_slot;
+    wave_topk<VPL>(logits, ex.E, k, renorm != 0, my_idx, my_gate, publisher ? k : slot + 1);
+    if (publisher && wave == 0 && lane < k) {
       idx_ws[lane] = my_idx;
       gate_ws[lane] = my_gate;
       if (idx_user) idx_user[lane] = my_idx;
       if (gate_user) gate_user[lane] = my_gate;
     }
-    e = __shfl(my_idx, slot, 64);
+    e = __builtin_amdgcn_readlane(my_idx, slot);
   } else {
     e = idx_in[slot];
-  }
-  const int H = ex.H, I = ex.I, NB = H / 32;
-  float xf[NBJ][32];
-#pragma unroll
-  for (int j = 0; j < NBJ; ++j) {
-    const int b = lane + 64 * j;
-    if (b < NB) load_x_block<XT>(x, 0, b, xf[j]);
-    else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) xf[j][i] = 0.0f;
-    }
   }
   const int n0 = (blk * 4 + wave) * RP;
   const int64_t rb = row_bytes<SCHEME>(H);
@@ -91,24 +89,22 @@ __global__ __launch_bounds__(256) void k_gate_up_t1(const void* __restrict__ x, 
     const int64_t grow = (int64_t)e * 2 * I + n, urow = grow + I;
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) {
-      const int b = lane + 64 * j;
-      if (b < NB) {
-        cg[r][j] = load_block<SCHEME>(ex.wgu + grow * rb, b);
-        cu[r][j] = load_block<SCHEME>(ex.wgu + urow * rb, b);
-        sg[r][j] = f16_bits_to_f32(ex.sgu[grow * NB + b]);
-        su[r][j] = f16_bits_to_f32(ex.sgu[urow * NB + b]);
-      }
+      const int b = min(lane + 64 * j, NB - 1);
+      cg[r][j] = load_block<SCHEME>(ex.wgu + grow * rb, b);
+      cu[r][j] = load_block<SCHEME>(ex.wgu + urow * rb, b);
+      sg[r][j] = f16_bits_to_f32(ex.sgu[grow * NB + b]);
+      su[r][j] = f16_bits_to_f32(ex.sgu[urow * NB + b]);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
     float ag = 0.0f, au = 0.0f;
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) {
-      if (lane + 64 * j < NB) {
-        ag = fmaf(sg[r][j], block_dot<SCHEME>(cg[r][j], xf[j]), ag);
-        au = fmaf(su[r][j], block_dot<SCHEME>(cu[r][j], xf[j]), au);
-      }
+      const bool valid = lane + 64 * j < NB;
+      ag = fmaf(valid ? sg[r][j] : 0.0f, xdot<SCHEME, XT>(cg[r][j], xr[j]), ag);
+      au = fmaf(valid ? su[r][j] : 0.0f, xdot<SCHEME, XT>(cu[r][j], xr[j]), au);
     }
     ag = wave_sum(ag);
     au = wave_sum(au);
@@ -116,52 +112,131 @@ __global__ __launch_bounds__(256) void k_gate_up_t1(const void* __restrict__ x, 
   }
 }
 
-// Grid: ceil(H / 16). 16 lanes per output row, 4 rows per wave. For each slot in
-// order: row of the slot's expert . h[slot], then y += gate * that (or, with
-// gate == nullptr, y[slot][m] = that).
-template <int SCHEME, int NBJ>
-__global__ __launch_bounds__(256) void k_down_t1(ExpertsDev ex, int k, const int32_t* __restrict__ idx,
-                                                 const float* __restrict__ gate, const float* __restrict__ h,
-                                                 float* __restrict__ y) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// Per-thread float4 registers that stage h (k * I floats) through LDS in the
+// single-token down kernel: 128 threads x 8 float4 = 4096 floats.
+constexpr int kHRegs = 8;
+
+// Grid: ceil(H / 8), two waves of four 16-lane row groups. For each slot in
+// order the row of the slot's expert is dotted with h[slot], then
+// y += gate * that (with gate == nullptr, y[slot][m] = that).
+//
+// k_down_t1_lds: k <= KC slots and k * I <= 128 * 4 * kHRegs. h is requested
+// first (into registers), then every slot's code rows, all unconditionally, so
+// one wait covers h and the rows stream in together; h goes to LDS for the
+// dot products.
+template <int SCHEME, int NBJ, int KC>
+__global__ __launch_bounds__(128) void k_down_t1_lds(ExpertsDev ex, int k, const int32_t* __restrict__ idx,
+                                                     const float* __restrict__ gate, const float* __restrict__ h,
+                                                     float* __restrict__ y) {
+  extern __shared__ float hs[];
+  const int tid = (int)threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int lg = lane >> 4, ll = lane & 15;
   const int H = ex.H, I = ex.I, NBI = I / 32;
-  const int m = (blockIdx.x * 4 + wave) * 4 + lg;
+  const int m = ((int)blockIdx.x * 2 + wave) * 4 + lg;
+  const int mm = min(m, H - 1);
+  const int64_t rb = row_bytes<SCHEME>(I);
+  float4 hr[kHRegs];
+#pragma unroll
+  for (int r = 0; r < kHRegs; ++r) hr[r] = *reinterpret_cast<const float4*>(h + min((tid + 128 * r) * 4, k * I - 4));
+  __builtin_amdgcn_sched_barrier(0);  // keep the h loads ahead of the code rows
+  Block<SCHEME> c[KC][NBJ];
+  float sc[KC][NBJ];
+#pragma unroll
+  for (int q = 0; q < KC; ++q) {
+    const int64_t row = (int64_t)idx[min(q, k - 1)] * H + mm;
+#pragma unroll
+    for (int j = 0; j < NBJ; ++j) {
+      const int b = min(ll + 16 * j, NBI - 1);
+      c[q][j] = load_block<SCHEME>(ex.wd + row * rb, b);
+      sc[q][j] = f16_bits_to_f32(ex.sd[row * NBI + b]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // all rows requested before any wait
+  // surplus threads rewrite the last chunk with the same data (no branch, so the
+  // h loads stay where they were issued)
+#pragma unroll
+  for (int r = 0; r < kHRegs; ++r)
+    *reinterpret_cast<float4*>(hs + hpad(min((tid + 128 * r) * 4, k * I - 4))) = hr[r];
+  __syncthreads();
+  float acc = 0.0f;
+#pragma unroll
+  for (int q = 0; q < KC; ++q) {
+    if (q < k) {
+      float part = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NBJ; ++j) {
+        const int b = ll + 16 * j;
+        if (b < NBI) {
+          float hv[32];
+          const float* src = hs + hpad(q * I + 32 * b);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float4 v = *reinterpret_cast<const float4*>(src + 4 * i);
+            hv[4 * i] = v.x; hv[4 * i + 1] = v.y; hv[4 * i + 2] = v.z; hv[4 * i + 3] = v.w;
+          }
+          part = fmaf(sc[q][j], block_dot<SCHEME>(c[q][j], hv), part);
+        }
+      }
+      part = row_sum16(part);
+      if (gate) acc = fmaf(gate[q], part, acc);
+      else if (ll == 0 && m < H) y[(int64_t)q * H + m] = part;
+    }
+  }
+  if (gate && ll == 0 && m < H) y[m] = acc;
+}
+
+// General single-token down (any k, any I): KC slots' rows in flight at a
+// time, h read from global memory.
+template <int SCHEME, int NBJ>
+__global__ __launch_bounds__(128) void k_down_t1(ExpertsDev ex, int k, const int32_t* __restrict__ idx,
+                                                 const float* __restrict__ gate, const float* __restrict__ h,
+                                                 float* __restrict__ y) {
+  constexpr int KC = NBJ >= 8 ? 1 : 8 / NBJ;
+  const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+  const int lg = lane >> 4, ll = lane & 15;
+  const int H = ex.H, I = ex.I, NBI = I / 32;
+  const int m = ((int)blockIdx.x * 2 + wave) * 4 + lg;
   const int mm = min(m, H - 1);
   const int64_t rb = row_bytes<SCHEME>(I);
   float acc = 0.0f;
-#pragma unroll 2
-  for (int s = 0; s < k; ++s) {
-    const int e = idx[s];
-    const int64_t row = (int64_t)e * H + mm;
-    Block<SCHEME> c[NBJ];
-    float sc[NBJ];
+  for (int s0 = 0; s0 < k; s0 += KC) {
+    Block<SCHEME> c[KC][NBJ];
+    float sc[KC][NBJ];
 #pragma unroll
-    for (int j = 0; j < NBJ; ++j) {
-      const int b = ll + 16 * j;
-      if (b < NBI) {
-        c[j] = load_block<SCHEME>(ex.wd + row * rb, b);
-        sc[j] = f16_bits_to_f32(ex.sd[row * NBI + b]);
+    for (int q = 0; q < KC; ++q) {
+      const int64_t row = (int64_t)idx[min(s0 + q, k - 1)] * H + mm;
+#pragma unroll
+      for (int j = 0; j < NBJ; ++j) {
+        const int b = min(ll + 16 * j, NBI - 1);
+        c[q][j] = load_block<SCHEME>(ex.wd + row * rb, b);
+        sc[q][j] = f16_bits_to_f32(ex.sd[row * NBI + b]);
       }
     }
-    float part = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NBJ; ++j) {
-      const int b = ll + 16 * j;
-      if (b < NBI) {
-        float hv[32];
-        const float4* hp = reinterpret_cast<const float4*>(h + (int64_t)s * I + 32 * b);
+    for (int q = 0; q < KC; ++q) {
+      const int s = s0 + q;
+      if (s < k) {
+        float part = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float4 v = hp[i];
-          hv[4 * i] = v.x; hv[4 * i + 1] = v.y; hv[4 * i + 2] = v.z; hv[4 * i + 3] = v.w;
+        for (int j = 0; j < NBJ; ++j) {
+          const int b = ll + 16 * j;
+          if (b < NBI) {
+            float hv[32];
+            const float4* hp = reinterpret_cast<const float4*>(h + (int64_t)s * I + 32 * b);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float4 v = hp[i];
+              hv[4 * i] = v.x; hv[4 * i + 1] = v.y; hv[4 * i + 2] = v.z; hv[4 * i + 3] = v.w;
+            }
+            part = fmaf(sc[q][j], block_dot<SCHEME>(c[q][j], hv), part);
+          }
         }
-        part = fmaf(sc[j], block_dot<SCHEME>(c[j], hv), part);
+        part = row_sum16(part);
+        if (gate) acc = fmaf(gate[s], part, acc);
+        else if (ll == 0 && m < H) y[(int64_t)s * H + m] = part;
       }
     }
-    part = group_sum<16>(part);
-    if (gate) acc = fmaf(gate[s], part, acc);
-    else if (ll == 0 && m < H) y[(int64_t)s * H + m] = part;
   }
   if (gate && ll == 0 && m < H) y[m] = acc;
 }
@@ -192,13 +267,12 @@ __global__ __launch_bounds__(256) void k_gate_up_grouped(const void* __restrict_
     const int64_t grow = (int64_t)e * 2 * I + n, urow = grow + I;
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) {
-      const int b = lane + 64 * j;
-      if (b < NB) {
-        cg[r][j] = load_block<SCHEME>(ex.wgu + grow * rb, b);
-        cu[r][j] = load_block<SCHEME>(ex.wgu + urow * rb, b);
-        sg[r][j] = f16_bits_to_f32(ex.sgu[grow * NB + b]);
-        su[r][j] = f16_bits_to_f32(ex.sgu[urow * NB + b]);
-      }
+      const int b = min(lane + 64 * j, NB - 1);
+      const float valid = lane + 64 * j < NB ? 1.0f : 0.0f;
+      cg[r][j] = load_block<SCHEME>(ex.wgu + grow * rb, b);
+      cu[r][j] = load_block<SCHEME>(ex.wgu + urow * rb, b);
+      sg[r][j] = valid * f16_bits_to_f32(ex.sgu[grow * NB + b]);
+      su[r][j] = valid * f16_bits_to_f32(ex.sgu[urow * NB + b]);
     }
   }
   for (int a = 0; a < cnt; ++a) {
@@ -209,15 +283,12 @@ __global__ __launch_bounds__(256) void k_gate_up_grouped(const void* __restrict_
     for (int r = 0; r < RP; ++r) ag[r] = au[r] = 0.0f;
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) {
-      const int b = lane + 64 * j;
-      if (b < NB) {
-        float xf[32];
-        load_x_block<XT>(x, (int64_t)t * H, b, xf);
+      XReg<SCHEME, XT> xr;
+      load_xreg<SCHEME, XT>(xr, x, (int64_t)t * H, min(lane + 64 * j, NB - 1));
 #pragma unroll
-        for (int r = 0; r < RP; ++r) {
-          ag[r] = fmaf(sg[r][j], block_dot<SCHEME>(cg[r][j], xf), ag[r]);
-          au[r] = fmaf(su[r][j], block_dot<SCHEME>(cu[r][j], xf), au[r]);
-        }
+      for (int r = 0; r < RP; ++r) {
+        ag[r] = fmaf(sg[r][j], xdot<SCHEME, XT>(cg[r][j], xr), ag[r]);
+        au[r] = fmaf(su[r][j], xdot<SCHEME, XT>(cu[r][j], xr), au[r]);
       }
     }
 #pragma unroll
@@ -252,11 +323,9 @@ __global__ __launch_bounds__(256) void k_down_grouped(ExpertsDev ex, int k, cons
   float sc[NBJ];
 #pragma unroll
   for (int j = 0; j < NBJ; ++j) {
-    const int b = ll + 16 * j;
-    if (b < NBI) {
-      c[j] = load_block<SCHEME>(ex.wd + row * rb, b);
-      sc[j] = f16_bits_to_f32(ex.sd[row * NBI + b]);
-    }
+    const int b = min(ll + 16 * j, NBI - 1);
+    c[j] = load_block<SCHEME>(ex.wd + row * rb, b);
+    sc[j] = (ll + 16 * j < NBI ? 1.0f : 0.0f) * f16_bits_to_f32(ex.sd[row * NBI + b]);
   }
   for (int a = 0; a < cnt; ++a) {
     const int f = perm[beg + a];
@@ -275,7 +344,7 @@ __global__ __launch_bounds__(256) void k_down_grouped(ExpertsDev ex, int k, cons
         part = fmaf(sc[j], block_dot<SCHEME>(c[j], hv), part);
       }
     }
-    part = group_sum<16>(part);
+    part = row_sum16(part);
     if (ll == 0 && m < H) ys[(int64_t)f * H + m] = part;
   }
 }
@@ -307,29 +376,39 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
         const int bps = (ex.I + 4 * RP - 1) / (4 * RP);
         dim3 grid(k * bps);
         if (!from_logits)
-          hipLaunchKernelGGL((k_gate_up_t1<SC, XT, NBJ, RP, false, 1>), grid, dim3(256), 0, s, x, ex, k, renorm,
+          MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_t1<SC, XT, NBJ, RP, false, 1>), grid, dim3(256), 0, s, x, ex, k, renorm,
                              logits, idx_in, idx_ws, gate_ws, idx_user, gate_user, h, bps);
         else if (ex.E <= 256)
-          hipLaunchKernelGGL((k_gate_up_t1<SC, XT, NBJ, RP, true, 4>), grid, dim3(256), 0, s, x, ex, k, renorm,
+          MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_t1<SC, XT, NBJ, RP, true, 4>), grid, dim3(256), 0, s, x, ex, k, renorm,
                              logits, idx_in, idx_ws, gate_ws, idx_user, gate_user, h, bps);
         else
-          hipLaunchKernelGGL((k_gate_up_t1<SC, XT, NBJ, RP, true, 16>), grid, dim3(256), 0, s, x, ex, k, renorm,
+          MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_t1<SC, XT, NBJ, RP, true, 16>), grid, dim3(256), 0, s, x, ex, k, renorm,
                              logits, idx_in, idx_ws, gate_ws, idx_user, gate_user, h, bps);
       };
-      if (nbj <= 1) go(IC<1>{}, IC<4>{});
-      else go(IC<2>{}, IC<2>{});
+      if (nbj <= 1) go(IC<1>{}, IC<2>{});
+      else go(IC<2>{}, IC<1>{});
     });
   });
   const int32_t* idx = from_logits ? idx_ws : idx_in;
   const float* gate = from_logits ? gate_ws : gate_in;
   const int nbi = (ex.I / 32 + 15) / 16;
-  dim3 grid((ex.H + 15) / 16);
+  const size_t lds = (size_t)k * ex.I / 32 * 36 * sizeof(float);
+  const bool hlds = nbi == 1 && k <= 8 && (int64_t)k * ex.I <= 128 * 4 * kHRegs;
+  dim3 grid((ex.H + 7) / 8);
   with_scheme(ex.scheme, [&](auto S) {
     constexpr int SC = decltype(S)::value;
-    if (nbi <= 1) hipLaunchKernelGGL((k_down_t1<SC, 1>), grid, dim3(256), 0, s, ex, k, idx, gate, h, y);
-    else if (nbi <= 2) hipLaunchKernelGGL((k_down_t1<SC, 2>), grid, dim3(256), 0, s, ex, k, idx, gate, h, y);
-    else if (nbi <= 4) hipLaunchKernelGGL((k_down_t1<SC, 4>), grid, dim3(256), 0, s, ex, k, idx, gate, h, y);
-    else hipLaunchKernelGGL((k_down_t1<SC, 8>), grid, dim3(256), 0, s, ex, k, idx, gate, h, y);
+    if (hlds) {
+      MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_t1_lds<SC, 1, 8>), grid, dim3(128), lds, s, ex, k, idx, gate, h, y);
+      return;
+    }
+    auto go = [&](auto NBJc) {
+      constexpr int NBJ = decltype(NBJc)::value;
+      MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_t1<SC, NBJ>), grid, dim3(128), 0, s, ex, k, idx, gate, h, y);
+    };
+    if (nbi <= 1) go(IC<1>{});
+    else if (nbi <= 2) go(IC<2>{});
+    else if (nbi <= 4) go(IC<4>{});
+    else go(IC<8>{});
   });
   return hipGetLastError();
 }
@@ -345,7 +424,7 @@ hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsD
       auto go = [&](auto NBJc, auto RPc) {
         constexpr int NBJ = decltype(NBJc)::value, RP = decltype(RPc)::value;
         dim3 grid((ex.I + 4 * RP - 1) / (4 * RP), maxu);
-        hipLaunchKernelGGL((k_gate_up_grouped<SC, XT, NBJ, RP>), grid, dim3(256), 0, s, x, ex, k, g.uniq, g.n_uniq,
+        MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_grouped<SC, XT, NBJ, RP>), grid, dim3(256), 0, s, x, ex, k, g.uniq, g.n_uniq,
                            g.counts, g.offsets, g.perm, h);
       };
       if (nbj <= 1) go(IC<1>{}, IC<4>{});
@@ -357,14 +436,14 @@ hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsD
   dim3 grid((ex.H + 15) / 16, maxu);
   with_scheme(ex.scheme, [&](auto S) {
     constexpr int SC = decltype(S)::value;
-    if (nbi <= 1) hipLaunchKernelGGL((k_down_grouped<SC, 1>), grid, dim3(256), 0, s, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h, out);
-    else if (nbi <= 2) hipLaunchKernelGGL((k_down_grouped<SC, 2>), grid, dim3(256), 0, s, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h, out);
-    else if (nbi <= 4) hipLaunchKernelGGL((k_down_grouped<SC, 4>), grid, dim3(256), 0, s, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h, out);
-    else hipLaunchKernelGGL((k_down_grouped<SC, 8>), grid, dim3(256), 0, s, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h, out);
+    if (nbi <= 1) MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_grouped<SC, 1>), grid, dim3(256), 0, s, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h, out);
+    else if (nbi <= 2) MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_grouped<SC, 2>), grid, dim3(256), 0, s, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h, out);
+    else if (nbi <= 4) MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_grouped<SC, 4>), grid, dim3(256), 0, s, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h, out);
+    else MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_grouped<SC, 8>), grid, dim3(256), 0, s, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h, out);
   });
   if (gate) {
     dim3 cg((unsigned)(((ex.H + 255) / 256) * (int64_t)T));
-    hipLaunchKernelGGL(k_combine, cg, dim3(256), 0, s, T, ex.H, k, gate, ys, y);
+    MOE_LAUNCH(MOE_KERNEL_COMBINE, k_combine, cg, dim3(256), 0, s, T, ex.H, k, gate, ys, y);
   }
   return hipGetLastError();
 }

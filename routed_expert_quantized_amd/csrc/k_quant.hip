@@ -70,8 +70,8 @@ hipError_t launch_quantize(const float* w, int64_t rows, int K, int scheme, uint
   const int64_t nblocks = rows * (K / 32);
   if (nblocks == 0) return hipSuccess;
   dim3 grid((unsigned)((nblocks + 255) / 256));
-  if (scheme == MOE_Q_SYM8) hipLaunchKernelGGL(k_quantize<MOE_Q_SYM8>, grid, dim3(256), 0, s, w, nblocks, codes, scales);
-  else hipLaunchKernelGGL(k_quantize<MOE_Q_INT4>, grid, dim3(256), 0, s, w, nblocks, codes, scales);
+  if (scheme == MOE_Q_SYM8) MOE_LAUNCH(MOE_KERNEL_QUANTIZE, k_quantize<MOE_Q_SYM8>, grid, dim3(256), 0, s, w, nblocks, codes, scales);
+  else MOE_LAUNCH(MOE_KERNEL_QUANTIZE, k_quantize<MOE_Q_INT4>, grid, dim3(256), 0, s, w, nblocks, codes, scales);
   return hipGetLastError();
 }
 

@@ -2,30 +2,41 @@
 //
 // [LR] "QwenのMoEルーターを観測してホットエキスパートを先読みしても速くならなかった" (lilting.ch),
 //      section "ルーターをフックする": the router is a gate linear, a softmax and a top-k.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace moe {
 
 // ---------------------------------------------------------------- logits, few tokens
 // One wave per expert row: logits[t][e] = R[e] . x[t] in fp32, for every token.
-// Each lane reads float4 chunks of the row (coalesced 1 KiB per wave load).
-template <int XT>
-__global__ __launch_bounds__(256) void k_logits_rows(const void* __restrict__ x, int T, int H,
-                                                     const float* __restrict__ R, int E,
-                                                     float* __restrict__ logits) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + wave;
-  if (e >= E) return;
+// The row is loaded once into registers (NCH float4 chunks per lane, all loads
+// issued together) and reused for each token.
+template <int XT, int NCH>
+__global__ __launch_bounds__(64) void k_logits_rows(const void* __restrict__ x, int T, int H,
+                                                    const float* __restrict__ R, int E,
+                                                    float* __restrict__ logits) {
+  const int lane = threadIdx.x;
+  const int e = blockIdx.x;
   const float* row = R + (int64_t)e * H;
+  float4 r[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i = lane * 4 + 256 * c;
+    r[c] = i < H ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   for (int t = 0; t < T; ++t) {
     float acc = 0.0f;
-    for (int i = lane * 4; i < H; i += 256) {
-      const float4 r = *reinterpret_cast<const float4*>(row + i);
-      const float4 v = load_x4<XT>(x, (int64_t)t * H + i);
-      acc = fmaf(r.x, v.x, acc);
-      acc = fmaf(r.y, v.y, acc);
-      acc = fmaf(r.z, v.z, acc);
-      acc = fmaf(r.w, v.w, acc);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int i = lane * 4 + 256 * c;
+      if (i < H) {
+        const float4 v = load_x4<XT>(x, (int64_t)t * H + i);
+        acc = fmaf(r[c].x, v.x, acc);
+        acc = fmaf(r[c].y, v.y, acc);
+        acc = fmaf(r[c].z, v.z, acc);
+        acc = fmaf(r[c].w, v.w, acc);
+      }
     }
     acc = wave_sum(acc);
     if (lane == 0) logits[(int64_t)t * E + e] = acc;
@@ -197,17 +208,25 @@ hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R,
   if (T >= kTiledLogitsMinT) {
     dim3 grid((T + 63) / 64, (E + 63) / 64);
     switch (xtype) {
-      case MOE_F32: hipLaunchKernelGGL(k_logits_tiled<MOE_F32>, grid, dim3(256), 0, s, x, T, H, R, E, logits); break;
-      case MOE_F16: hipLaunchKernelGGL(k_logits_tiled<MOE_F16>, grid, dim3(256), 0, s, x, T, H, R, E, logits); break;
-      default:      hipLaunchKernelGGL(k_logits_tiled<MOE_BF16>, grid, dim3(256), 0, s, x, T, H, R, E, logits); break;
+      case MOE_F32: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, k_logits_tiled<MOE_F32>, grid, dim3(256), 0, s, x, T, H, R, E, logits); break;
+      case MOE_F16: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, k_logits_tiled<MOE_F16>, grid, dim3(256), 0, s, x, T, H, R, E, logits); break;
+      default:      MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, k_logits_tiled<MOE_BF16>, grid, dim3(256), 0, s, x, T, H, R, E, logits); break;
     }
   } else {
-    dim3 grid((E + 3) / 4);
-    switch (xtype) {
-      case MOE_F32: hipLaunchKernelGGL(k_logits_rows<MOE_F32>, grid, dim3(256), 0, s, x, T, H, R, E, logits); break;
-      case MOE_F16: hipLaunchKernelGGL(k_logits_rows<MOE_F16>, grid, dim3(256), 0, s, x, T, H, R, E, logits); break;
-      default:      hipLaunchKernelGGL(k_logits_rows<MOE_BF16>, grid, dim3(256), 0, s, x, T, H, R, E, logits); break;
-    }
+    const int nch = (H + 255) / 256;
+    auto go = [&](auto NC) {
+      constexpr int N = decltype(NC)::value;
+      switch (xtype) {
+        case MOE_F32: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_F32, N>), dim3(E), dim3(64), 0, s, x, T, H, R, E, logits); break;
+        case MOE_F16: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_F16, N>), dim3(E), dim3(64), 0, s, x, T, H, R, E, logits); break;
+        default:      MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_BF16, N>), dim3(E), dim3(64), 0, s, x, T, H, R, E, logits); break;
+      }
+    };
+    if (nch <= 1) go(std::integral_constant<int, 1>{});
+    else if (nch <= 2) go(std::integral_constant<int, 2>{});
+    else if (nch <= 4) go(std::integral_constant<int, 4>{});
+    else if (nch <= 8) go(std::integral_constant<int, 8>{});
+    else go(std::integral_constant<int, 16>{});
   }
   return hipGetLastError();
 }
@@ -216,21 +235,21 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int renorm, int
                        int32_t* idx2, float* gate2, hipStream_t s) {
   dim3 grid((T + 3) / 4);
   const int vpl = (E + 63) / 64;
-  if (vpl <= 1)      hipLaunchKernelGGL(k_topk<1>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
-  else if (vpl <= 2) hipLaunchKernelGGL(k_topk<2>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
-  else if (vpl <= 4) hipLaunchKernelGGL(k_topk<4>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
-  else if (vpl <= 8) hipLaunchKernelGGL(k_topk<8>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
-  else               hipLaunchKernelGGL(k_topk<16>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
+  if (vpl <= 1)      MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<1>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
+  else if (vpl <= 2) MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<2>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
+  else if (vpl <= 4) MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<4>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
+  else if (vpl <= 8) MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<8>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
+  else               MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<16>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
   return hipGetLastError();
 }
 
 hipError_t launch_group(const int32_t* idx, int T, int k, int E, const GroupBufs& g, hipStream_t s) {
   const int C = (T + 63) / 64;
-  hipLaunchKernelGGL(k_group_mask, dim3(C), dim3(256), 0, s, idx, T, k, E, g.mask);
-  hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(1024), 0, s, g.mask, C, E, g.base, g.counts, g.offsets, g.uniq,
+  MOE_LAUNCH(MOE_KERNEL_GROUP, k_group_mask, dim3(C), dim3(256), 0, s, idx, T, k, E, g.mask);
+  MOE_LAUNCH(MOE_KERNEL_GROUP, k_group_scan, dim3(1), dim3(1024), 0, s, g.mask, C, E, g.base, g.counts, g.offsets, g.uniq,
                      g.n_uniq);
   const int64_t n = (int64_t)T * k;
-  hipLaunchKernelGGL(k_group_scatter, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, T, k, E, g.mask,
+  MOE_LAUNCH(MOE_KERNEL_GROUP, k_group_scatter, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, T, k, E, g.mask,
                      g.base, g.perm);
   return hipGetLastError();
 }

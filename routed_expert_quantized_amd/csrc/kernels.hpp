@@ -1,13 +1,31 @@
 // kernels.hpp — launch wrappers of the gfx950 kernels, called by the C ABI layer.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 
 namespace moe {
 
+// Benchmark timer (moe_timer_start / moe_timer_read): hands out the next event
+// pair when launches of kernel family `kid` are being timed.
+bool timer_take(int kid, hipEvent_t* start, hipEvent_t* stop);
+
+// Launch a kernel; when its family is being timed, launch it through
+// hipExtLaunchKernelGGL so the events bracket exactly this kernel.
+#define MOE_LAUNCH(KID, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                    \
+  do {                                                                                            \
+    hipEvent_t moe_ev_a_, moe_ev_b_;                                                              \
+    if (::moe::timer_take((KID), &moe_ev_a_, &moe_ev_b_))                                          \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, moe_ev_a_, moe_ev_b_, 0, __VA_ARGS__); \
+    else                                                                                          \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                         \
+  } while (0)
+
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
 constexpr int kTiledLogitsMinT = 128;  // from this many tokens the router logits run as a tiled GEMM
+
 
 // Device buffers of the token-by-expert grouping.
 struct GroupBufs {

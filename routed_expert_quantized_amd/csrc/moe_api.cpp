@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "kernels.hpp"
 #include "moe.h"
@@ -141,9 +142,59 @@ moe_status run_experts(const void* x, int32_t xtype, int32_t T, const moe::Exper
                     "decode (grouped)");
 }
 
+// Benchmark timer state (see moe_timer_start).
+struct KernelTimer {
+  int kid = -1;
+  int cap = 0;
+  int used = 0;
+  std::vector<hipEvent_t> start, stop;
+};
+KernelTimer g_timer;
+
 }  // namespace
 
+namespace moe {
+bool timer_take(int kid, hipEvent_t* start, hipEvent_t* stop) {
+  if (g_timer.kid != kid || g_timer.used >= g_timer.cap) return false;
+  *start = g_timer.start[g_timer.used];
+  *stop = g_timer.stop[g_timer.used];
+  ++g_timer.used;
+  return true;
+}
+}  // namespace moe
+
 extern "C" {
+
+moe_status moe_timer_start(int32_t kernel, int32_t capacity) {
+  if (kernel < 0 || kernel >= MOE_KERNEL_COUNT) return fail(MOE_ERR_INVALID_ARG, "unknown kernel id %d", kernel);
+  if (capacity < 1 || capacity > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "capacity %d outside [1, 2^20]", capacity);
+  while ((int)g_timer.start.size() < capacity) {
+    hipEvent_t a, b;
+    hipError_t e = hipEventCreate(&a);
+    if (e == hipSuccess) e = hipEventCreate(&b);
+    if (e != hipSuccess) return hip_status(e, "timer events");
+    g_timer.start.push_back(a);
+    g_timer.stop.push_back(b);
+  }
+  g_timer.kid = kernel;
+  g_timer.cap = capacity;
+  g_timer.used = 0;
+  return ok();
+}
+
+moe_status moe_timer_read(float* ms, int32_t capacity, int32_t* count) {
+  if (!ms || !count) return fail(MOE_ERR_INVALID_ARG, "ms or count is NULL");
+  const int n = std::min(g_timer.used, (int)capacity);
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = hipEventSynchronize(g_timer.stop[i]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms[i], g_timer.start[i], g_timer.stop[i]);
+    if (e != hipSuccess) return hip_status(e, "timer read");
+  }
+  *count = n;
+  g_timer.kid = -1;
+  g_timer.used = 0;
+  return ok();
+}
 
 size_t moe_workspace_bytes(int32_t T, int32_t E, int32_t H, int32_t I, int32_t k, int32_t scheme) {
   if (!shape_ok(T, E, H, I, k) || (scheme != MOE_Q_SYM8 && scheme != MOE_Q_INT4)) return 0;

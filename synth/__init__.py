@@ -186,3 +186,28 @@ def redraw_tokens(x32: np.ndarray, tokens, seed: int, workload: int, layer: int,
         x32[t] = g.standard_normal(x32.shape[1], dtype=np.float32)
         if const_channel:
             x32[t, -1] = 1.0
+
+
+def draw_step_x(w: Workload, seed: int, step: int, T: int | None = None) -> np.ndarray:
+    """Activations of one decode/prefill step, with the workload's structure
+    (constant channel under a popularity skew, token reuse), encoded."""
+    T = w.T if T is None else T
+    x32 = draw_x(rng(seed, w.wid, 100000 + step, 0, 0), T, w.H)
+    if w.zipf_s > 0:
+        x32[:, -1] = 1.0
+    if w.reuse_p > 0:
+        apply_reuse(x32, rng(seed, w.wid, 100000 + step, 0, 4), w.reuse_p)
+    return encode_x(x32, w.xtype)
+
+
+def torch_expert_chunks(w: Workload, seed: int, layer: int, chunk: int, device):
+    """Device fp32 draws of a layer's experts, `chunk` experts at a time, from a
+    seeded torch generator on the device: yields (e0, w_gate_up [c][2I][H], w_down [c][H][I])."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 1000003 + w.wid * 7919 + layer) & 0x7FFFFFFFFFFFFFFF)
+    for e0 in range(0, w.E, chunk):
+        c = min(chunk, w.E - e0)
+        wgu = torch.randn((c, 2 * w.I, w.H), generator=g, device=device, dtype=torch.float32).mul_(w.weight_std)
+        wd = torch.randn((c, w.H, w.I), generator=g, device=device, dtype=torch.float32).mul_(w.weight_std)
+        yield e0, wgu, wd

@@ -77,6 +77,25 @@ def test_route_many_experts_and_max_k():
         assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
 
 
+@pytest.mark.parametrize("E,k", [(16, 4), (256, 8), (64, 16), (1000, 10)])
+def test_route_exact_ties_go_to_lower_ids(E, k):
+    g = np.random.default_rng(E + k)
+    R = (g.standard_normal((E, 64)) * 0.3).astype(np.float32)
+    # all-zero activations: every logit is 0, so the first k ids win with equal gates
+    idx, gate = rq.moe_route(torch.zeros((3, 64), device="cuda"), torch.from_numpy(R).cuda(), k)
+    assert (idx.cpu().numpy() == np.arange(k)).all()
+    assert np.allclose(gate.cpu().numpy(), 1.0 / k, atol=GATE_ATOL)
+    # duplicated router rows: equal logits, the lower id first
+    x = g.standard_normal((4, 64)).astype(np.float32)
+    R2 = R.copy()
+    R2[E - 1] = R2[E // 2]
+    R2[E - 2] = R2[1]
+    ridx, rgate = oracle.route(x, R2, k)
+    gi, gg = rq.moe_route(torch.from_numpy(x).cuda(), torch.from_numpy(R2).cuda(), k)
+    assert np.array_equal(gi.cpu().numpy(), ridx)
+    assert np.abs(gg.cpu().numpy() - rgate).max() <= GATE_ATOL
+
+
 # ---------------------------------------------------------------- grouping
 @pytest.mark.parametrize("T,k,E", [(1, 8, 256), (63, 10, 512), (64, 10, 512), (65, 3, 8), (16, 10, 512),
                                    (2048, 8, 256), (300, 16, 1024), (5, 4, 4)])
@@ -159,3 +178,24 @@ def test_layer_is_deterministic():
     a = rq.moe_layer_forward(xd, Rd, ex, w.k)[0].clone()
     b = rq.moe_layer_forward(xd, Rd, ex, w.k)[0]
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode40"])
+def test_single_token_paths_agree_with_oracle(name):
+    """One token: the fused two-kernel path (default) and the three-kernel
+    gathered path (forced) both match the oracle, and both route identically."""
+    w = synth.WORKLOADS[name]
+    outs = []
+    for layer in range(3):
+        li = enforce_gap(w, synth.draw_layer(w, seed=5, layer=layer, with_experts=False), seed=5, layer=layer)
+        ridx, rgate = oracle.route(li.x, li.R, w.k)
+        ex = device_pool(w, 5, layer, np.unique(ridx))
+        rex, m = oracle_compact(w, 5, layer, np.unique(ridx))
+        ref = oracle.gather_forward(li.x, rex, remap(ridx, m), rgate)
+        xd, Rd = to_dev_x(li.x, w.xtype), torch.from_numpy(li.R).cuda()
+        for flags in (rq.MOE_FLAG_RENORM, rq.MOE_FLAG_RENORM | rq.MOE_FLAG_PATH_GATHER):
+            y, idx, gate = rq.moe_layer_forward(xd, Rd, ex, w.k, flags)
+            assert np.array_equal(idx.cpu().numpy(), ridx)
+            assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
+            assert rel_norm_err(y.cpu().numpy(), ref) <= Y_REL_NORM
+            outs.append(y.cpu().numpy())
