@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--timer-steps", type=int, default=16, help="steps of the per-kernel event timing pass")
+    ap.add_argument("--path", choices=["auto", "gather", "gemm"], default="auto",
+                    help="expert path: the library's choice, the gathered matvec or the grouped MFMA GEMM")
     return ap.parse_args()
 
 
@@ -167,12 +169,15 @@ def main():
     log(f"setup {time.perf_counter() - t_setup:.1f} s, pool {sum(p.w_gate_up.numel() + p.w_down.numel() for p in pools) / 1e9:.1f} GB codes")
 
     layers_per_step = nl if multi else 1
+    path_flag = {"auto": 0, "gather": rq.MOE_FLAG_PATH_GATHER, "gemm": rq.MOE_FLAG_PATH_GEMM}[args.path]
+    # the library's own choice (kept in step with moe_api.cpp): the GEMM path for T > 1
+    gemm = args.path == "gemm" or (args.path == "auto" and w.T > 1)
 
     def run_layers(step):
         ls = range(nl) if multi else [step % nl]
         for l in ls:
-            rq.moe_layer_forward(xbuf, routers[l], pools[l], w.k, rq.MOE_FLAG_RENORM, ws=ws, out=ys[l],
-                                 return_routing=False)
+            rq.moe_layer_forward(xbuf, routers[l], pools[l], w.k, rq.MOE_FLAG_RENORM | path_flag, ws=ws,
+                                 out=ys[l], return_routing=False)
 
     # eager warm-up (also checks every call succeeds)
     xbuf.copy_(xs[0])
@@ -239,16 +244,28 @@ def main():
         torch.cuda.synchronize()
         return float(np.mean(t.ms)) * 1e3 if t.ms else None  # microseconds
 
-    gu_us = timed_kernel(rq.MOE_KERNEL_GATE_UP, args.timer_steps)
-    dn_us = timed_kernel(rq.MOE_KERNEL_DOWN, args.timer_steps)
-    rt_us = timed_kernel(rq.MOE_KERNEL_ROUTE_LOGITS, args.timer_steps)
-    # algorithmic bytes of one launch of the dominant kernel
+    kids = {"route_logits": rq.MOE_KERNEL_ROUTE_LOGITS}
+    if w.T > 1:
+        kids.update(topk=rq.MOE_KERNEL_TOPK, group=rq.MOE_KERNEL_GROUP, combine=rq.MOE_KERNEL_COMBINE)
+    if gemm:
+        kids.update(gemm_gate_up=rq.MOE_KERNEL_GEMM_GATE_UP, gemm_down=rq.MOE_KERNEL_GEMM_DOWN)
+        dom = "gemm_gate_up"
+    else:
+        kids.update(gate_up=rq.MOE_KERNEL_GATE_UP, down=rq.MOE_KERNEL_DOWN)
+        dom = "gate_up"
+    kern_us = {name: timed_kernel(kid, args.timer_steps) for name, kid in kids.items()}
+    gu_us = kern_us[dom]
+    # algorithmic bytes of one launch of the dominant kernel (gate/up stage):
+    # routed gate/up codes + scales, the activations, and the SwiGLU output
+    # (fp32 on the matvec path, fp16 on the GEMM path); single token: + router logits
     xbytes = w.T * w.H * (4 if w.xtype == 0 else 2)
-    # gathered gate/up: routed gate/up codes + scales, x, router logits (single token,
-    # where the top-k runs inside this kernel) and the fp32 SwiGLU output
-    gu_alg = uniq_mean * gate_up_bytes(w) + xbytes + w.T * w.k * w.I * 4 + (w.E * 4 if w.T == 1 else 0)
-    kname = "gathered gate/up + SwiGLU" + (" (with the top-k)" if w.T == 1 else " (grouped)")
+    hbytes = w.T * w.k * w.I * (2 if gemm else 4)
+    gu_alg = uniq_mean * gate_up_bytes(w) + xbytes + hbytes + (w.E * 4 if (w.T == 1 and not gemm) else 0)
+    kname = ("grouped MFMA GEMM gate/up + SwiGLU" if gemm else
+             "gathered gate/up + SwiGLU" + (" (with the top-k)" if w.T == 1 else " (grouped)"))
     achieved = gu_alg / (gu_us * 1e-6) / 1e9
+    gu_flops = 2.0 * w.T * w.k * 2 * w.I * w.H
+    mfma_tflops = gu_flops / (gu_us * 1e-6) / 1e12
 
     traffic = None
     tf = os.path.join(ROOT, "profiles", f"traffic_gate_up_{w.name}.json")
@@ -270,23 +287,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16xf16->f32 (mfma)" if gemm else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
                    "codec": "sym8" if w.scheme == 0 else "int4",
                    "x": {0: "f32", 1: "f16", 2: "bf16"}[w.xtype], "layers_per_step": layers_per_step,
-                   "layer_copies": nl, "fresh_x": nx, "graph": not args.no_graph},
+                   "layer_copies": nl, "fresh_x": nx, "graph": not args.no_graph,
+                   "path": "gemm" if gemm else "gather"},
         "us_per_layer": round(t_layer_s * 1e6, 3),
         "step_tokens_per_s": round(w.T / (elapsed_ms * 1e-3 / K), 1),
         "routed_bytes_per_layer": int(routed_bytes),
         "unique_experts_per_layer": round(uniq_mean, 2),
         "routed_hbm_gbps": round(routed_gbps, 1),
         "routed_hbm_frac": round(routed_gbps / HBM_PEAK_GBPS, 4),
-        "kernel_us": {"gate_up": round(gu_us, 3), "down": round(dn_us, 3), "route_logits": round(rt_us, 3)},
+        "kernel_us": {n: round(v, 3) for n, v in kern_us.items()},
         "roofline": {"kernel": kname, "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": int(gu_alg), "avg_launch_us": round(gu_us, 3)},
+                     "algorithmic_bytes_per_launch": int(gu_alg), "avg_launch_us": round(gu_us, 3),
+                     **({"mfma_tflops": round(mfma_tflops, 1), "mfma_peak_tflops_f16": 2500.0,
+                         "mfma_frac": round(mfma_tflops / 2500.0, 4)} if gemm else {})},
         "kernel_source_sha": sha,
     }
     if not args.no_cpu_baseline:

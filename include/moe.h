@@ -68,8 +68,11 @@ typedef enum { MOE_Q_SYM8 = 0, MOE_Q_INT4 = 1 } moe_qscheme;
 enum {
   /* Renormalise the k gates of each token so they sum to one. */
   MOE_FLAG_RENORM = 1u,
-  /* Expert-path selection; with neither bit set the library chooses.
-   * GATHER: gathered matvec kernels. GEMM: grouped MFMA GEMM (x bf16/f16 only). */
+  /* Expert-path selection; with neither bit set the library uses the gathered
+   * matvec kernels for T == 1 and the grouped MFMA GEMM for T > 1.
+   * GATHER: gathered matvec kernels (fp32 arithmetic on dequantised codes).
+   * GEMM: grouped fp16 MFMA GEMM, fp32 accumulation (weights rounded once to
+   *       fp16 as code * scale, activations staged as fp16, h stored as fp16). */
   MOE_FLAG_PATH_GATHER = 2u,
   MOE_FLAG_PATH_GEMM = 4u
 };

@@ -13,6 +13,7 @@
 // Lane mapping: a lane owns whole quantisation blocks (32 codes, one scale), so
 // each code row is read with coalesced 16-byte loads, dequantised in registers
 // and the scale applied once per block partial.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -242,16 +243,81 @@ __global__ __launch_bounds__(128) void k_down_t1(ExpertsDev ex, int k, const int
 }
 
 // ------------------------------------------------------------------ T > 1, grouped
+// Rows staged in LDS: each 32-element block of a row is followed by 16 bytes of
+// padding, so the lanes of a wave (each reading its own block) spread over the
+// banks. Copies go in 16-byte chunks, 8 loads per thread issued before their
+// stores.
+__device__ __forceinline__ int lds_block_stride(int elem_bytes) { return 32 * elem_bytes + 16; }
+
+template <typename SrcRow>
+__device__ __forceinline__ void stage_rows(uint8_t* lds, int row_stride, int nrow, int elems, int elem_bytes,
+                                           SrcRow src_row) {
+  const int blk = 32 * elem_bytes, cpb = blk / 16, pblk = blk + 16;
+  const int chunks = elems * elem_bytes / 16, total = nrow * chunks;
+  const int tid = (int)threadIdx.x, nth = (int)blockDim.x;
+  for (int base = 0; base < total; base += 8 * nth) {
+    uint4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int c = min(base + q * nth + tid, total - 1);
+      v[q] = *reinterpret_cast<const uint4*>(src_row(c / chunks) + 16 * (c % chunks));
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int c = base + q * nth + tid;
+      if (c < total) {
+        const int i = c / chunks, j = c % chunks;
+        *reinterpret_cast<uint4*>(lds + i * row_stride + (j / cpb) * pblk + 16 * (j % cpb)) = v[q];
+      }
+    }
+  }
+}
+
+// Activations of block b from an LDS row (layout of stage_rows).
+template <int SCHEME, int XT>
+__device__ __forceinline__ void xreg_from_lds(XReg<SCHEME, XT>& r, const uint8_t* p) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  if constexpr (XT == MOE_F16) {
+    uint32_t nat[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = q[i];
+      nat[4 * i] = v.x; nat[4 * i + 1] = v.y; nat[4 * i + 2] = v.z; nat[4 * i + 3] = v.w;
+    }
+    r.h = xblock_from_pairs<SCHEME>(nat);
+  } else if constexpr (XT == MOE_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = q[i];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        r.f[8 * i + 2 * j] = bf16_bits_to_f32((uint16_t)(w[j] & 0xFFFF));
+        r.f[8 * i + 2 * j + 1] = bf16_bits_to_f32((uint16_t)(w[j] >> 16));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 v = reinterpret_cast<const float4*>(p)[i];
+      r.f[4 * i] = v.x; r.f[4 * i + 1] = v.y; r.f[4 * i + 2] = v.z; r.f[4 * i + 3] = v.w;
+    }
+  }
+}
+
 // Grid: (blocks_per_u, max unique experts). Workgroup column u serves expert
-// uniq[u] for all of its n_e assignments: the code rows are loaded once and
-// dotted with each routed token, so a batch reads each routed expert once.
+// uniq[u] for all of its n_e assignments: the code rows are loaded once, the
+// routed tokens' activations are staged in LDS CH at a time, and every row is
+// dotted with each of them, so a batch reads each routed expert once.
 template <int SCHEME, int XT, int NBJ, int RP>
 __global__ __launch_bounds__(256) void k_gate_up_grouped(const void* __restrict__ x, ExpertsDev ex, int k,
                                                          const int32_t* __restrict__ uniq,
                                                          const int32_t* __restrict__ n_uniq,
                                                          const int32_t* __restrict__ counts,
                                                          const int32_t* __restrict__ offsets,
-                                                         const int32_t* __restrict__ perm, float* __restrict__ h) {
+                                                         const int32_t* __restrict__ perm, float* __restrict__ h,
+                                                         int CH) {
+  extern __shared__ uint8_t xs[];
   const int u = blockIdx.y;
   if (u >= *n_uniq) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -275,40 +341,50 @@ __global__ __launch_bounds__(256) void k_gate_up_grouped(const void* __restrict_
       su[r][j] = valid * f16_bits_to_f32(ex.sgu[urow * NB + b]);
     }
   }
-  for (int a = 0; a < cnt; ++a) {
-    const int f = perm[beg + a];
-    const int t = f / k;
-    float ag[RP], au[RP];
+  constexpr int xbytes = XT == MOE_F32 ? 4 : 2;
+  const int pblk = lds_block_stride(xbytes), stride = NB * pblk;
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  for (int a0 = 0; a0 < cnt; a0 += CH) {
+    const int nt = min(CH, cnt - a0);
+    __syncthreads();
+    stage_rows(xs, stride, nt, H, xbytes,
+               [&](int i) { return xb + (int64_t)(perm[beg + a0 + i] / k) * H * xbytes; });
+    __syncthreads();
+    for (int i = 0; i < nt; ++i) {
+      const int f = perm[beg + a0 + i];
+      float ag[RP], au[RP];
 #pragma unroll
-    for (int r = 0; r < RP; ++r) ag[r] = au[r] = 0.0f;
+      for (int r = 0; r < RP; ++r) ag[r] = au[r] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NBJ; ++j) {
-      XReg<SCHEME, XT> xr;
-      load_xreg<SCHEME, XT>(xr, x, (int64_t)t * H, min(lane + 64 * j, NB - 1));
+      for (int j = 0; j < NBJ; ++j) {
+        XReg<SCHEME, XT> xr;
+        xreg_from_lds<SCHEME, XT>(xr, xs + i * stride + min(lane + 64 * j, NB - 1) * pblk);
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+          ag[r] = fmaf(sg[r][j], xdot<SCHEME, XT>(cg[r][j], xr), ag[r]);
+          au[r] = fmaf(su[r][j], xdot<SCHEME, XT>(cu[r][j], xr), au[r]);
+        }
+      }
 #pragma unroll
       for (int r = 0; r < RP; ++r) {
-        ag[r] = fmaf(sg[r][j], xdot<SCHEME, XT>(cg[r][j], xr), ag[r]);
-        au[r] = fmaf(su[r][j], xdot<SCHEME, XT>(cu[r][j], xr), au[r]);
+        const float g = wave_sum(ag[r]);
+        const float v = wave_sum(au[r]);
+        if (lane == 0 && n0 + r < I) h[(int64_t)f * I + n0 + r] = silu(g) * v;
       }
-    }
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      const float g = wave_sum(ag[r]);
-      const float v = wave_sum(au[r]);
-      if (lane == 0 && n0 + r < I) h[(int64_t)f * I + n0 + r] = silu(g) * v;
     }
   }
 }
 
 // Grid: (ceil(H / 16), max unique experts). ys[f][m] = row m of expert uniq[u] . h[f]
-// for each assignment f of that expert.
+// for each assignment f of that expert; the h rows are staged in LDS CH at a time.
 template <int SCHEME, int NBJ>
 __global__ __launch_bounds__(256) void k_down_grouped(ExpertsDev ex, int k, const int32_t* __restrict__ uniq,
                                                       const int32_t* __restrict__ n_uniq,
                                                       const int32_t* __restrict__ counts,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ perm, const float* __restrict__ h,
-                                                      float* __restrict__ ys) {
+                                                      float* __restrict__ ys, int CH) {
+  extern __shared__ uint8_t hsm[];
   const int u = blockIdx.y;
   if (u >= *n_uniq) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -327,25 +403,31 @@ __global__ __launch_bounds__(256) void k_down_grouped(ExpertsDev ex, int k, cons
     c[j] = load_block<SCHEME>(ex.wd + row * rb, b);
     sc[j] = (ll + 16 * j < NBI ? 1.0f : 0.0f) * f16_bits_to_f32(ex.sd[row * NBI + b]);
   }
-  for (int a = 0; a < cnt; ++a) {
-    const int f = perm[beg + a];
-    float part = 0.0f;
+  const int pblk = lds_block_stride(4), stride = NBI * pblk;
+  const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
+  for (int a0 = 0; a0 < cnt; a0 += CH) {
+    const int nt = min(CH, cnt - a0);
+    __syncthreads();
+    stage_rows(hsm, stride, nt, I, 4, [&](int i) { return hb + (int64_t)perm[beg + a0 + i] * I * 4; });
+    __syncthreads();
+    for (int i = 0; i < nt; ++i) {
+      const int f = perm[beg + a0 + i];
+      float part = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NBJ; ++j) {
-      const int b = ll + 16 * j;
-      if (b < NBI) {
+      for (int j = 0; j < NBJ; ++j) {
+        const int b = min(ll + 16 * j, NBI - 1);
         float hv[32];
-        const float4* hp = reinterpret_cast<const float4*>(h + (int64_t)f * I + 32 * b);
+        const float4* hp = reinterpret_cast<const float4*>(hsm + i * stride + b * pblk);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float4 v = hp[i];
-          hv[4 * i] = v.x; hv[4 * i + 1] = v.y; hv[4 * i + 2] = v.z; hv[4 * i + 3] = v.w;
+        for (int q = 0; q < 8; ++q) {
+          const float4 v = hp[q];
+          hv[4 * q] = v.x; hv[4 * q + 1] = v.y; hv[4 * q + 2] = v.z; hv[4 * q + 3] = v.w;
         }
         part = fmaf(sc[j], block_dot<SCHEME>(c[j], hv), part);
       }
+      part = row_sum16(part);
+      if (ll == 0 && m < H) ys[(int64_t)f * H + m] = part;
     }
-    part = row_sum16(part);
-    if (ll == 0 && m < H) ys[(int64_t)f * H + m] = part;
   }
 }
 
@@ -413,19 +495,25 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
   return hipGetLastError();
 }
 
+// Rows per LDS chunk for the grouped kernels: up to 16, within 64 KiB.
+static int lds_chunk_rows(int row_stride) { return std::max(1, std::min(16, 65536 / row_stride)); }
+
 hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsDev& ex, int k,
                                  const GroupBufs& g, const float* gate, float* h, float* ys, float* y,
                                  hipStream_t s) {
   const int maxu = (int)std::min<int64_t>((int64_t)ex.E, (int64_t)T * k);
   const int nbj = (ex.H / 32 + 63) / 64;
+  const int xbytes = xtype == MOE_F32 ? 4 : 2;
+  const int xstride = ex.H / 32 * (32 * xbytes + 16);
+  const int xch = lds_chunk_rows(xstride);
   with_scheme(ex.scheme, [&](auto S) {
     with_xtype(xtype, [&](auto X) {
       constexpr int SC = decltype(S)::value, XT = decltype(X)::value;
       auto go = [&](auto NBJc, auto RPc) {
         constexpr int NBJ = decltype(NBJc)::value, RP = decltype(RPc)::value;
         dim3 grid((ex.I + 4 * RP - 1) / (4 * RP), maxu);
-        MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_grouped<SC, XT, NBJ, RP>), grid, dim3(256), 0, s, x, ex, k, g.uniq, g.n_uniq,
-                           g.counts, g.offsets, g.perm, h);
+        MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_grouped<SC, XT, NBJ, RP>), grid, dim3(256),
+                   (size_t)xch * xstride, s, x, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h, xch);
       };
       if (nbj <= 1) go(IC<1>{}, IC<4>{});
       else go(IC<2>{}, IC<2>{});
@@ -433,18 +521,29 @@ hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsD
   });
   float* out = gate ? ys : y;  // per-slot mode writes [T][k][H] directly
   const int nbi = (ex.I / 32 + 15) / 16;
+  const int hstride = ex.I / 32 * (32 * 4 + 16);
+  const int hch = lds_chunk_rows(hstride);
+  const size_t hlds = (size_t)hch * hstride;
   dim3 grid((ex.H + 15) / 16, maxu);
   with_scheme(ex.scheme, [&](auto S) {
     constexpr int SC = decltype(S)::value;
-    if (nbi <= 1) MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_grouped<SC, 1>), grid, dim3(256), 0, s, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h, out);
-    else if (nbi <= 2) MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_grouped<SC, 2>), grid, dim3(256), 0, s, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h, out);
-    else if (nbi <= 4) MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_grouped<SC, 4>), grid, dim3(256), 0, s, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h, out);
-    else MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_grouped<SC, 8>), grid, dim3(256), 0, s, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h, out);
+    auto go = [&](auto NBJc) {
+      constexpr int NBJ = decltype(NBJc)::value;
+      MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_grouped<SC, NBJ>), grid, dim3(256), hlds, s, ex, k, g.uniq, g.n_uniq,
+                 g.counts, g.offsets, g.perm, h, out, hch);
+    };
+    if (nbi <= 1) go(IC<1>{});
+    else if (nbi <= 2) go(IC<2>{});
+    else if (nbi <= 4) go(IC<4>{});
+    else go(IC<8>{});
   });
-  if (gate) {
-    dim3 cg((unsigned)(((ex.H + 255) / 256) * (int64_t)T));
-    MOE_LAUNCH(MOE_KERNEL_COMBINE, k_combine, cg, dim3(256), 0, s, T, ex.H, k, gate, ys, y);
-  }
+  if (gate) return launch_combine(T, ex.H, k, gate, ys, y, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(int T, int H, int k, const float* gate, const float* ys, float* y, hipStream_t s) {
+  dim3 cg((unsigned)(((H + 255) / 256) * (int64_t)T));
+  MOE_LAUNCH(MOE_KERNEL_COMBINE, k_combine, cg, dim3(256), 0, s, T, H, k, gate, ys, y);
   return hipGetLastError();
 }
 

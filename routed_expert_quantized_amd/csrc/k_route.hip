@@ -11,8 +11,9 @@ namespace moe {
 // ---------------------------------------------------------------- logits, few tokens
 // One wave per expert row: logits[t][e] = R[e] . x[t] in fp32, for every token.
 // The row is loaded once into registers (NCH float4 chunks per lane, all loads
-// issued together) and reused for each token.
-template <int XT, int NCH>
+// issued together) and reused for each token; tokens go TU at a time with
+// their activation loads issued before any arithmetic.
+template <int XT, int NCH, int TU>
 __global__ __launch_bounds__(64) void k_logits_rows(const void* __restrict__ x, int T, int H,
                                                     const float* __restrict__ R, int E,
                                                     float* __restrict__ logits) {
@@ -22,24 +23,32 @@ __global__ __launch_bounds__(64) void k_logits_rows(const void* __restrict__ x, 
   float4 r[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int i = lane * 4 + 256 * c;
-    r[c] = i < H ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int i = min(lane * 4 + 256 * c, H - 4);
+    r[c] = *reinterpret_cast<const float4*>(row + i);
   }
-  for (int t = 0; t < T; ++t) {
-    float acc = 0.0f;
+  for (int t0 = 0; t0 < T; t0 += TU) {
+    float4 v[TU][NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int i = lane * 4 + 256 * c;
-      if (i < H) {
-        const float4 v = load_x4<XT>(x, (int64_t)t * H + i);
-        acc = fmaf(r[c].x, v.x, acc);
-        acc = fmaf(r[c].y, v.y, acc);
-        acc = fmaf(r[c].z, v.z, acc);
-        acc = fmaf(r[c].w, v.w, acc);
-      }
+    for (int u = 0; u < TU; ++u) {
+      const int t = min(t0 + u, T - 1);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) v[u][c] = load_x4<XT>(x, (int64_t)t * H + min(lane * 4 + 256 * c, H - 4));
     }
-    acc = wave_sum(acc);
-    if (lane == 0) logits[(int64_t)t * E + e] = acc;
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if (lane * 4 + 256 * c < H) {
+          acc = fmaf(r[c].x, v[u][c].x, acc);
+          acc = fmaf(r[c].y, v[u][c].y, acc);
+          acc = fmaf(r[c].z, v[u][c].z, acc);
+          acc = fmaf(r[c].w, v[u][c].w, acc);
+        }
+      }
+      acc = wave_sum(acc);
+      if (lane == 0 && t0 + u < T) logits[(int64_t)(t0 + u) * E + e] = acc;
+    }
   }
 }
 
@@ -216,10 +225,11 @@ hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R,
     const int nch = (H + 255) / 256;
     auto go = [&](auto NC) {
       constexpr int N = decltype(NC)::value;
+      constexpr int TU = N >= 16 ? 2 : N >= 8 ? 4 : 8;
       switch (xtype) {
-        case MOE_F32: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_F32, N>), dim3(E), dim3(64), 0, s, x, T, H, R, E, logits); break;
-        case MOE_F16: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_F16, N>), dim3(E), dim3(64), 0, s, x, T, H, R, E, logits); break;
-        default:      MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_BF16, N>), dim3(E), dim3(64), 0, s, x, T, H, R, E, logits); break;
+        case MOE_F32: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_F32, N, TU>), dim3(E), dim3(64), 0, s, x, T, H, R, E, logits); break;
+        case MOE_F16: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_F16, N, TU>), dim3(E), dim3(64), 0, s, x, T, H, R, E, logits); break;
+        default:      MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_BF16, N, TU>), dim3(E), dim3(64), 0, s, x, T, H, R, E, logits); break;
       }
     };
     if (nch <= 1) go(std::integral_constant<int, 1>{});

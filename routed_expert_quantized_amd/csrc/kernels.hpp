@@ -67,6 +67,14 @@ hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsD
                                  const GroupBufs& g, const float* gate, float* h, float* ys, float* y,
                                  hipStream_t s);
 
+// Gate-weighted combine y[t] = sum_s gate[t][s] * ys[t*k+s] (T > 1 paths).
+hipError_t launch_combine(int T, int H, int k, const float* gate, const float* ys, float* y, hipStream_t s);
+
+// Grouped MFMA GEMM path (after launch_group): gate/up + SwiGLU into fp16 h,
+// down into ys (or y itself in per-slot mode), then the combine.
+hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev& ex, int k, const GroupBufs& g,
+                               const float* gate, uint16_t* h16, float* ys, float* y, hipStream_t s);
+
 hipError_t launch_quantize(const float* w, int64_t rows, int K, int scheme, uint8_t* codes, uint16_t* scales,
                            hipStream_t s);
 

@@ -62,7 +62,7 @@ Layout layout(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
   L.uniq = take(E * 4);
   L.n_uniq = take(4);
   L.h = take(T * k * I * 4);
-  L.ys = take(T > 1 ? T * k * H * 4 : 0);
+  L.ys = take(T * k * H * 4);
   L.total = off;
   return L;
 }
@@ -128,16 +128,21 @@ moe_status check_experts(const moe_experts* ex, moe::ExpertsDev* d) {
 moe_status run_experts(const void* x, int32_t xtype, int32_t T, const moe::ExpertsDev& d, int32_t k,
                        const int32_t* idx, const float* gate, float* y, uint32_t flags, void* ws,
                        const Layout& L, hipStream_t s) {
-  if (flags & MOE_FLAG_PATH_GEMM)
-    return fail(MOE_ERR_UNSUPPORTED, "the grouped MFMA GEMM path is not available in this build");
   float* h = at<float>(ws, L.h);
-  if (T == 1)
+  // Path choice: the grouped MFMA GEMM when asked, and by default for T > 1;
+  // the gathered matvec for a single token or when asked.
+  const bool gemm = (flags & MOE_FLAG_PATH_GEMM) || (!(flags & MOE_FLAG_PATH_GATHER) && T > 1);
+  if (T == 1 && !gemm)
     return hip_status(moe::launch_decode_t1(x, xtype, d, k, 0, nullptr, idx, gate, nullptr, nullptr, nullptr,
                                             nullptr, h, y, s),
                       "decode (one token)");
   const moe::GroupBufs g = group_bufs(ws, L);
   hipError_t e = moe::launch_group(idx, T, k, d.E, g, s);
   if (e != hipSuccess) return hip_status(e, "grouping");
+  if (gemm)
+    return hip_status(moe::launch_gemm_grouped(x, xtype, T, d, k, g, gate, reinterpret_cast<uint16_t*>(h),
+                                               at<float>(ws, L.ys), y, s),
+                      "grouped GEMM");
   return hip_status(moe::launch_decode_grouped(x, xtype, T, d, k, g, gate, h, at<float>(ws, L.ys), y, s),
                     "decode (grouped)");
 }

@@ -116,11 +116,15 @@ SMALL = [(1, 6, 96, 64, 3), (1, 16, 256, 128, 4), (5, 6, 96, 64, 3), (37, 9, 160
          (2, 16, 64, 32, 16)]
 
 
+PATHS = {"auto": 0, "gather": rq.MOE_FLAG_PATH_GATHER, "gemm": rq.MOE_FLAG_PATH_GEMM}
+
+
+@pytest.mark.parametrize("path", ["gather", "gemm"])
 @pytest.mark.parametrize("T,E,H,I,k", SMALL)
 @pytest.mark.parametrize("scheme", [rq.MOE_Q_SYM8, rq.MOE_Q_INT4])
 @pytest.mark.parametrize("xtype", [synth.F32, synth.F16, synth.BF16])
-def test_gather_parity_small(T, E, H, I, k, scheme, xtype):
-    say(f"gather T={T} E={E} H={H} I={I} k={k} scheme={scheme} xtype={xtype}")
+def test_gather_parity_small(T, E, H, I, k, scheme, xtype, path):
+    say(f"experts T={T} E={E} H={H} I={I} k={k} scheme={scheme} xtype={xtype} path={path}")
     g = np.random.default_rng(T + E + H + I + k + 10 * scheme + xtype)
     wgu = (g.standard_normal((E, 2 * I, H)) * 0.02).astype(np.float32)
     wd = (g.standard_normal((E, H, I)) * 0.02).astype(np.float32)
@@ -132,29 +136,33 @@ def test_gather_parity_small(T, E, H, I, k, scheme, xtype):
     rex = oracle.quantize_experts(wgu, wd, scheme)
     xd = to_dev_x(x, xtype)
     bf16 = xtype == synth.BF16
-    y = rq.moe_gather_qmm_forward(xd, ex, torch.from_numpy(idx).cuda(), torch.from_numpy(gate).cuda())
+    fl = PATHS[path]
+    y = rq.moe_gather_qmm_forward(xd, ex, torch.from_numpy(idx).cuda(), torch.from_numpy(gate).cuda(), flags=fl)
     ref = oracle.gather_forward(x, rex, idx, gate, bf16=bf16)
     assert rel_norm_err(y.cpu().numpy(), ref) <= Y_REL_NORM
-    ys = rq.moe_gather_qmm_forward(xd, ex, torch.from_numpy(idx).cuda(), None)
+    ys = rq.moe_gather_qmm_forward(xd, ex, torch.from_numpy(idx).cuda(), None, flags=fl)
     rys = oracle.gather_forward(x, rex, idx, None, bf16=bf16)
     assert rel_norm_err(ys.cpu().numpy(), rys) <= Y_REL_NORM
 
 
 # ---------------------------------------------------------------- whole layer at the workloads' sizes
-LAYER_CASES = [("tiny", None, None), ("decode40", None, None), ("batched_int4", None, 16), ("large_int4", None, 6),
-               ("prefill", None, 12), ("batched_int4", 7, None)]
+LAYER_CASES = [("tiny", None, None, "auto"), ("decode40", None, None, "auto"), ("batched_int4", None, 16, "auto"),
+               ("large_int4", None, 6, "auto"), ("prefill", None, 12, "auto"), ("batched_int4", 7, None, "auto"),
+               ("batched_int4", None, 16, "gemm"), ("large_int4", None, 6, "gemm"), ("prefill", None, 12, "gather"),
+               ("decode40", None, None, "gemm"), ("prefill", 300, 8, "gemm")]
 
 
-@pytest.mark.parametrize("name,T,sample", LAYER_CASES)
-def test_layer_parity(name, T, sample):
+@pytest.mark.parametrize("name,T,sample,path", LAYER_CASES)
+def test_layer_parity(name, T, sample, path):
     w = synth.WORKLOADS[name]
     li = enforce_gap(w, synth.draw_layer(w, seed=0, layer=0, T=T, with_experts=False), seed=0, layer=0)
     bf16 = w.xtype == synth.BF16
     ridx, rgate = oracle.route(li.x, li.R, w.k, bf16=bf16)
     routed = np.unique(ridx)
-    say(f"layer {name} T={li.x.shape[0]} unique experts={len(routed)}")
+    say(f"layer {name} T={li.x.shape[0]} unique experts={len(routed)} path={path}")
     ex = device_pool(w, 0, 0, routed)
-    y, idx, gate = rq.moe_layer_forward(to_dev_x(li.x, w.xtype), torch.from_numpy(li.R).cuda(), ex, w.k)
+    y, idx, gate = rq.moe_layer_forward(to_dev_x(li.x, w.xtype), torch.from_numpy(li.R).cuda(), ex, w.k,
+                                        rq.MOE_FLAG_RENORM | PATHS[path])
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), ridx)
     assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
