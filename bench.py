@@ -17,7 +17,7 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import glob
+import dataclasses
 import hashlib
 import json
 import os
@@ -31,10 +31,16 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "MoE-layer decode tokens/s + achieved HBM GB/s on routed bytes (1 MI355X)"
 
 
-def kernel_source_sha() -> str:
+# sources that define each path's dominant kernel; a stored counter reading is
+# used only while these files are unchanged
+KERNEL_SOURCES = {"gather": ("k_decode.hip", "common.hpp", "kernels.hpp"),
+                  "gemm": ("k_gemm.hip", "common.hpp", "kernels.hpp")}
+
+
+def kernel_source_sha(path: str) -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "routed_expert_quantized_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
+    for name in KERNEL_SOURCES[path]:
+        with open(os.path.join(ROOT, "routed_expert_quantized_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -55,6 +61,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--timer-steps", type=int, default=16, help="steps of the per-kernel event timing pass")
+    ap.add_argument("--k", type=int, default=None,
+                    help="override the workload's top-k (for the bytes-read-versus-k counter sweep)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run a plain fp32 copy kernel over this many MiB (counter calibration)")
     ap.add_argument("--path", choices=["auto", "gather", "gemm"], default="auto",
                     help="expert path: the library's choice, the gathered matvec or the grouped MFMA GEMM")
     return ap.parse_args()
@@ -152,6 +162,8 @@ def main():
     import synth
 
     w = synth.WORKLOADS[args.workload]
+    if args.k is not None:
+        w = dataclasses.replace(w, k=args.k)
     K = args.steps if args.steps is not None else (512 if w.T == 1 else 64)
     W = args.warmup if args.warmup is not None else 32
     multi = w.layers > 1
@@ -268,9 +280,9 @@ def main():
     mfma_tflops = gu_flops / (gu_us * 1e-6) / 1e12
 
     traffic = None
-    tf = os.path.join(ROOT, "profiles", f"traffic_gate_up_{w.name}.json")
-    sha = kernel_source_sha()
-    if os.path.exists(tf):
+    tf = os.path.join(ROOT, "profiles", f"traffic_{dom}_{w.name}.json")
+    sha = kernel_source_sha("gemm" if gemm else "gather")
+    if os.path.exists(tf) and args.k is None:
         with open(tf) as f:
             tj = json.load(f)
         if tj.get("kernel_source_sha") == sha:
@@ -309,6 +321,17 @@ def main():
                          "mfma_frac": round(mfma_tflops / 2500.0, 4)} if gemm else {})},
         "kernel_source_sha": sha,
     }
+    if args.calib_copy_mib:
+        # a plain elementwise copy of known size (negation: a kernel nothing else
+        # here launches): its FETCH_SIZE / WRITE_SIZE per dispatch give the factor
+        # between counter units and bytes moved
+        n = args.calib_copy_mib << 18
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = n * 4
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds)

@@ -14,13 +14,16 @@
 // input, one rounding for bf16 values below the fp16 normal range or for fp32).
 //
 // Operand layout of the MFMA (checked on gfx950): lane l holds A[l%16][8(l/16)+j],
-// B[8(l/16)+j][l%16] for j < 8, and D[4(l/16)+i][l%16] for i < 4. A K chunk of
-// 128 covers four quantisation blocks: lane group g = l/16 loads the whole
-// block 4q+g of its weight row (contiguous, coalesced with the other groups),
-// and MFMA j of the chunk takes elements 8j..8j+7 of that block. The A tile in
-// LDS is laid out to match (for int4 the pair order of the nibble unpacking
-// is mirrored in A while staging). Since the scale is folded into B, mixing
-// blocks across lane groups inside one MFMA is exact.
+// B[8(l/16)+j][l%16] for j < 8, and D[4(l/16)+i][l%16] for i < 4. A K chunk
+// covers one 128-byte line of every weight row: four sym8 blocks (K=128) or
+// eight int4 blocks (K=256). Lane group g = l/16 loads BPG = 1 (sym8) or 2
+// (int4) whole consecutive blocks of its row, so the four groups read the line
+// together and no half line is left for a later refetch; MFMA j of the chunk
+// takes elements 8(j%4)..8(j%4)+7 of the group's block j/4, which is chunk
+// element 32*BPG*g + 8j. The A tile in LDS is laid out to match (for int4 the
+// pair order of the nibble unpacking is mirrored in A while staging). Since
+// the scale is folded into B, mixing blocks across lane groups inside one MFMA
+// is exact.
 #include <algorithm>
 #include <type_traits>
 
@@ -34,8 +37,13 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 template <int V>
 using ICg = std::integral_constant<int, V>;
 
-constexpr int kGemmChunk = 128;                 // K per chunk: four blocks of 32
-constexpr int kGemmARow = kGemmChunk * 2 + 16;  // bytes per LDS A row (fp16 + 16 pad)
+// blocks per lane group and K per chunk (one 128-byte weight line per row)
+template <int SCHEME>
+constexpr int gemm_bpg() { return SCHEME == MOE_Q_INT4 ? 2 : 1; }
+template <int SCHEME>
+constexpr int gemm_kc() { return 128 * gemm_bpg<SCHEME>(); }
+template <int SCHEME>
+constexpr int gemm_arow() { return gemm_kc<SCHEME>() * 2 + 16; }  // bytes per LDS A row (fp16 + pad)
 
 // 8 fp16 values: elements 8j..8j+7 of a 32-code block, times the block scale.
 template <int SCHEME>
@@ -120,7 +128,9 @@ __global__ __launch_bounds__(256) void k_gemm_grouped(const void* __restrict__ a
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ perm, uint16_t* __restrict__ h16,
                                                       float* __restrict__ ys) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[16 * MT * kGemmARow];
+  constexpr int BPG = gemm_bpg<SCHEME>(), KC = gemm_kc<SCHEME>(), AROW = gemm_arow<SCHEME>();
+  constexpr int NJ = KC / 32;  // MFMAs per chunk per output tile
+  __shared__ __attribute__((aligned(16))) uint8_t As[16 * MT * AROW];
   __shared__ int fs[16 * MT];
   const int u = blockIdx.y;
   if (u >= *n_uniq) return;
@@ -156,7 +166,7 @@ __global__ __launch_bounds__(256) void k_gemm_grouped(const void* __restrict__ a
     const int rr = min(col[c] + r16, NROW - 1);
     wrow[c] = (int64_t)e * NROW + rr;
   }
-  const int nchunks = (NB + 3) / 4;
+  const int nchunks = (NB + 4 * BPG - 1) / (4 * BPG);
 
   for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
     const int nm = min(16 * MT, cnt - m0);
@@ -169,34 +179,39 @@ __global__ __launch_bounds__(256) void k_gemm_grouped(const void* __restrict__ a
 #pragma unroll
       for (int c = 0; c < 2; ++c) acc[mt][c] = float4v{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int NST = (16 * MT * 16 + 255) / 256;  // 16-byte activation pieces per thread per chunk
+    constexpr int PPR = KC / 8;                          // 16-byte activation pieces per row per chunk
+    constexpr int NST = (16 * MT * PPR + 255) / 256;    // pieces per thread per chunk
     const int mtiles = (nm + 15) / 16;                 // M tiles holding assignments (uniform)
-    // chunk loads: lane group g holds block 4q+g of its weight rows; the
-    // activation tile is 16*MT rows x 128 elements, 8 elements per piece
-    auto load_w = [&](int q, Block<SCHEME>* wb, half2v* s2) {
-      const int blk = 4 * q + g;
-      const int bc = min(blk, NB - 1);
+    // chunk loads: lane group g holds blocks 4*BPG*q + BPG*g + b (b < BPG) of
+    // its weight rows; the activation tile is 16*MT rows x KC elements, 8
+    // elements per piece
+    auto load_w = [&](int q, Block<SCHEME> (*wb)[BPG], half2v (*s2)[BPG]) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        wb[c] = load_block<SCHEME>(W + wrow[c] * rb, bc);
-        const float sv = blk < NB ? f16_bits_to_f32(S[wrow[c] * NB + bc]) : 0.0f;
-        s2[c] = half2v{(_Float16)sv, (_Float16)sv};
+      for (int b = 0; b < BPG; ++b) {
+        const int blk = 4 * BPG * q + BPG * g + b;
+        const int bc = min(blk, NB - 1);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          wb[c][b] = load_block<SCHEME>(W + wrow[c] * rb, bc);
+          const float sv = blk < NB ? f16_bits_to_f32(S[wrow[c] * NB + bc]) : 0.0f;
+          s2[c][b] = half2v{(_Float16)sv, (_Float16)sv};
+        }
       }
     };
     auto load_a = [&](int q, uint4* st) {
 #pragma unroll
       for (int i = 0; i < NST; ++i) {
         const int c = tid + 256 * i;
-        const int row = min(c >> 4, 16 * MT - 1), grp = c & 15;
+        const int row = min(c / PPR, 16 * MT - 1), grp = c % PPR;
         const int f = fs[row] >= 0 ? fs[row] : fs[0];
         const int64_t src = MODE == 0 ? (int64_t)(f / k) : (int64_t)f;
-        const int kk = min(q * kGemmChunk + grp * 8, K - 8);
+        const int kk = min(q * KC + grp * 8, K - 8);
         st[i] = order_for_b<SCHEME>(load8_f16<MODE == 1 ? MOE_F16 : XT>(Ab + src * arow_bytes, kk));
       }
     };
     for (int q = 0; q < nchunks; ++q) {
-      Block<SCHEME> wb[2];
-      half2v s2[2];
+      Block<SCHEME> wb[2][BPG];
+      half2v s2[2][BPG];
       uint4 st[NST];
       load_w(q, wb, s2);
       load_a(q, st);
@@ -204,20 +219,20 @@ __global__ __launch_bounds__(256) void k_gemm_grouped(const void* __restrict__ a
 #pragma unroll
       for (int i = 0; i < NST; ++i) {
         const int c = tid + 256 * i;
-        if (c < 16 * MT * 16) *reinterpret_cast<uint4*>(As + (c >> 4) * kGemmARow + (c & 15) * 16) = st[i];
+        if (c < 16 * MT * PPR) *reinterpret_cast<uint4*>(As + (c / PPR) * AROW + (c % PPR) * 16) = st[i];
       }
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         half8v b[2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) b[c] = block_slice_f16<SCHEME>(wb[c], j, s2[c]);
+        for (int c = 0; c < 2; ++c) b[c] = block_slice_f16<SCHEME>(wb[c][j / 4], j % 4, s2[c][j / 4]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           if (mt < mtiles) {
-            // A: row mt*16 + r16, elements of block 4q+g at 8j..8j+7 -> LDS offset (32g + 8j) * 2
+            // A: row mt*16 + r16, chunk elements 32*BPG*g + 8j .. +7
             const half8v a =
-                *reinterpret_cast<const half8v*>(As + (mt * 16 + r16) * kGemmARow + (32 * g + 8 * j) * 2);
+                *reinterpret_cast<const half8v*>(As + (mt * 16 + r16) * AROW + (32 * BPG * g + 8 * j) * 2);
 #pragma unroll
             for (int c = 0; c < 2; ++c)
               acc[mt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[c], acc[mt][c], 0, 0, 0);
