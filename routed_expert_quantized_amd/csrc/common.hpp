@@ -473,6 +473,8 @@ __device__ __forceinline__ float xdot(const Block<SCHEME>& c, const XReg<SCHEME,
 // a row group (each reading its own block) spread over the banks.
 __device__ __forceinline__ int hpad(int i) { return i + (i >> 5) * 4; }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z * sigmoid(z), with the hardware exponential and reciprocal
+// (about 1 ulp each); exp overflow for very negative z gives 0.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 }  // namespace moe

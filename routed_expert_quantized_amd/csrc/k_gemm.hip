@@ -179,9 +179,22 @@ __global__ __launch_bounds__(256) void k_gemm_grouped(const void* __restrict__ a
 #pragma unroll
       for (int c = 0; c < 2; ++c) acc[mt][c] = float4v{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int PPR = KC / 8;                          // 16-byte activation pieces per row per chunk
-    constexpr int NST = (16 * MT * PPR + 255) / 256;    // pieces per thread per chunk
-    const int mtiles = (nm + 15) / 16;                 // M tiles holding assignments (uniform)
+    constexpr int PPR = KC / 8;                 // 16-byte activation pieces per row per chunk
+    constexpr int NST = 16 * MT * PPR / 256;    // pieces per thread per chunk
+    static_assert((16 * MT * PPR) % 256 == 0, "activation tile must split evenly over 256 threads");
+    const int mtiles = (nm + 15) / 16;          // M tiles holding assignments (uniform)
+    // Thread tid stages pieces c = tid + 256 i: row c / PPR, column group tid % PPR
+    // (256 is a multiple of PPR). The rows' source offsets are fixed for the pass,
+    // so they are found once here (rows past the assignments repeat row 0).
+    const int grp8 = (tid % PPR) * 8;
+    uint32_t aoff[NST];
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      const int row = tid / PPR + i * (256 / PPR);
+      const int f = fs[row] >= 0 ? fs[row] : fs[0];
+      const uint32_t src = MODE == 0 ? (uint32_t)(f / k) : (uint32_t)f;
+      aoff[i] = src * (uint32_t)arow_bytes;
+    }
     // chunk loads: lane group g holds blocks 4*BPG*q + BPG*g + b (b < BPG) of
     // its weight rows; the activation tile is 16*MT rows x KC elements, 8
     // elements per piece
@@ -199,15 +212,12 @@ __global__ __launch_bounds__(256) void k_gemm_grouped(const void* __restrict__ a
       }
     };
     auto load_a = [&](int q, uint4* st) {
+      // K tail (K not a multiple of KC): the piece is clamped to the row's last
+      // one; its weights carry scale 0 there
+      const int kk = min(q * KC + grp8, K - 8);
 #pragma unroll
-      for (int i = 0; i < NST; ++i) {
-        const int c = tid + 256 * i;
-        const int row = min(c / PPR, 16 * MT - 1), grp = c % PPR;
-        const int f = fs[row] >= 0 ? fs[row] : fs[0];
-        const int64_t src = MODE == 0 ? (int64_t)(f / k) : (int64_t)f;
-        const int kk = min(q * KC + grp * 8, K - 8);
-        st[i] = order_for_b<SCHEME>(load8_f16<MODE == 1 ? MOE_F16 : XT>(Ab + src * arow_bytes, kk));
-      }
+      for (int i = 0; i < NST; ++i)
+        st[i] = order_for_b<SCHEME>(load8_f16<MODE == 1 ? MOE_F16 : XT>(Ab + aoff[i], kk));
     };
     for (int q = 0; q < nchunks; ++q) {
       Block<SCHEME> wb[2][BPG];
@@ -217,10 +227,8 @@ __global__ __launch_bounds__(256) void k_gemm_grouped(const void* __restrict__ a
       load_a(q, st);
       __syncthreads();  // previous chunk's MFMAs are done with As
 #pragma unroll
-      for (int i = 0; i < NST; ++i) {
-        const int c = tid + 256 * i;
-        if (c < 16 * MT * PPR) *reinterpret_cast<uint4*>(As + (c / PPR) * AROW + (c % PPR) * 16) = st[i];
-      }
+      for (int i = 0; i < NST; ++i)
+        *reinterpret_cast<uint4*>(As + (tid / PPR + i * (256 / PPR)) * AROW + grp8 * 2) = st[i];
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
