@@ -72,8 +72,9 @@ hipError_t launch_combine(int T, int H, int k, const float* gate, const float* y
 
 // Grouped MFMA GEMM path (after launch_group): gate/up + SwiGLU into fp16 h,
 // down into ys (or y itself in per-slot mode), then the combine.
+// x16: [T][H] fp16 scratch for the activations when x is not fp16 already.
 hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev& ex, int k, const GroupBufs& g,
-                               const float* gate, uint16_t* h16, float* ys, float* y, hipStream_t s);
+                               const float* gate, uint16_t* h16, uint16_t* x16, float* ys, float* y, hipStream_t s);
 
 hipError_t launch_quantize(const float* w, int64_t rows, int K, int scheme, uint8_t* codes, uint16_t* scales,
                            hipStream_t s);

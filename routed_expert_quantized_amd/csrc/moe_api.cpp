@@ -39,7 +39,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 // Scratch regions inside the caller's workspace, each 256-byte aligned.
 struct Layout {
-  size_t logits, idx, gate, mask, base, counts, offsets, perm, uniq, n_uniq, h, ys, total;
+  size_t logits, idx, gate, mask, base, counts, offsets, perm, uniq, n_uniq, h, ys, x16, total;
 };
 
 Layout layout(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
@@ -63,6 +63,7 @@ Layout layout(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
   L.n_uniq = take(4);
   L.h = take(T * k * I * 4);
   L.ys = take(T * k * H * 4);
+  L.x16 = take(T * H * 2);
   L.total = off;
   return L;
 }
@@ -141,7 +142,7 @@ moe_status run_experts(const void* x, int32_t xtype, int32_t T, const moe::Exper
   if (e != hipSuccess) return hip_status(e, "grouping");
   if (gemm)
     return hip_status(moe::launch_gemm_grouped(x, xtype, T, d, k, g, gate, reinterpret_cast<uint16_t*>(h),
-                                               at<float>(ws, L.ys), y, s),
+                                               at<uint16_t>(ws, L.x16), at<float>(ws, L.ys), y, s),
                       "grouped GEMM");
   return hip_status(moe::launch_decode_grouped(x, xtype, T, d, k, g, gate, h, at<float>(ws, L.ys), y, s),
                     "decode (grouped)");

@@ -112,8 +112,13 @@ def test_group_bit_exact(T, k, E):
 
 
 # ---------------------------------------------------------------- gathered experts, small shapes
+# Shapes: rows with an odd number of 32-blocks (H=96, 160; I=32, 96) take the
+# register-staged GEMM; the rest the LDS-pipelined one. (200, 4, 192, 128, 2)
+# has ~100 assignments per expert (several passes at every tile height) and a
+# K tail (H=192); (48, 8, 128, 192, 2) takes four-tile passes with a K tail in
+# the down projection (I=192).
 SMALL = [(1, 6, 96, 64, 3), (1, 16, 256, 128, 4), (5, 6, 96, 64, 3), (37, 9, 160, 96, 4), (3, 2, 4096, 4096, 2),
-         (2, 16, 64, 32, 16)]
+         (2, 16, 64, 32, 16), (200, 4, 192, 128, 2), (48, 8, 128, 192, 2)]
 
 
 PATHS = {"auto": 0, "gather": rq.MOE_FLAG_PATH_GATHER, "gemm": rq.MOE_FLAG_PATH_GEMM}
