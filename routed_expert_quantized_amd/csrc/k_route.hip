@@ -52,68 +52,47 @@ __global__ __launch_bounds__(64) void k_logits_rows(const void* __restrict__ x, 
   }
 }
 
-// ---------------------------------------------------------------- logits, many tokens
-// Tiled fp32 GEMM logits[T][E] = X[T][H] R[E][H]^T: 64x64 output tile per
-// workgroup, K steps of 16 staged in LDS, 4x4 outputs per thread.
-template <int XT>
-__global__ __launch_bounds__(256) void k_logits_tiled(const void* __restrict__ x, int T, int H,
-                                                      const float* __restrict__ R, int E,
-                                                      float* __restrict__ logits) {
-  __shared__ float xs[16][64 + 4];
-  __shared__ float rs[16][64 + 4];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int tx = tid & 15, ty = tid >> 4;  // outputs (t0 + ty*4 + i, e0 + tx*4 + j)
-  float acc[4][4] = {};
-  // loader: 256 threads load 64 rows x 16 columns = 4 elements each
-  const int lr = tid >> 2, lc = (tid & 3) * 4;
-  for (int h0 = 0; h0 < H; h0 += 16) {
-    {
-      const int t = t0 + lr;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < T) v = load_x4<XT>(x, (int64_t)t * H + h0 + lc);
-      xs[lc + 0][lr] = v.x; xs[lc + 1][lr] = v.y; xs[lc + 2][lr] = v.z; xs[lc + 3][lr] = v.w;
-      const int e = e0 + lr;
-      float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e < E) r = *reinterpret_cast<const float4*>(R + (int64_t)e * H + h0 + lc);
-      rs[lc + 0][lr] = r.x; rs[lc + 1][lr] = r.y; rs[lc + 2][lr] = r.z; rs[lc + 3][lr] = r.w;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { a[i] = xs[kk][ty * 4 + i]; b[i] = rs[kk][tx * 4 + i]; }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < E) logits[(int64_t)t * E + e] = acc[i][j];
-    }
-  }
-}
-
 // ---------------------------------------------------------------- top-k, one wave per token
+// With nsplit > 1 the logits arrive as split-K partial planes [nsplit][T][E];
+// the wave first adds them, in plane order, into its own LDS row.
 template <int VPL>
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int nsplit, int T, int E, int k,
                                               int renorm, int32_t* __restrict__ idx, float* __restrict__ gate,
                                               int32_t* __restrict__ idx2, float* __restrict__ gate2) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ float lsum[4][64 * VPL];
+  const int wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
+  const float* row = logits + (int64_t)t * E;
+  if (nsplit > 1) {
+    // loads of four planes for all of the lane's logits go out together, then
+    // are added in plane order
+    const int64_t plane = (int64_t)T * E;
+    float v[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) v[j] = lane + 64 * j < E ? row[lane + 64 * j] : 0.0f;
+    for (int sp = 1; sp < nsplit; sp += 4) {
+      float p[4][VPL];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < VPL; ++j)
+          p[q][j] = (sp + q < nsplit && lane + 64 * j < E) ? row[(sp + q) * plane + lane + 64 * j] : 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < VPL; ++j)
+          if (sp + q < nsplit) v[j] += p[q][j];
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      if (lane + 64 * j < E) lsum[wv][lane + 64 * j] = v[j];
+    row = lsum[wv];  // written and read by this wave only, in order
+  }
   int my_idx;
   float my_gate;
-  wave_topk<VPL>(logits + (int64_t)t * E, E, k, renorm != 0, my_idx, my_gate);
+  wave_topk<VPL>(row, E, k, renorm != 0, my_idx, my_gate);
   if (lane < k) {
     idx[(int64_t)t * k + lane] = my_idx;
     gate[(int64_t)t * k + lane] = my_gate;
@@ -212,14 +191,121 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------------- launchers
+// Router logits for batches on the matrix cores: v_mfma_f32_16x16x4_f32, fp32
+// operands (activations upcast exactly) and fp32 accumulation, the precision of
+// the router's gate linear ("QwenのMoEルーターを観測してホットエキスパートを先読みしても速くならなかった",
+// section "ルーターをフックする").
+// A workgroup owns a (16*MTT tokens) x (16*NTT experts) tile; its NW waves split
+// its K range and add their partial tiles in LDS. Workgroups along blockIdx.z
+// split K further and write separate partial planes, which the top-k adds. In the MFMA, lane l holds A[l%16][l/16],
+// B[l/16][l%16] and D[4(l/16)+i][l%16]. A lane loads four consecutive K values
+// of its token row and of its expert row at once and feeds one to each of four
+// MFMAs: MFMA i of a step takes K values k + 4g + i (g = l/16), the same
+// permutation on both operands, so the four MFMAs together cover k .. k+15.
+typedef float float4v_r __attribute__((ext_vector_type(4)));
+template <int XT, int MTT, int NTT>
+__global__ __launch_bounds__(1024) void k_logits_mfma(const void* __restrict__ x, int T, int H,
+                                                      const float* __restrict__ R, int E, float* __restrict__ logits,
+                                                      int kw) {
+  extern __shared__ float red[];  // [waves][MTT*NTT*4][64]
+  // split blockIdx.z takes K range [z*nw*kw, (z+1)*nw*kw) into plane z
+  logits += (int64_t)blockIdx.z * T * E;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * 16 * MTT, e0 = blockIdx.y * 16 * NTT;
+  int64_t xrow[MTT];
+  const float* rrow[NTT];
+#pragma unroll
+  for (int mt = 0; mt < MTT; ++mt) xrow[mt] = (int64_t)min(t0 + 16 * mt + r, T - 1) * H;
+#pragma unroll
+  for (int nt = 0; nt < NTT; ++nt) rrow[nt] = R + (int64_t)min(e0 + 16 * nt + r, E - 1) * H;
+  float4v_r acc[MTT][NTT];
+#pragma unroll
+  for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTT; ++nt) acc[mt][nt] = float4v_r{0.f, 0.f, 0.f, 0.f};
+  const int kb = (blockIdx.z * nw + w) * kw;
+#pragma unroll 4
+  for (int k = kb; k < kb + kw; k += 16) {
+    float4 a[MTT], b[NTT];
+#pragma unroll
+    for (int mt = 0; mt < MTT; ++mt) a[mt] = load_x4<XT>(x, xrow[mt] + k + 4 * g);
+#pragma unroll
+    for (int nt = 0; nt < NTT; ++nt) b[nt] = *reinterpret_cast<const float4*>(rrow[nt] + k + 4 * g);
+#pragma unroll
+    for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTT; ++nt) {
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt].x, b[nt].x, acc[mt][nt], 0, 0, 0);
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt].y, b[nt].y, acc[mt][nt], 0, 0, 0);
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt].z, b[nt].z, acc[mt][nt], 0, 0, 0);
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt].w, b[nt].w, acc[mt][nt], 0, 0, 0);
+      }
+  }
+  constexpr int NO = MTT * NTT * 4 * 64;  // outputs of the tile
+  auto store = [&](int o, float v) {
+    const int l = o & 63, i = (o >> 6) & 3, tile = o >> 8;
+    const int mt = tile / NTT, nt = tile % NTT;
+    const int t = t0 + 16 * mt + 4 * (l >> 4) + i, e = e0 + 16 * nt + (l & 15);
+    if (t < T && e < E) logits[(int64_t)t * E + e] = v;
+  };
+  if (nw == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store(((mt * NTT + nt) * 4 + i) * 64 + lane, acc[mt][nt][i]);
+    return;
+  }
+#pragma unroll
+  for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[w * NO + ((mt * NTT + nt) * 4 + i) * 64 + lane] = acc[mt][nt][i];
+  __syncthreads();
+  for (int o = threadIdx.x; o < NO; o += blockDim.x) {
+    float v = 0.f;
+    for (int j = 0; j < nw; ++j) v += red[j * NO + o];  // waves in K order
+    store(o, v);
+  }
+}
+
 hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R, int E, float* logits,
-                         hipStream_t s) {
-  if (T >= kTiledLogitsMinT) {
-    dim3 grid((T + 63) / 64, (E + 63) / 64);
+                         int* nsplit, hipStream_t s) {
+  *nsplit = 1;
+  if (T >= kMfmaLogitsMinT) {
+    // tile shape and split-K: aim for about two waves per SIMD (2048 waves)
+    const int mtt = T >= 32 && (int64_t)((T + 31) / 32) * ((E + 31) / 32) >= 128 ? 2 : 1;
+    const int ntt = E >= 32 && (int64_t)((T + 16 * mtt - 1) / (16 * mtt)) * ((E + 31) / 32) >= 128 ? 2 : 1;
+    dim3 grid((T + 16 * mtt - 1) / (16 * mtt), (E + 16 * ntt - 1) / (16 * ntt));
+    const int64_t tiles = (int64_t)grid.x * grid.y;
+    // waves per workgroup (up to 4), then K splits across workgroups, while the
+    // total stays within about 2048 waves and every wave keeps >= 64 of K
+    int nw = 1, ns = 1;
+    auto fits = [&](int w, int sp) { return tiles * w * sp <= 2048 && H % (16 * w * sp) == 0 && H / (w * sp) >= 64; };
+    while (nw < 4 && fits(nw * 2, ns)) nw *= 2;
+    while (ns < logits_max_splits(T, E) && fits(nw, ns * 2)) ns *= 2;
+    grid.z = ns;
+    *nsplit = ns;
+    const int kw = H / (nw * ns);
+    const size_t lds = nw > 1 ? (size_t)nw * mtt * ntt * 256 * sizeof(float) : 0;
+    auto go = [&](auto XC, auto MC, auto NC) {
+      constexpr int X_ = decltype(XC)::value, M_ = decltype(MC)::value, N_ = decltype(NC)::value;
+      MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_mfma<X_, M_, N_>), grid, dim3(64 * nw), lds, s, x, T, H, R, E,
+                 logits, kw);
+    };
+    auto with_tile = [&](auto XC) {
+      if (mtt == 2 && ntt == 2) go(XC, std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+      else if (ntt == 2) go(XC, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+      else if (mtt == 2) go(XC, std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
+      else go(XC, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+    };
     switch (xtype) {
-      case MOE_F32: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, k_logits_tiled<MOE_F32>, grid, dim3(256), 0, s, x, T, H, R, E, logits); break;
-      case MOE_F16: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, k_logits_tiled<MOE_F16>, grid, dim3(256), 0, s, x, T, H, R, E, logits); break;
-      default:      MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, k_logits_tiled<MOE_BF16>, grid, dim3(256), 0, s, x, T, H, R, E, logits); break;
+      case MOE_F32: with_tile(std::integral_constant<int, MOE_F32>{}); break;
+      case MOE_F16: with_tile(std::integral_constant<int, MOE_F16>{}); break;
+      default: with_tile(std::integral_constant<int, MOE_BF16>{}); break;
     }
   } else {
     const int nch = (H + 255) / 256;
@@ -241,15 +327,15 @@ hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R,
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, int T, int E, int k, int renorm, int32_t* idx, float* gate,
+hipError_t launch_topk(const float* logits, int nsplit, int T, int E, int k, int renorm, int32_t* idx, float* gate,
                        int32_t* idx2, float* gate2, hipStream_t s) {
   dim3 grid((T + 3) / 4);
   const int vpl = (E + 63) / 64;
-  if (vpl <= 1)      MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<1>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
-  else if (vpl <= 2) MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<2>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
-  else if (vpl <= 4) MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<4>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
-  else if (vpl <= 8) MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<8>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
-  else               MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<16>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, gate, idx2, gate2);
+  if (vpl <= 1)      MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<1>, grid, dim3(256), 0, s, logits, nsplit, T, E, k, renorm, idx, gate, idx2, gate2);
+  else if (vpl <= 2) MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<2>, grid, dim3(256), 0, s, logits, nsplit, T, E, k, renorm, idx, gate, idx2, gate2);
+  else if (vpl <= 4) MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<4>, grid, dim3(256), 0, s, logits, nsplit, T, E, k, renorm, idx, gate, idx2, gate2);
+  else if (vpl <= 8) MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<8>, grid, dim3(256), 0, s, logits, nsplit, T, E, k, renorm, idx, gate, idx2, gate2);
+  else               MOE_LAUNCH(MOE_KERNEL_TOPK, k_topk<16>, grid, dim3(256), 0, s, logits, nsplit, T, E, k, renorm, idx, gate, idx2, gate2);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ bool timer_take(int kid, hipEvent_t* start, hipEvent_t* stop);
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
-constexpr int kTiledLogitsMinT = 128;  // from this many tokens the router logits run as a tiled GEMM
+constexpr int kMfmaLogitsMinT = 16;  // from this many tokens the router logits run on the matrix cores
 
 
 // Device buffers of the token-by-expert grouping.
@@ -47,9 +47,17 @@ struct ExpertsDev {
   const uint16_t* sd;
 };
 
+// Split-K planes of the router logits the workspace holds room for: the batch
+// router may write up to this many partial [T][E] planes (summed by the top-k).
+inline int logits_max_splits(int64_t T, int64_t E) {
+  if (T < kMfmaLogitsMinT) return 1;
+  int64_t s = (1 << 20) / (T * E);
+  return (int)(s < 1 ? 1 : s > 8 ? 8 : s);
+}
+// Writes *nsplit partial planes logits[s][T][E] (one for T < kMfmaLogitsMinT).
 hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R, int E, float* logits,
-                         hipStream_t s);
-hipError_t launch_topk(const float* logits, int T, int E, int k, int renorm, int32_t* idx, float* gate,
+                         int* nsplit, hipStream_t s);
+hipError_t launch_topk(const float* logits, int nsplit, int T, int E, int k, int renorm, int32_t* idx, float* gate,
                        int32_t* idx2, float* gate2, hipStream_t s);
 hipError_t launch_group(const int32_t* idx, int T, int k, int E, const GroupBufs& g, hipStream_t s);
 

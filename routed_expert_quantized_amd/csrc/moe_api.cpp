@@ -51,7 +51,7 @@ Layout layout(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
     return o;
   };
   const int64_t C = (T + 63) / 64;
-  L.logits = take(T * E * 4);
+  L.logits = take(T * E * 4 * moe::logits_max_splits(T, E));
   L.idx = take(T * k * 4);
   L.gate = take(T * k * 4);
   L.mask = take(C * E * 8);
@@ -221,9 +221,10 @@ moe_status moe_route(const void* x, int32_t xtype, int32_t T, int32_t H, const f
   if ((st = check_ws(ws, ws_bytes, L))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* logits = at<float>(ws, L.logits);
-  hipError_t e = moe::launch_logits(x, xtype, T, H, router_w, E, logits, s);
+  int nsplit = 1;
+  hipError_t e = moe::launch_logits(x, xtype, T, H, router_w, E, logits, &nsplit, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
-  return hip_status(moe::launch_topk(logits, T, E, k, (flags & MOE_FLAG_RENORM) ? 1 : 0, topk_idx, topk_gate,
+  return hip_status(moe::launch_topk(logits, nsplit, T, E, k, (flags & MOE_FLAG_RENORM) ? 1 : 0, topk_idx, topk_gate,
                                      nullptr, nullptr, s),
                     "top-k");
 }
@@ -286,13 +287,14 @@ moe_status moe_layer_forward(const void* x, int32_t xtype, int32_t T, const floa
   float* logits = at<float>(ws, L.logits);
   int32_t* idx = at<int32_t>(ws, L.idx);
   float* gate = at<float>(ws, L.gate);
-  hipError_t e = moe::launch_logits(x, xtype, T, d.H, router_w, d.E, logits, s);
+  int nsplit = 1;
+  hipError_t e = moe::launch_logits(x, xtype, T, d.H, router_w, d.E, logits, &nsplit, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
   if (T == 1 && !(flags & MOE_FLAG_PATH_GEMM))
     return hip_status(moe::launch_decode_t1(x, xtype, d, k, renorm, logits, nullptr, nullptr, idx, gate,
                                             topk_idx_out, topk_gate_out, at<float>(ws, L.h), y, s),
                       "decode (one token)");
-  e = moe::launch_topk(logits, T, d.E, k, renorm, idx, gate, topk_idx_out, topk_gate_out, s);
+  e = moe::launch_topk(logits, nsplit, T, d.E, k, renorm, idx, gate, topk_idx_out, topk_gate_out, s);
   if (e != hipSuccess) return hip_status(e, "top-k");
   return run_experts(x, xtype, T, d, k, idx, gate, y, flags, ws, L, s);
 }
