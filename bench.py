@@ -33,8 +33,8 @@ METRIC = "MoE-layer decode tokens/s + achieved HBM GB/s on routed bytes (1 MI355
 
 # sources that define each path's dominant kernel; a stored counter reading is
 # used only while these files are unchanged
-KERNEL_SOURCES = {"gather": ("k_decode.hip", "common.hpp", "kernels.hpp"),
-                  "gemm": ("k_gemm.hip", "common.hpp", "kernels.hpp")}
+KERNEL_SOURCES = {"gather": ("k_decode.hip", "common.hpp"),
+                  "gemm": ("k_gemm.hip", "common.hpp")}
 
 
 def kernel_source_sha(path: str) -> str:
