@@ -436,7 +436,7 @@ __global__ __launch_bounds__(256) void k_gemm_dma(const uint16_t* __restrict__ a
                                                   const int32_t* __restrict__ counts,
                                                   const int32_t* __restrict__ offsets,
                                                   const int32_t* __restrict__ perm, uint16_t* __restrict__ h16,
-                                                  float* __restrict__ ys) {
+                                                  float* __restrict__ ys, int ncb) {
   using D = DmaTile<SCHEME, MT, LB>;
   static_assert((NS - 2) * D::NI < 64, "in-flight loads exceed vmcnt");
   // One LDS array per stage, always addressed with a compile-time stage index.
@@ -453,193 +453,206 @@ __global__ __launch_bounds__(256) void k_gemm_dma(const uint16_t* __restrict__ a
   };
   static_assert(NS >= 2 && NS <= 4, "stage count");
   __shared__ int fs[16 * MT];
-  const int u = blockIdx.y;
-  if (u >= *n_uniq) return;
+  // Persistent: the grid holds as many workgroups as fit on the chip at once
+  // (a multiple of 8), each taking tiles blockIdx.x, +gridDim.x, ... until the
+  // routed experts' tiles run out, so no partly filled last round of
+  // workgroups is left. Tile order is XCD-aware: ids go round-robin over the 8
+  // XCDs, and tile (expert u, column block cb) has id (u/8)*8*ncb + cb*8 + u%8,
+  // so all column blocks of an expert (which read the same activation rows)
+  // run on one XCD, with the experts alternating over the XCDs.
+  const int nu = *n_uniq;
+  const int ntiles = ncb * ((nu + 7) / 8 * 8);
   const int tid = (int)threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
-  const int e = uniq[u], cnt = counts[e], beg = offsets[e];
-  const int H = ex.H, I = ex.I;
-  const int K = MODE == 0 ? H : I;
-  const int NB = K / 32;
-  const int NROW = MODE == 0 ? 2 * I : H;
-  const int lim = MODE == 0 ? I : H;
-  const int rb = (int)row_bytes<SCHEME>(K);
-  const uint8_t* Wexp = (MODE == 0 ? ex.wgu : ex.wd) + (int64_t)e * NROW * rb;
-  const uint16_t* Sexp = (MODE == 0 ? ex.sgu : ex.sd) + (int64_t)e * NROW * NB;
-  const int n0 = MODE == 0 ? blockIdx.x * 64 : blockIdx.x * 128;
-  // workgroup-local weight row lr (0..127) -> row of the expert (clamped in range)
-  auto grow = [&](int lr) {
-    const int r = MODE == 0 ? (lr < 64 ? n0 + lr : I + n0 + lr - 64) : n0 + lr;
-    return min(r, NROW - 1);
-  };
-  // this lane's rows in the two 16-column tiles of its wave
-  int lrow[2];
-  lrow[0] = MODE == 0 ? wave * 16 + r16 : wave * 32 + r16;
-  lrow[1] = MODE == 0 ? 64 + wave * 16 + r16 : wave * 32 + 16 + r16;
-
-  // DMA sources that stay fixed for the whole kernel: code rows and scale rows
-  int ro[D::NBI], bcol[D::NBI];
-#pragma unroll
-  for (int i = 0; i < D::NBI; ++i) {
-    const int row = (i * 4 + wave) * (1024 / LB) + lane / D::SB;
-    ro[i] = grow(row) * rb;
-    bcol[i] = 16 * ((lane % D::SB) ^ D::swz_b(row));
-  }
-  constexpr int DPR = D::BPS / 2;  // scale dwords per row per stage
-  int so[D::NSI], sp[D::NSI];
-#pragma unroll
-  for (int i = 0; i < D::NSI; ++i) {
-    const int d = (i * 4 + wave) * 64 + lane;
-    so[i] = grow(min(d / DPR, 127)) * NB;
-    sp[i] = 2 * (d % DPR);
-  }
-  const int nchunks = (NB + D::BPS - 1) / D::BPS;
-
-  for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
-    const int nm = min(16 * MT, cnt - m0);
-    __syncthreads();
-    if (tid < 16 * MT) fs[tid] = tid < nm ? perm[beg + m0 + tid] : -1;
-    __syncthreads();
-    // activation rows of this pass (rows past the assignments repeat row 0)
-    int64_t aoff[D::NAI];
-    int apc[D::NAI];
-#pragma unroll
-    for (int i = 0; i < D::NAI; ++i) {
-      const int row = (i * 4 + wave) * D::RPI + lane / D::SPR;
-      const int fr = row < 16 * MT ? fs[row] : -1;
-      const int f = fr >= 0 ? fr : fs[0];
-      const int64_t src = MODE == 0 ? (int64_t)(f / k) : (int64_t)f;
-      aoff[i] = src * K;
-      apc[i] = 8 * ((lane % D::SPR) ^ D::swz_a(row));
-    }
-    float4v acc[MT][2];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) acc[mt][c] = float4v{0.f, 0.f, 0.f, 0.f};
-    const int mtiles = (nm + 15) / 16;
-
-    auto issue = [&](int q, uint8_t* Bst) {
-      uint8_t* Sst = Bst + D::B_BYTES;
-      uint8_t* Ast = Sst + D::S_BYTES;
-#pragma unroll
-      for (int i = 0; i < D::NBI; ++i)
-        dma16(Wexp + ro[i] + min(q * LB + bcol[i], rb - 16), Bst + (i * 4 + wave) * 1024);
-#pragma unroll
-      for (int i = 0; i < D::NSI; ++i)
-        dma4(Sexp + so[i] + min(q * D::BPS + sp[i], NB - 2), Sst + (i * 4 + wave) * 256);
-#pragma unroll
-      for (int i = 0; i < D::NAI; ++i)
-        dma16(act + aoff[i] + min(q * D::KC + apc[i], K - 8), Ast + (i * 4 + wave) * 1024);
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int rest = tile >> 3;
+    const int cb = rest % ncb;
+    const int u = (rest / ncb) * 8 + (tile & 7);
+    if (u >= nu) continue;
+    const int e = uniq[u], cnt = counts[e], beg = offsets[e];
+    const int H = ex.H, I = ex.I;
+    const int K = MODE == 0 ? H : I;
+    const int NB = K / 32;
+    const int NROW = MODE == 0 ? 2 * I : H;
+    const int lim = MODE == 0 ? I : H;
+    const int rb = (int)row_bytes<SCHEME>(K);
+    const uint8_t* Wexp = (MODE == 0 ? ex.wgu : ex.wd) + (int64_t)e * NROW * rb;
+    const uint16_t* Sexp = (MODE == 0 ? ex.sgu : ex.sd) + (int64_t)e * NROW * NB;
+    const int n0 = MODE == 0 ? cb * 64 : cb * 128;
+    // workgroup-local weight row lr (0..127) -> row of the expert (clamped in range)
+    auto grow = [&](int lr) {
+      const int r = MODE == 0 ? (lr < 64 ? n0 + lr : I + n0 + lr - 64) : n0 + lr;
+      return min(r, NROW - 1);
     };
-    auto compute = [&](int q, const uint8_t* Bst) {
-      const uint32_t bb = lds_addr(Bst);
-      const uint32_t sb = bb + D::B_BYTES;
-      const uint32_t ab = sb + D::S_BYTES;
-      // codes: lane group g's span of each of its two rows; scales of that span
-      u32x4 raw[4] = {};
-      uint32_t sc[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int lr = lrow[c];
-#pragma unroll
-        for (int t = 0; t < D::NSL; ++t)
-          raw[2 * c + t] = lds_read16(bb + lr * LB + ((g * D::NSL + t) ^ D::swz_b(lr)) * 16);
-#pragma unroll
-        for (int b = 0; b < D::NSC; ++b)
-          sc[2 * c + b] = lds_read_u16(sb + (lr * D::BPS + g * D::SPAN / 32 + b) * 2);
+    // this lane's rows in the two 16-column tiles of its wave
+    int lrow[2];
+    lrow[0] = MODE == 0 ? wave * 16 + r16 : wave * 32 + r16;
+    lrow[1] = MODE == 0 ? 64 + wave * 16 + r16 : wave * 32 + 16 + r16;
+
+    // DMA sources that stay fixed for the whole kernel: code rows and scale rows
+    int ro[D::NBI], bcol[D::NBI];
+  #pragma unroll
+    for (int i = 0; i < D::NBI; ++i) {
+      const int row = (i * 4 + wave) * (1024 / LB) + lane / D::SB;
+      ro[i] = grow(row) * rb;
+      bcol[i] = 16 * ((lane % D::SB) ^ D::swz_b(row));
+    }
+    constexpr int DPR = D::BPS / 2;  // scale dwords per row per stage
+    int so[D::NSI], sp[D::NSI];
+  #pragma unroll
+    for (int i = 0; i < D::NSI; ++i) {
+      const int d = (i * 4 + wave) * 64 + lane;
+      so[i] = grow(min(d / DPR, 127)) * NB;
+      sp[i] = 2 * (d % DPR);
+    }
+    const int nchunks = (NB + D::BPS - 1) / D::BPS;
+
+    for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
+      const int nm = min(16 * MT, cnt - m0);
+      __syncthreads();
+      if (tid < 16 * MT) fs[tid] = tid < nm ? perm[beg + m0 + tid] : -1;
+      __syncthreads();
+      // activation rows of this pass (rows past the assignments repeat row 0)
+      int64_t aoff[D::NAI];
+      int apc[D::NAI];
+  #pragma unroll
+      for (int i = 0; i < D::NAI; ++i) {
+        const int row = (i * 4 + wave) * D::RPI + lane / D::SPR;
+        const int fr = row < 16 * MT ? fs[row] : -1;
+        const int f = fr >= 0 ? fr : fs[0];
+        const int64_t src = MODE == 0 ? (int64_t)(f / k) : (int64_t)f;
+        aoff[i] = src * K;
+        apc[i] = 8 * ((lane % D::SPR) ^ D::swz_a(row));
       }
-      // activation fragments of MFMA step j: row mt*16 + r16, logical slot g*SPAN/8 + j
-      auto read_a = [&](int j, u32x4 (&a)[MT]) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          a[mt] = lds_read16(ab + (mt * 16 + r16) * D::ARB + (((g * D::SPAN / 8 + j) ^ D::swz_a(r16)) * 16));
+      float4v acc[MT][2];
+  #pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+  #pragma unroll
+        for (int c = 0; c < 2; ++c) acc[mt][c] = float4v{0.f, 0.f, 0.f, 0.f};
+      const int mtiles = (nm + 15) / 16;
+
+      auto issue = [&](int q, uint8_t* Bst) {
+        uint8_t* Sst = Bst + D::B_BYTES;
+        uint8_t* Ast = Sst + D::S_BYTES;
+  #pragma unroll
+        for (int i = 0; i < D::NBI; ++i)
+          dma16(Wexp + ro[i] + min(q * LB + bcol[i], rb - 16), Bst + (i * 4 + wave) * 1024);
+  #pragma unroll
+        for (int i = 0; i < D::NSI; ++i)
+          dma4(Sexp + so[i] + min(q * D::BPS + sp[i], NB - 2), Sst + (i * 4 + wave) * 256);
+  #pragma unroll
+        for (int i = 0; i < D::NAI; ++i)
+          dma16(act + aoff[i] + min(q * D::KC + apc[i], K - 8), Ast + (i * 4 + wave) * 1024);
       };
-      u32x4 acur[MT], anext[MT];
-      read_a(0, acur);
-      lds_wait_b(raw, sc);
-      lds_wait<MT>(acur);
-      uint32_t w[2][D::NW];
-      half2v s2[2][D::NSC];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int t = 0; t < D::NSL; ++t) {
-          const u32x4 v = raw[2 * c + t];
-          w[c][4 * t + 0] = v.x; w[c][4 * t + 1] = v.y; w[c][4 * t + 2] = v.z; w[c][4 * t + 3] = v.w;
+      auto compute = [&](int q, const uint8_t* Bst) {
+        const uint32_t bb = lds_addr(Bst);
+        const uint32_t sb = bb + D::B_BYTES;
+        const uint32_t ab = sb + D::S_BYTES;
+        // codes: lane group g's span of each of its two rows; scales of that span
+        u32x4 raw[4] = {};
+        uint32_t sc[4] = {0u, 0u, 0u, 0u};
+  #pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int lr = lrow[c];
+  #pragma unroll
+          for (int t = 0; t < D::NSL; ++t)
+            raw[2 * c + t] = lds_read16(bb + lr * LB + ((g * D::NSL + t) ^ D::swz_b(lr)) * 16);
+  #pragma unroll
+          for (int b = 0; b < D::NSC; ++b)
+            sc[2 * c + b] = lds_read_u16(sb + (lr * D::BPS + g * D::SPAN / 32 + b) * 2);
         }
-#pragma unroll
-        for (int b = 0; b < D::NSC; ++b) {
-          // blocks past the row end (K tail) were clamped to valid memory; scale 0 drops them
-          const float sv =
-              q * D::BPS + g * D::SPAN / 32 + b < NB ? f16_bits_to_f32((uint16_t)sc[2 * c + b]) : 0.0f;
-          s2[c][b] = half2v{(_Float16)sv, (_Float16)sv};
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < D::NJ; ++j) {
-        if (j + 1 < D::NJ) read_a(j + 1, anext);
-        half8v b[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) b[c] = span_slice_f16<SCHEME, D::NW>(w[c], j, s2[c][j / 4]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          if (mt < mtiles) {
-            const uint4 ra = make_uint4(acur[mt].x, acur[mt].y, acur[mt].z, acur[mt].w);
-            const half8v a = __builtin_bit_cast(half8v, order_for_b<SCHEME>(ra));
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-              acc[mt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[c], acc[mt][c], 0, 0, 0);
+        // activation fragments of MFMA step j: row mt*16 + r16, logical slot g*SPAN/8 + j
+        auto read_a = [&](int j, u32x4 (&a)[MT]) {
+  #pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            a[mt] = lds_read16(ab + (mt * 16 + r16) * D::ARB + (((g * D::SPAN / 8 + j) ^ D::swz_a(r16)) * 16));
+        };
+        u32x4 acur[MT], anext[MT];
+        read_a(0, acur);
+        lds_wait_b(raw, sc);
+        lds_wait<MT>(acur);
+        uint32_t w[2][D::NW];
+        half2v s2[2][D::NSC];
+  #pragma unroll
+        for (int c = 0; c < 2; ++c) {
+  #pragma unroll
+          for (int t = 0; t < D::NSL; ++t) {
+            const u32x4 v = raw[2 * c + t];
+            w[c][4 * t + 0] = v.x; w[c][4 * t + 1] = v.y; w[c][4 * t + 2] = v.z; w[c][4 * t + 3] = v.w;
+          }
+  #pragma unroll
+          for (int b = 0; b < D::NSC; ++b) {
+            // blocks past the row end (K tail) were clamped to valid memory; scale 0 drops them
+            const float sv =
+                q * D::BPS + g * D::SPAN / 32 + b < NB ? f16_bits_to_f32((uint16_t)sc[2 * c + b]) : 0.0f;
+            s2[c][b] = half2v{(_Float16)sv, (_Float16)sv};
           }
         }
-        if (j + 1 < D::NJ) {
-          lds_wait<MT>(anext);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acur[mt] = anext[mt];
+  #pragma unroll
+        for (int j = 0; j < D::NJ; ++j) {
+          if (j + 1 < D::NJ) read_a(j + 1, anext);
+          half8v b[2];
+  #pragma unroll
+          for (int c = 0; c < 2; ++c) b[c] = span_slice_f16<SCHEME, D::NW>(w[c], j, s2[c][j / 4]);
+  #pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            if (mt < mtiles) {
+              const uint4 ra = make_uint4(acur[mt].x, acur[mt].y, acur[mt].z, acur[mt].w);
+              const half8v a = __builtin_bit_cast(half8v, order_for_b<SCHEME>(ra));
+  #pragma unroll
+              for (int c = 0; c < 2; ++c)
+                acc[mt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[c], acc[mt][c], 0, 0, 0);
+            }
+          }
+          if (j + 1 < D::NJ) {
+            lds_wait<MT>(anext);
+  #pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acur[mt] = anext[mt];
+          }
         }
-      }
-    };
+      };
 
-    // Every iteration issues one stage and waits for the oldest one, so all
-    // waits are the same constant; past the last chunk a stage is refilled with
-    // the last chunk again (clamped, cache-resident) and never read.
-    static_for<NS - 1>([&](auto R) { issue(min((int)decltype(R)::value, nchunks - 1), stage(R)); });
-    // chunk q lives in stage q % NS; the loop is unrolled NS times so that every
-    // stage index is a constant
-    for (int q0 = 0; q0 < nchunks; q0 += NS) {
-      static_for<NS>([&](auto R) {
-        constexpr int r = decltype(R)::value;
-        const int q = q0 + r;
-        if (q < nchunks) {
-          wait_vmcnt<(NS - 2) * D::NI>();
-          raw_barrier();  // chunk q is in LDS for every wave; chunk q-1's stage is free
-          issue(min(q + NS - 1, nchunks - 1), stage(ICg<(r + NS - 1) % NS>{}));
-          compute(q, stage(R));  // ends with its LDS reads complete
-        }
-      });
-    }
-    wait_vmcnt<0>();  // the trailing refills land before the next pass reuses the stages
-    // epilogue: lane holds rows m = mt*16 + 4g + i of its two 16-column tiles, column r16
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mt * 16 + 4 * g + i;
-        if (m >= nm) continue;
-        const int f = fs[m];
-        if (MODE == 0) {
-          // gate tile column n0 + 16*wave + r16 pairs with the same up tile column
-          const int n = n0 + wave * 16 + r16;
-          if (n < lim) {
-            const float hv = silu(acc[mt][0][i]) * acc[mt][1][i];
-            h16[(int64_t)f * I + n] = __builtin_bit_cast(uint16_t, (_Float16)hv);
+      // Every iteration issues one stage and waits for the oldest one, so all
+      // waits are the same constant; past the last chunk a stage is refilled with
+      // the last chunk again (clamped, cache-resident) and never read.
+      static_for<NS - 1>([&](auto R) { issue(min((int)decltype(R)::value, nchunks - 1), stage(R)); });
+      // chunk q lives in stage q % NS; the loop is unrolled NS times so that every
+      // stage index is a constant
+      for (int q0 = 0; q0 < nchunks; q0 += NS) {
+        static_for<NS>([&](auto R) {
+          constexpr int r = decltype(R)::value;
+          const int q = q0 + r;
+          if (q < nchunks) {
+            wait_vmcnt<(NS - 2) * D::NI>();
+            raw_barrier();  // chunk q is in LDS for every wave; chunk q-1's stage is free
+            issue(min(q + NS - 1, nchunks - 1), stage(ICg<(r + NS - 1) % NS>{}));
+            compute(q, stage(R));  // ends with its LDS reads complete
           }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int n = n0 + wave * 32 + 16 * c + r16;
-            if (n < lim) ys[(int64_t)f * H + n] = acc[mt][c][i];
+        });
+      }
+      wait_vmcnt<0>();  // the trailing refills land before the next pass reuses the stages
+      // epilogue: lane holds rows m = mt*16 + 4g + i of its two 16-column tiles, column r16
+  #pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = mt * 16 + 4 * g + i;
+          if (m >= nm) continue;
+          const int f = fs[m];
+          if (MODE == 0) {
+            // gate tile column n0 + 16*wave + r16 pairs with the same up tile column
+            const int n = n0 + wave * 16 + r16;
+            if (n < lim) {
+              const float hv = silu(acc[mt][0][i]) * acc[mt][1][i];
+              h16[(int64_t)f * I + n] = __builtin_bit_cast(uint16_t, (_Float16)hv);
+            }
+          } else {
+  #pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const int n = n0 + wave * 32 + 16 * c + r16;
+              if (n < lim) ys[(int64_t)f * H + n] = acc[mt][c][i];
+            }
           }
         }
       }
@@ -658,19 +671,33 @@ __global__ __launch_bounds__(256) void k_to_f16(const void* __restrict__ x, int6
     *reinterpret_cast<uint4*>(out + 8 * i) = load8_f16<XT>(xs + 8 * xb * i, 0);
 }
 
+// Workgroups of a kernel that fit on the device at once (a multiple of 8).
+template <typename K>
+static int resident_workgroups(K kernel) {
+  int per_cu = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  return (per_cu * cus + 7) / 8 * 8;
+}
+
 template <int SCHEME, int MODE, int MT, int NS, int LB>
-static void launch_dma(dim3 grid, const uint16_t* act, const ExpertsDev& ex, int k, const GroupBufs& g,
+static void launch_dma(int ncb, int maxu8, const uint16_t* act, const ExpertsDev& ex, int k, const GroupBufs& g,
                        uint16_t* h16, float* ys, hipStream_t s) {
-  MOE_LAUNCH(MODE == 0 ? MOE_KERNEL_GEMM_GATE_UP : MOE_KERNEL_GEMM_DOWN, (k_gemm_dma<SCHEME, MODE, MT, NS, LB>),
-             grid, dim3(256), 0, s, act, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h16, ys);
+  auto kernel = k_gemm_dma<SCHEME, MODE, MT, NS, LB>;
+  static const int resident = resident_workgroups(kernel);  // per kernel, first call
+  const int grid = std::min(resident, ncb * maxu8);
+  MOE_LAUNCH(MODE == 0 ? MOE_KERNEL_GEMM_GATE_UP : MOE_KERNEL_GEMM_DOWN, kernel, dim3(grid), dim3(256), 0, s, act,
+             ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h16, ys, ncb);
 }
 
 // gate/up then down with one tuning (M tiles per pass, stages, line bytes per stage)
 template <int SCHEME, int MT, int NS, int LB>
-static void launch_dma_pair(dim3 g1, dim3 g2, const uint16_t* act, const ExpertsDev& ex, int k, const GroupBufs& g,
+static void launch_dma_pair(int maxu8, const uint16_t* act, const ExpertsDev& ex, int k, const GroupBufs& g,
                             uint16_t* h16, float* ys, float* out, hipStream_t s) {
-  launch_dma<SCHEME, 0, MT, NS, LB>(g1, act, ex, k, g, h16, ys, s);
-  launch_dma<SCHEME, 1, MT, NS, LB>(g2, h16, ex, k, g, h16, out, s);
+  launch_dma<SCHEME, 0, MT, NS, LB>((ex.I + 63) / 64, maxu8, act, ex, k, g, h16, ys, s);
+  launch_dma<SCHEME, 1, MT, NS, LB>((ex.H + 127) / 128, maxu8, h16, ex, k, g, h16, out, s);
 }
 
 hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev& ex, int k, const GroupBufs& g,
@@ -690,18 +717,18 @@ hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev
         hipLaunchKernelGGL(k_to_f16<MOE_BF16>, dim3(blocks), dim3(256), 0, s, x, n8, x16);
       act = x16;
     }
-    const dim3 g1((ex.I + 63) / 64, maxu), g2((ex.H + 127) / 128, maxu);
+    const int maxu8 = (maxu + 7) / 8 * 8;
     // Tunings measured on MI355X. Whole 128-byte lines per stage with two stages
     // keep three workgroups per CU for one- and four-tile passes; six-tile passes
     // (about 64 assignments per expert) stage half lines in three stages.
     // int4 four-tile passes use half lines (whole lines exceed the registers).
     if (ex.scheme == MOE_Q_SYM8) {
-      if (avg > 24) launch_dma_pair<MOE_Q_SYM8, 6, 3, 64>(g1, g2, act, ex, k, g, h16, ys, out, s);
-      else if (avg > 6) launch_dma_pair<MOE_Q_SYM8, 4, 2, 128>(g1, g2, act, ex, k, g, h16, ys, out, s);
-      else launch_dma_pair<MOE_Q_SYM8, 1, 2, 128>(g1, g2, act, ex, k, g, h16, ys, out, s);
+      if (avg > 24) launch_dma_pair<MOE_Q_SYM8, 6, 3, 64>(maxu8, act, ex, k, g, h16, ys, out, s);
+      else if (avg > 6) launch_dma_pair<MOE_Q_SYM8, 4, 2, 128>(maxu8, act, ex, k, g, h16, ys, out, s);
+      else launch_dma_pair<MOE_Q_SYM8, 1, 2, 128>(maxu8, act, ex, k, g, h16, ys, out, s);
     } else {
-      if (avg > 6) launch_dma_pair<MOE_Q_INT4, 4, 2, 64>(g1, g2, act, ex, k, g, h16, ys, out, s);
-      else launch_dma_pair<MOE_Q_INT4, 1, 2, 128>(g1, g2, act, ex, k, g, h16, ys, out, s);
+      if (avg > 6) launch_dma_pair<MOE_Q_INT4, 4, 2, 64>(maxu8, act, ex, k, g, h16, ys, out, s);
+      else launch_dma_pair<MOE_Q_INT4, 1, 2, 128>(maxu8, act, ex, k, g, h16, ys, out, s);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
