@@ -432,15 +432,34 @@ __global__ __launch_bounds__(256) void k_down_grouped(ExpertsDev ex, int k, cons
 }
 
 // y[t][m] = sum over slots s, in order, of gate[t][s] * ys[t*k+s][m].
+// Four consecutive outputs of one token per thread; every slot's loads are
+// issued before the fused multiply-adds, which run in slot order (KMAX >= k).
+template <int KMAX>
 __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const float* __restrict__ gate,
                                                  const float* __restrict__ ys, float* __restrict__ y) {
-  const int nbx = (H + 255) / 256;
+  const int nbx = (H / 4 + 255) / 256;
   const int t = blockIdx.x / nbx;
-  const int m = (blockIdx.x % nbx) * 256 + threadIdx.x;
+  const int m = ((blockIdx.x % nbx) * 256 + threadIdx.x) * 4;
   if (t >= T || m >= H) return;
-  float acc = 0.0f;
-  for (int s = 0; s < k; ++s) acc = fmaf(gate[(int64_t)t * k + s], ys[((int64_t)t * k + s) * H + m], acc);
-  y[(int64_t)t * H + m] = acc;
+  float4 v[KMAX];
+  float g[KMAX];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    const int sc = min(s, k - 1);
+    v[s] = *reinterpret_cast<const float4*>(ys + ((int64_t)t * k + sc) * H + m);
+    g[s] = gate[(int64_t)t * k + sc];
+  }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    if (s < k) {
+      acc.x = fmaf(g[s], v[s].x, acc.x);
+      acc.y = fmaf(g[s], v[s].y, acc.y);
+      acc.z = fmaf(g[s], v[s].z, acc.z);
+      acc.w = fmaf(g[s], v[s].w, acc.w);
+    }
+  }
+  *reinterpret_cast<float4*>(y + (int64_t)t * H + m) = acc;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -542,8 +561,9 @@ hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsD
 }
 
 hipError_t launch_combine(int T, int H, int k, const float* gate, const float* ys, float* y, hipStream_t s) {
-  dim3 cg((unsigned)(((H + 255) / 256) * (int64_t)T));
-  MOE_LAUNCH(MOE_KERNEL_COMBINE, k_combine, cg, dim3(256), 0, s, T, H, k, gate, ys, y);
+  const dim3 cg((unsigned)((int64_t)T * ((H / 4 + 255) / 256)));
+  if (k <= 8) MOE_LAUNCH(MOE_KERNEL_COMBINE, k_combine<8>, cg, dim3(256), 0, s, T, H, k, gate, ys, y);
+  else MOE_LAUNCH(MOE_KERNEL_COMBINE, k_combine<16>, cg, dim3(256), 0, s, T, H, k, gate, ys, y);
   return hipGetLastError();
 }
 

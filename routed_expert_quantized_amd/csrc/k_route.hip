@@ -158,9 +158,17 @@ __global__ __launch_bounds__(1024) void k_group_scan(const uint64_t* __restrict_
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E) {
-    for (int c = 0; c < C; ++c) {
-      base[(int64_t)c * E + e] = cnt;
-      cnt += __popcll(mask[(int64_t)c * E + e]);
+    // masks of 8 chunks requested together, then counted in chunk order
+    for (int c0 = 0; c0 < C; c0 += 8) {
+      uint64_t mk[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mk[j] = c0 + j < C ? mask[(int64_t)(c0 + j) * E + e] : 0ull;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c0 + j < C) {
+          base[(int64_t)(c0 + j) * E + e] = cnt;
+          cnt += __popcll(mk[j]);
+        }
     }
     counts[e] = cnt;
   }

@@ -154,7 +154,10 @@ def test_gather_parity_small(T, E, H, I, k, scheme, xtype, path):
 LAYER_CASES = [("tiny", None, None, "auto"), ("decode40", None, None, "auto"), ("batched_int4", None, 16, "auto"),
                ("large_int4", None, 6, "auto"), ("prefill", None, 12, "auto"), ("batched_int4", 7, None, "auto"),
                ("batched_int4", None, 16, "gemm"), ("large_int4", None, 6, "gemm"), ("prefill", None, 12, "gather"),
-               ("decode40", None, None, "gemm"), ("prefill", 300, 8, "gemm")]
+               ("decode40", None, None, "gemm"), ("prefill", 300, 8, "gemm"),
+               # one token at the E=512, top-10 shapes: scan top-k, two blocks per lane (H=4096),
+               # the general down kernel (k*I > 4096)
+               ("large_int4", 1, None, "auto"), ("batched_int4", 1, None, "auto")]
 
 
 @pytest.mark.parametrize("name,T,sample,path", LAYER_CASES)
