@@ -511,7 +511,7 @@ __global__ __launch_bounds__(256) void k_gemm_dma(const uint16_t* __restrict__ a
     for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
       const int nm = min(16 * MT, cnt - m0);
       __syncthreads();
-      if (tid < 16 * MT) fs[tid] = tid < nm ? perm[beg + m0 + tid] : -1;
+      for (int i = tid; i < 16 * MT; i += 256) fs[i] = i < nm ? perm[beg + m0 + i] : -1;
       __syncthreads();
       // activation rows of this pass (rows past the assignments repeat row 0)
       int64_t aoff[D::NAI];
@@ -562,58 +562,61 @@ __global__ __launch_bounds__(256) void k_gemm_dma(const uint16_t* __restrict__ a
           for (int b = 0; b < D::NSC; ++b)
             sc[2 * c + b] = lds_read_u16(sb + (lr * D::BPS + g * D::SPAN / 32 + b) * 2);
         }
-        // activation fragments of MFMA step j: row mt*16 + r16, logical slot g*SPAN/8 + j
-        auto read_a = [&](int j, u32x4 (&a)[MT]) {
-  #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            a[mt] = lds_read16(ab + (mt * 16 + r16) * D::ARB + (((g * D::SPAN / 8 + j) ^ D::swz_a(r16)) * 16));
-        };
-        u32x4 acur[MT], anext[MT];
-        read_a(0, acur);
-        lds_wait_b(raw, sc);
-        lds_wait<MT>(acur);
-        uint32_t w[2][D::NW];
-        half2v s2[2][D::NSC];
-  #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-  #pragma unroll
-          for (int t = 0; t < D::NSL; ++t) {
-            const u32x4 v = raw[2 * c + t];
-            w[c][4 * t + 0] = v.x; w[c][4 * t + 1] = v.y; w[c][4 * t + 2] = v.z; w[c][4 * t + 3] = v.w;
-          }
-  #pragma unroll
-          for (int b = 0; b < D::NSC; ++b) {
-            // blocks past the row end (K tail) were clamped to valid memory; scale 0 drops them
-            const float sv =
-                q * D::BPS + g * D::SPAN / 32 + b < NB ? f16_bits_to_f32((uint16_t)sc[2 * c + b]) : 0.0f;
-            s2[c][b] = half2v{(_Float16)sv, (_Float16)sv};
-          }
-        }
-  #pragma unroll
-        for (int j = 0; j < D::NJ; ++j) {
-          if (j + 1 < D::NJ) read_a(j + 1, anext);
-          half8v b[2];
-  #pragma unroll
-          for (int c = 0; c < 2; ++c) b[c] = span_slice_f16<SCHEME, D::NW>(w[c], j, s2[c][j / 4]);
-  #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            if (mt < mtiles) {
-              const uint4 ra = make_uint4(acur[mt].x, acur[mt].y, acur[mt].z, acur[mt].w);
-              const half8v a = __builtin_bit_cast(half8v, order_for_b<SCHEME>(ra));
-  #pragma unroll
-              for (int c = 0; c < 2; ++c)
-                acc[mt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[c], acc[mt][c], 0, 0, 0);
-            }
-          }
-          if (j + 1 < D::NJ) {
-            lds_wait<MT>(anext);
-  #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acur[mt] = anext[mt];
-          }
-        }
+        // activation fragments of MFMA step j, M tiles mt0 .. mt0+G-1: row mt*16 + r16,
+      // logical slot g*SPAN/8 + j. Steps go (j, group) in order; the next
+      // group's fragments are read while the current group's MFMAs run.
+      constexpr int G = MT % 4 == 0 ? 4 : MT % 3 == 0 ? 3 : MT % 2 == 0 ? 2 : 1;
+      constexpr int NG = MT / G;
+      auto read_a = [&](int j, int grp, u32x4 (&a)[G]) {
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+          a[i] = lds_read16(ab + ((grp * G + i) * 16 + r16) * D::ARB + (((g * D::SPAN / 8 + j) ^ D::swz_a(r16)) * 16));
       };
+      u32x4 fa[2][G];
+      read_a(0, 0, fa[0]);
+      lds_wait_b(raw, sc);
+      lds_wait<G>(fa[0]);
+      uint32_t w[2][D::NW];
+      half2v s2[2][D::NSC];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int t = 0; t < D::NSL; ++t) {
+          const u32x4 v = raw[2 * c + t];
+          w[c][4 * t + 0] = v.x; w[c][4 * t + 1] = v.y; w[c][4 * t + 2] = v.z; w[c][4 * t + 3] = v.w;
+        }
+#pragma unroll
+        for (int b = 0; b < D::NSC; ++b) {
+          // blocks past the row end (K tail) were clamped to valid memory; scale 0 drops them
+          const float sv =
+              q * D::BPS + g * D::SPAN / 32 + b < NB ? f16_bits_to_f32((uint16_t)sc[2 * c + b]) : 0.0f;
+          s2[c][b] = half2v{(_Float16)sv, (_Float16)sv};
+        }
+      }
+      half8v b[2];
+#pragma unroll
+      for (int st = 0; st < D::NJ * NG; ++st) {
+        const int j = st / NG, grp = st % NG;
+        if (grp == 0) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) b[c] = span_slice_f16<SCHEME, D::NW>(w[c], j, s2[c][j / 4]);
+        }
+        if (st + 1 < D::NJ * NG) read_a((st + 1) / NG, (st + 1) % NG, fa[(st + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          if (grp * G + i < mtiles) {
+            const u32x4 f = fa[st & 1][i];
+            const half8v a = __builtin_bit_cast(half8v, order_for_b<SCHEME>(make_uint4(f.x, f.y, f.z, f.w)));
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              acc[grp * G + i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[c], acc[grp * G + i][c], 0, 0, 0);
+          }
+        }
+        if (st + 1 < D::NJ * NG) lds_wait<G>(fa[(st + 1) & 1]);
+      }
+    };
 
-      // Every iteration issues one stage and waits for the oldest one, so all
+    // Every iteration issues one stage and waits for the oldest one, so all
       // waits are the same constant; past the last chunk a stage is refilled with
       // the last chunk again (clamped, cache-resident) and never read.
       static_for<NS - 1>([&](auto R) { issue(min((int)decltype(R)::value, nchunks - 1), stage(R)); });
@@ -720,7 +723,8 @@ hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev
     const int maxu8 = (maxu + 7) / 8 * 8;
     // Tunings measured on MI355X. Whole 128-byte lines per stage with two stages
     // keep three workgroups per CU for one- and four-tile passes; six-tile passes
-    // (about 64 assignments per expert) stage half lines in three stages.
+    // (about 64 assignments per expert and more) stage half lines in three
+    // stages (taller passes measured no faster at ~256 assignments per expert).
     // int4 four-tile passes use half lines (whole lines exceed the registers).
     if (ex.scheme == MOE_Q_SYM8) {
       if (avg > 24) launch_dma_pair<MOE_Q_SYM8, 6, 3, 64>(maxu8, act, ex, k, g, h16, ys, out, s);

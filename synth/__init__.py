@@ -10,6 +10,8 @@ Workloads (shapes and distributions of the pages' models):
   batched_int4  T=64,   H=2048, E=512, k=10, I=512,  int4, x fp16, Zipf(1.1) expert popularity
   prefill       T=2048, H=2048, E=256, k=8,  I=512,  sym8, x bf16
   large_int4    T=16,   H=4096, E=512, k=10, I=1024, int4, x fp16, 60 layers, 27% token reuse
+  prefill8k     T=8192, H=2048, E=256, k=8,  I=512,  sym8, x bf16 (supplementary: ~256
+                assignments per expert, where the grouped GEMM is bound by the matrix cores)
 
 The 256-expert top-8, d_model 2048, 40-layer shape is the 35B-A3B model of
 "QwenのMoEルーターを観測してホットエキスパートを先読みしても速くならなかった"
@@ -31,7 +33,7 @@ F32, F16, BF16 = 0, 1, 2
 # oracle's router so that ~60% of the 512 experts are hit by 64 tokens.
 ZIPF_BETA_BATCHED = 0.62
 
-_WORKLOAD_IDS = {"tiny": 0, "decode40": 1, "batched_int4": 2, "prefill": 3, "large_int4": 4}
+_WORKLOAD_IDS = {"tiny": 0, "decode40": 1, "batched_int4": 2, "prefill": 3, "large_int4": 4, "prefill8k": 5}
 
 
 @dataclass(frozen=True)
@@ -67,6 +69,7 @@ WORKLOADS = {
     "prefill": Workload("prefill", T=2048, H=2048, E=256, k=8, I=512, scheme=SYM8, xtype=BF16),
     "large_int4": Workload("large_int4", T=16, H=4096, E=512, k=10, I=1024, scheme=INT4, xtype=F16,
                            layers=60, router_std=4096 ** -0.5, reuse_p=0.27),
+    "prefill8k": Workload("prefill8k", T=8192, H=2048, E=256, k=8, I=512, scheme=SYM8, xtype=BF16),
 }
 
 

@@ -157,7 +157,9 @@ LAYER_CASES = [("tiny", None, None, "auto"), ("decode40", None, None, "auto"), (
                ("decode40", None, None, "gemm"), ("prefill", 300, 8, "gemm"),
                # one token at the E=512, top-10 shapes: scan top-k, two blocks per lane (H=4096),
                # the general down kernel (k*I > 4096)
-               ("large_int4", 1, None, "auto"), ("batched_int4", 1, None, "auto")]
+               ("large_int4", 1, None, "auto"), ("batched_int4", 1, None, "auto"),
+               # ~256 assignments per expert: 18-tile GEMM passes
+               ("prefill8k", None, 8, "auto")]
 
 
 @pytest.mark.parametrize("name,T,sample,path", LAYER_CASES)
