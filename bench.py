@@ -299,7 +299,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16xf16->f32 (mfma)" if gemm else "f32",
+        "dtype": ("f16xf16->f32 (grouped GEMM, mfma); f32 router" if gemm else
+                  ("f16xf16->f32 (gate/up, v_dot2); f32 router, down, combine" if w.xtype == 1 else "f32")),
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
                    "codec": "sym8" if w.scheme == 0 else "int4",
