@@ -469,10 +469,6 @@ __device__ __forceinline__ float xdot(const Block<SCHEME>& c, const XReg<SCHEME,
   else return block_dot<SCHEME>(c, r.f);
 }
 
-// h staged in LDS with 4 floats of padding after every 32, so the 16 lanes of
-// a row group (each reading its own block) spread over the banks.
-__device__ __forceinline__ int hpad(int i) { return i + (i >> 5) * 4; }
-
 // silu(z) = z * sigmoid(z), with the hardware exponential and reciprocal
 // (about 1 ulp each); exp overflow for very negative z gives 0.
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }

@@ -43,7 +43,9 @@ static void with_xtype(int xt, F&& f) {
 // With FROM_LOGITS the wave first picks the top k from the router logits (each
 // workgroup redoes this small step so no cross-workgroup sync is needed);
 // workgroup 0 publishes the routing for the down kernel and the caller.
-template <int SCHEME, int XT, int NBJ, int RP, bool FROM_LOGITS, int VPL>
+// With H16 the activation is stored as fp16 (round to nearest even) for the
+// slot-parallel down kernel, else as fp32.
+template <int SCHEME, int XT, int NBJ, int RP, bool FROM_LOGITS, int VPL, bool H16>
 __global__ __launch_bounds__(256) void k_gate_up_t1(const void* __restrict__ x, ExpertsDev ex, int k, int renorm,
                                                     const float* __restrict__ logits,
                                                     const int32_t* __restrict__ idx_in,
@@ -109,82 +111,67 @@ __global__ __launch_bounds__(256) void k_gate_up_t1(const void* __restrict__ x, 
     }
     ag = wave_sum(ag);
     au = wave_sum(au);
-    if (lane == 0 && n0 + r < I) h[(int64_t)slot * I + n0 + r] = silu(ag) * au;
+    if (lane == 0 && n0 + r < I) {
+      const float hv = silu(ag) * au;
+      if constexpr (H16) reinterpret_cast<uint16_t*>(h)[(int64_t)slot * I + n0 + r] = __builtin_bit_cast(uint16_t, (_Float16)hv);
+      else h[(int64_t)slot * I + n0 + r] = hv;
+    }
   }
 }
 
-// Per-thread float4 registers that stage h (k * I floats) through LDS in the
-// single-token down kernel: 128 threads x 8 float4 = 4096 floats.
-constexpr int kHRegs = 8;
-
-// Grid: ceil(H / 8), two waves of four 16-lane row groups. For each slot in
-// order the row of the slot's expert is dotted with h[slot], then
-// y += gate * that (with gate == nullptr, y[slot][m] = that).
-//
-// k_down_t1_lds: k <= KC slots and k * I <= 128 * 4 * kHRegs. h is requested
-// first (into registers), then every slot's code rows, all unconditionally, so
-// one wait covers h and the rows stream in together; h goes to LDS for the
-// dot products.
-template <int SCHEME, int NBJ, int KC>
-__global__ __launch_bounds__(128) void k_down_t1_lds(ExpertsDev ex, int k, const int32_t* __restrict__ idx,
-                                                     const float* __restrict__ gate, const float* __restrict__ h,
-                                                     float* __restrict__ y) {
-  extern __shared__ float hs[];
+// Single-token down, one wave per slot. Grid: ceil(H / (4 RW)) workgroups of
+// k waves. Wave q takes slot q; its four 16-lane row groups take RW rows each,
+// and lane ll of a group owns blocks ll + 16 j of the I inputs for those rows,
+// so the fp16 h block it loads once serves all RW rows. Row sums over the 16
+// lanes are kept in LDS; after a barrier the first 4 RW threads add the slots in
+// slot order, each times its gate (with gate == nullptr every wave writes its
+// own slot's rows, y[q][m]). Many small waves per CU let the dot products of
+// the rows that have arrived overlap the loads still in flight.
+template <int SCHEME, int NBJ, int RW>
+__global__ __launch_bounds__(1024) void k_down_t1_slots(ExpertsDev ex, int k, const int32_t* __restrict__ idx,
+                                                       const float* __restrict__ gate,
+                                                       const uint16_t* __restrict__ h16, float* __restrict__ y) {
+  __shared__ float part[kMaxK][4 * RW];
   const int tid = (int)threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int lg = lane >> 4, ll = lane & 15;
+  const int q = tid >> 6, lane = tid & 63, lg = lane >> 4, ll = lane & 15;
   const int H = ex.H, I = ex.I, NBI = I / 32;
-  const int m = ((int)blockIdx.x * 2 + wave) * 4 + lg;
-  const int mm = min(m, H - 1);
+  const int mb = (int)blockIdx.x * 4 * RW, m0 = mb + lg * RW;
   const int64_t rb = row_bytes<SCHEME>(I);
-  float4 hr[kHRegs];
+  XBlockH<SCHEME> hb[NBJ];
 #pragma unroll
-  for (int r = 0; r < kHRegs; ++r) hr[r] = *reinterpret_cast<const float4*>(h + min((tid + 128 * r) * 4, k * I - 4));
-  __builtin_amdgcn_sched_barrier(0);  // keep the h loads ahead of the code rows
-  Block<SCHEME> c[KC][NBJ];
-  float sc[KC][NBJ];
+  for (int j = 0; j < NBJ; ++j) hb[j] = load_xblock_h<SCHEME>(h16, (int64_t)q * I, min(ll + 16 * j, NBI - 1));
+  const int e = idx[q];
+  Block<SCHEME> c[RW][NBJ];
+  float sc[RW][NBJ];
 #pragma unroll
-  for (int q = 0; q < KC; ++q) {
-    const int64_t row = (int64_t)idx[min(q, k - 1)] * H + mm;
+  for (int r = 0; r < RW; ++r) {
+    const int64_t row = (int64_t)e * H + min(m0 + r, H - 1);
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) {
       const int b = min(ll + 16 * j, NBI - 1);
-      c[q][j] = load_block<SCHEME>(ex.wd + row * rb, b);
-      sc[q][j] = f16_bits_to_f32(ex.sd[row * NBI + b]);
+      c[r][j] = load_block<SCHEME>(ex.wd + row * rb, b);
+      sc[r][j] = f16_bits_to_f32(ex.sd[row * NBI + b]);
     }
   }
-  __builtin_amdgcn_sched_barrier(0);  // all rows requested before any wait
-  // surplus threads rewrite the last chunk with the same data (no branch, so the
-  // h loads stay where they were issued)
 #pragma unroll
-  for (int r = 0; r < kHRegs; ++r)
-    *reinterpret_cast<float4*>(hs + hpad(min((tid + 128 * r) * 4, k * I - 4))) = hr[r];
+  for (int r = 0; r < RW; ++r) {
+    float part_r = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NBJ; ++j)
+      part_r = fmaf(ll + 16 * j < NBI ? sc[r][j] : 0.0f, block_dot_h<SCHEME>(c[r][j], hb[j]), part_r);
+    part_r = row_sum16(part_r);
+    if (ll == 0) {
+      if (gate) part[q][lg * RW + r] = part_r;
+      else if (m0 + r < H) y[(int64_t)q * H + m0 + r] = part_r;
+    }
+  }
+  if (!gate) return;
   __syncthreads();
-  float acc = 0.0f;
-#pragma unroll
-  for (int q = 0; q < KC; ++q) {
-    if (q < k) {
-      float part = 0.0f;
-#pragma unroll
-      for (int j = 0; j < NBJ; ++j) {
-        const int b = ll + 16 * j;
-        if (b < NBI) {
-          float hv[32];
-          const float* src = hs + hpad(q * I + 32 * b);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float4 v = *reinterpret_cast<const float4*>(src + 4 * i);
-            hv[4 * i] = v.x; hv[4 * i + 1] = v.y; hv[4 * i + 2] = v.z; hv[4 * i + 3] = v.w;
-          }
-          part = fmaf(sc[q][j], block_dot<SCHEME>(c[q][j], hv), part);
-        }
-      }
-      part = row_sum16(part);
-      if (gate) acc = fmaf(gate[q], part, acc);
-      else if (ll == 0 && m < H) y[(int64_t)q * H + m] = part;
-    }
+  if (tid < 4 * RW && mb + tid < H) {
+    float acc = 0.0f;
+    for (int s = 0; s < k; ++s) acc = fmaf(gate[s], part[s][tid], acc);
+    y[mb + tid] = acc;
   }
-  if (gate && ll == 0 && m < H) y[m] = acc;
 }
 
 // General single-token down (any k, any I): KC slots' rows in flight at a
@@ -463,11 +450,17 @@ __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const floa
 }
 
 // ------------------------------------------------------------------ launchers
+// The single-token down kernel: one wave per slot (fp16 h) for I <= 1024, the
+// general kernel (fp32 h) above that.
+constexpr int kDownRows = 2;
+
 hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int k, int renorm,
                             const float* logits, const int32_t* idx_in, const float* gate_in,
                             int32_t* idx_ws, float* gate_ws, int32_t* idx_user, float* gate_user,
                             float* h, float* y, hipStream_t s) {
   const bool from_logits = logits != nullptr;
+  const int nbi = (ex.I / 32 + 15) / 16;
+  const bool slots = nbi <= 2;
   const int nbj = (ex.H / 32 + 63) / 64;  // 1 (H <= 2048) or 2 (H <= 4096)
   with_scheme(ex.scheme, [&](auto S) {
     with_xtype(xtype, [&](auto X) {
@@ -476,15 +469,19 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
         constexpr int NBJ = decltype(NBJc)::value, RP = decltype(RPc)::value;
         const int bps = (ex.I + 4 * RP - 1) / (4 * RP);
         dim3 grid(k * bps);
-        if (!from_logits)
-          MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_t1<SC, XT, NBJ, RP, false, 1>), grid, dim3(256), 0, s, x, ex, k, renorm,
-                             logits, idx_in, idx_ws, gate_ws, idx_user, gate_user, h, bps);
-        else if (ex.E <= 256)
-          MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_t1<SC, XT, NBJ, RP, true, 4>), grid, dim3(256), 0, s, x, ex, k, renorm,
-                             logits, idx_in, idx_ws, gate_ws, idx_user, gate_user, h, bps);
-        else
-          MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_t1<SC, XT, NBJ, RP, true, 16>), grid, dim3(256), 0, s, x, ex, k, renorm,
-                             logits, idx_in, idx_ws, gate_ws, idx_user, gate_user, h, bps);
+        auto launch = [&](auto FLc, auto VPLc, auto H16c) {
+          constexpr bool FL = decltype(FLc)::value != 0, H16 = decltype(H16c)::value != 0;
+          constexpr int VPL = decltype(VPLc)::value;
+          MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_t1<SC, XT, NBJ, RP, FL, VPL, H16>), grid, dim3(256), 0, s, x, ex,
+                     k, renorm, logits, idx_in, idx_ws, gate_ws, idx_user, gate_user, h, bps);
+        };
+        auto with_h = [&](auto FLc, auto VPLc) {
+          if (slots) launch(FLc, VPLc, IC<1>{});
+          else launch(FLc, VPLc, IC<0>{});
+        };
+        if (!from_logits) with_h(IC<0>{}, IC<1>{});
+        else if (ex.E <= 256) with_h(IC<1>{}, IC<4>{});
+        else with_h(IC<1>{}, IC<16>{});
       };
       if (nbj <= 1) go(IC<1>{}, IC<2>{});
       else go(IC<2>{}, IC<1>{});
@@ -492,23 +489,25 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
   });
   const int32_t* idx = from_logits ? idx_ws : idx_in;
   const float* gate = from_logits ? gate_ws : gate_in;
-  const int nbi = (ex.I / 32 + 15) / 16;
-  const size_t lds = (size_t)k * ex.I / 32 * 36 * sizeof(float);
-  const bool hlds = nbi == 1 && k <= 8 && (int64_t)k * ex.I <= 128 * 4 * kHRegs;
-  dim3 grid((ex.H + 7) / 8);
   with_scheme(ex.scheme, [&](auto S) {
     constexpr int SC = decltype(S)::value;
-    if (hlds) {
-      MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_t1_lds<SC, 1, 8>), grid, dim3(128), lds, s, ex, k, idx, gate, h, y);
+    if (slots) {
+      dim3 grid((ex.H + 4 * kDownRows - 1) / (4 * kDownRows));
+      const uint16_t* h16 = reinterpret_cast<const uint16_t*>(h);
+      if (nbi <= 1)
+        MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_t1_slots<SC, 1, kDownRows>), grid, dim3(64 * k), 0, s, ex, k, idx, gate,
+                   h16, y);
+      else
+        MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_t1_slots<SC, 2, kDownRows>), grid, dim3(64 * k), 0, s, ex, k, idx, gate,
+                   h16, y);
       return;
     }
+    dim3 grid((ex.H + 7) / 8);
     auto go = [&](auto NBJc) {
       constexpr int NBJ = decltype(NBJc)::value;
       MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_t1<SC, NBJ>), grid, dim3(128), 0, s, ex, k, idx, gate, h, y);
     };
-    if (nbi <= 1) go(IC<1>{});
-    else if (nbi <= 2) go(IC<2>{});
-    else if (nbi <= 4) go(IC<4>{});
+    if (nbi <= 4) go(IC<4>{});
     else go(IC<8>{});
   });
   return hipGetLastError();

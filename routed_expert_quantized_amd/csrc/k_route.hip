@@ -9,21 +9,25 @@
 namespace moe {
 
 // ---------------------------------------------------------------- logits, few tokens
-// One wave per expert row: logits[t][e] = R[e] . x[t] in fp32, for every token.
-// The row is loaded once into registers (NCH float4 chunks per lane, all loads
-// issued together) and reused for each token; tokens go TU at a time with
-// their activation loads issued before any arithmetic.
-template <int XT, int NCH, int TU>
-__global__ __launch_bounds__(64) void k_logits_rows(const void* __restrict__ x, int T, int H,
-                                                    const float* __restrict__ R, int E,
-                                                    float* __restrict__ logits) {
-  const int lane = threadIdx.x;
+// WPE waves per expert row: logits[t][e] = R[e] . x[t] in fp32, for every token.
+// Wave w owns the columns of chunks [w NCH, (w+1) NCH) (a chunk is 256
+// columns, 4 per lane). Its part of the row is loaded once into registers (all
+// loads issued together) and reused for each token; tokens go TU at a time with
+// their activation loads issued before any arithmetic. The waves' partial sums
+// meet in LDS and are added in wave order.
+template <int XT, int NCH, int TU, int WPE>
+__global__ __launch_bounds__(64 * WPE) void k_logits_rows(const void* __restrict__ x, int T, int H,
+                                                          const float* __restrict__ R, int E,
+                                                          float* __restrict__ logits) {
+  __shared__ float red[WPE][TU];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int e = blockIdx.x;
+  const int c0 = w * NCH;
   const float* row = R + (int64_t)e * H;
   float4 r[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int i = min(lane * 4 + 256 * c, H - 4);
+    const int i = min(lane * 4 + 256 * (c0 + c), H - 4);
     r[c] = *reinterpret_cast<const float4*>(row + i);
   }
   for (int t0 = 0; t0 < T; t0 += TU) {
@@ -32,14 +36,15 @@ __global__ __launch_bounds__(64) void k_logits_rows(const void* __restrict__ x, 
     for (int u = 0; u < TU; ++u) {
       const int t = min(t0 + u, T - 1);
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) v[u][c] = load_x4<XT>(x, (int64_t)t * H + min(lane * 4 + 256 * c, H - 4));
+      for (int c = 0; c < NCH; ++c)
+        v[u][c] = load_x4<XT>(x, (int64_t)t * H + min(lane * 4 + 256 * (c0 + c), H - 4));
     }
 #pragma unroll
     for (int u = 0; u < TU; ++u) {
       float acc = 0.0f;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        if (lane * 4 + 256 * c < H) {
+        if (lane * 4 + 256 * (c0 + c) < H) {
           acc = fmaf(r[c].x, v[u][c].x, acc);
           acc = fmaf(r[c].y, v[u][c].y, acc);
           acc = fmaf(r[c].z, v[u][c].z, acc);
@@ -47,7 +52,21 @@ __global__ __launch_bounds__(64) void k_logits_rows(const void* __restrict__ x, 
         }
       }
       acc = wave_sum(acc);
-      if (lane == 0 && t0 + u < T) logits[(int64_t)(t0 + u) * E + e] = acc;
+      if constexpr (WPE == 1) {
+        if (lane == 0 && t0 + u < T) logits[(int64_t)(t0 + u) * E + e] = acc;
+      } else if (lane == 0) {
+        red[w][u] = acc;
+      }
+    }
+    if constexpr (WPE > 1) {
+      __syncthreads();
+      if (w == 0 && lane < TU && t0 + lane < T) {
+        float acc = red[0][lane];
+#pragma unroll
+        for (int q = 1; q < WPE; ++q) acc += red[q][lane];
+        logits[(int64_t)(t0 + lane) * E + e] = acc;
+      }
+      __syncthreads();
     }
   }
 }
@@ -280,6 +299,9 @@ __global__ __launch_bounds__(1024) void k_logits_mfma(const void* __restrict__ x
   }
 }
 
+// Waves per expert row in the few-token router kernel.
+constexpr int kLogitsWaves = 4;
+
 hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R, int E, float* logits,
                          int* nsplit, hipStream_t s) {
   *nsplit = 1;
@@ -316,15 +338,23 @@ hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R,
       default: with_tile(std::integral_constant<int, MOE_BF16>{}); break;
     }
   } else {
-    const int nch = (H + 255) / 256;
+    // chunks of 256 columns per wave, kLogitsWaves waves per expert row
+    const int nch = ((H + 255) / 256 + kLogitsWaves - 1) / kLogitsWaves;
     auto go = [&](auto NC) {
-      constexpr int N = decltype(NC)::value;
+      constexpr int N = decltype(NC)::value, WPE = kLogitsWaves;
       constexpr int TU = N >= 16 ? 2 : N >= 8 ? 4 : 8;
-      switch (xtype) {
-        case MOE_F32: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_F32, N, TU>), dim3(E), dim3(64), 0, s, x, T, H, R, E, logits); break;
-        case MOE_F16: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_F16, N, TU>), dim3(E), dim3(64), 0, s, x, T, H, R, E, logits); break;
-        default:      MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_BF16, N, TU>), dim3(E), dim3(64), 0, s, x, T, H, R, E, logits); break;
-      }
+      const dim3 block(64 * WPE);
+      // a single token takes the one-token unroll (no repeated activation loads)
+      auto launch = [&](auto TUc) {
+        constexpr int U = decltype(TUc)::value;
+        switch (xtype) {
+          case MOE_F32: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_F32, N, U, WPE>), dim3(E), block, 0, s, x, T, H, R, E, logits); break;
+          case MOE_F16: MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_F16, N, U, WPE>), dim3(E), block, 0, s, x, T, H, R, E, logits); break;
+          default:      MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_rows<MOE_BF16, N, U, WPE>), dim3(E), block, 0, s, x, T, H, R, E, logits); break;
+        }
+      };
+      if (T == 1) launch(std::integral_constant<int, 1>{});
+      else launch(std::integral_constant<int, TU>{});
     };
     if (nch <= 1) go(std::integral_constant<int, 1>{});
     else if (nch <= 2) go(std::integral_constant<int, 2>{});

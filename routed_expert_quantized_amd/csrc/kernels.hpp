@@ -61,7 +61,8 @@ hipError_t launch_topk(const float* logits, int nsplit, int T, int E, int k, int
                        int32_t* idx2, float* gate2, hipStream_t s);
 hipError_t launch_group(const int32_t* idx, int T, int k, int E, const GroupBufs& g, hipStream_t s);
 
-// Single-token decode: gate/up + SwiGLU into h[k][I], then down + combine.
+// Single-token decode: gate/up + SwiGLU into h[k][I] (fp16 for I <= 1024, where
+// the one-wave-per-slot down kernel runs; fp32 otherwise), then down + combine.
 // With logits != nullptr the routing is computed from them inside the gate/up
 // kernel (and written to idx_ws/gate_ws and the optional user copies); otherwise
 // idx/gate are read from idx_in/gate_in.

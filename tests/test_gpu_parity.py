@@ -117,7 +117,7 @@ def test_group_bit_exact(T, k, E):
 # has ~100 assignments per expert (several passes at every tile height) and a
 # K tail (H=192); (48, 8, 128, 192, 2) takes four-tile passes with a K tail in
 # the down projection (I=192).
-SMALL = [(1, 6, 96, 64, 3), (1, 16, 256, 128, 4), (5, 6, 96, 64, 3), (37, 9, 160, 96, 4), (3, 2, 4096, 4096, 2),
+SMALL = [(1, 6, 96, 64, 3), (1, 16, 256, 128, 4), (1, 4, 128, 2048, 3), (5, 6, 96, 64, 3), (37, 9, 160, 96, 4), (3, 2, 4096, 4096, 2),
          (2, 16, 64, 32, 16), (200, 4, 192, 128, 2), (48, 8, 128, 192, 2)]
 
 
