@@ -80,6 +80,17 @@ def gate_up_bytes(w) -> int:
     return 2 * w.I * w.H // 32 * (per_block + 2)
 
 
+def dtype_name(w, gemm: bool) -> str:
+    """The arithmetic each stage of the timed path runs in."""
+    if gemm:
+        return "f16xf16->f32 (grouped GEMM, mfma); f32 router, combine"
+    if w.T > 1:
+        return "f32 (grouped matvec)"
+    gu = "f16xf16->f32 (v_dot2)" if w.xtype == 1 else "f32"
+    down = "f16xf16->f32 (v_dot2, fp16 h)" if w.I <= 1024 else "f32"
+    return f"gate/up {gu}; down {down}; f32 router, combine"
+
+
 def build_layers(w, nl, seed, rq, synth, torch):
     """nl layers of device experts (quantised on the device) and host-drawn routers."""
     pools, routers = [], []
@@ -299,8 +310,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("f16xf16->f32 (grouped GEMM, mfma); f32 router" if gemm else
-                  ("f16xf16->f32 (gate/up, v_dot2); f32 router, down, combine" if w.xtype == 1 else "f32")),
+        "dtype": dtype_name(w, gemm),
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
                    "codec": "sym8" if w.scheme == 0 else "int4",

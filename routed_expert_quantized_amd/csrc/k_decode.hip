@@ -40,9 +40,10 @@ static void with_xtype(int xt, F&& f) {
 // ------------------------------------------------------------------ T = 1
 // Grid: k slots x blocks_per_slot. A wave computes RP (gate row n, up row I+n)
 // pairs of its slot's expert and writes h[slot][n] = silu(gate) * up.
-// With FROM_LOGITS the wave first picks the top k from the router logits (each
-// workgroup redoes this small step so no cross-workgroup sync is needed);
-// workgroup 0 publishes the routing for the down kernel and the caller.
+// With FROM_LOGITS wave 0 of each workgroup first picks the top k from the
+// router logits (every workgroup redoes this small step, so no cross-workgroup
+// sync is needed); one workgroup publishes the routing for the down kernel and
+// the caller.
 // With H16 the activation is stored as fp16 (round to nearest even) for the
 // slot-parallel down kernel, else as fp32.
 template <int SCHEME, int XT, int NBJ, int RP, bool FROM_LOGITS, int VPL, bool H16>
@@ -71,14 +72,20 @@ __global__ __launch_bounds__(256) void k_gate_up_t1(const void* __restrict__ x, 
     int my_idx;
     float my_gate;
     const bool publisher = blockIdx.x == (k - 1) * blocks_per_slot;
-    wave_topk<VPL>(logits, ex.E, k, renorm != 0, my_idx, my_gate, publisher ? k : slot + 1);
-    if (publisher && wave == 0 && lane < k) {
-      idx_ws[lane] = my_idx;
-      gate_ws[lane] = my_gate;
-      if (idx_user) idx_user[lane] = my_idx;
-      if (gate_user) gate_user[lane] = my_gate;
+    // wave 0 picks the routing; the other waves wait for it at the barrier
+    __shared__ int e_sh;
+    if (wave == 0) {
+      wave_topk<VPL>(logits, ex.E, k, renorm != 0, my_idx, my_gate, publisher ? k : slot + 1);
+      if (publisher && lane < k) {
+        idx_ws[lane] = my_idx;
+        gate_ws[lane] = my_gate;
+        if (idx_user) idx_user[lane] = my_idx;
+        if (gate_user) gate_user[lane] = my_gate;
+      }
+      if (lane == slot) e_sh = my_idx;
     }
-    e = __builtin_amdgcn_readlane(my_idx, slot);
+    __syncthreads();
+    e = e_sh;
   } else {
     e = idx_in[slot];
   }
@@ -483,7 +490,7 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
         else if (ex.E <= 256) with_h(IC<1>{}, IC<4>{});
         else with_h(IC<1>{}, IC<16>{});
       };
-      if (nbj <= 1) go(IC<1>{}, IC<2>{});
+      if (nbj <= 1) go(IC<1>{}, IC<1>{});
       else go(IC<2>{}, IC<1>{});
     });
   });
