@@ -91,6 +91,40 @@ def dtype_name(w, gemm: bool) -> str:
     return f"gate/up {gu}; down {down}; f32 router, combine"
 
 
+def stream_ceiling(nbytes: int, rq, torch) -> dict:
+    """A plain streaming read of one layer's routed bytes (moe_stream_read), as
+    back-to-back launches in a HIP graph over distinct buffers that together far
+    exceed the 256 MB MALL: the bandwidth a kernel moving that many bytes can
+    reach on this GPU, next to the HBM peak."""
+    nb = (nbytes + 15) // 16 * 16
+    nbuf = max(2, min(64, -(-(2 << 30) // nb)))
+    bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    reps = max(2, 256 // nbuf)
+
+    def run():
+        for b in bufs:
+            rq.moe_stream_read(b, nb)
+
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * nbuf)
+    del g, bufs
+    gbps = nb / (us * 1e-6) / 1e9
+    return {"bytes": nb, "us_per_read": round(us, 3), "gbps": round(gbps, 1),
+            "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4), "buffers": nbuf}
+
+
 def build_layers(w, nl, seed, rq, synth, torch):
     """nl layers of device experts (quantised on the device) and host-drawn routers."""
     pools, routers = [], []
@@ -290,6 +324,8 @@ def main():
     gu_flops = 2.0 * w.T * w.k * 2 * w.I * w.H
     mfma_tflops = gu_flops / (gu_us * 1e-6) / 1e12
 
+    ceiling = stream_ceiling(int(round(routed_bytes)), rq, torch)
+
     traffic = None
     tf = os.path.join(ROOT, "profiles", f"traffic_{dom}_{w.name}.json")
     sha = kernel_source_sha("gemm" if gemm else "gather")
@@ -323,6 +359,7 @@ def main():
         "unique_experts_per_layer": round(uniq_mean, 2),
         "routed_hbm_gbps": round(routed_gbps, 1),
         "routed_hbm_frac": round(routed_gbps / HBM_PEAK_GBPS, 4),
+        "stream_read_ceiling": {**ceiling, "layer_vs_ceiling": round(routed_gbps / ceiling["gbps"], 4)},
         "kernel_us": {n: round(v, 3) for n, v in kern_us.items()},
         "roofline": {"kernel": kname, "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

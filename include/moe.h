@@ -183,6 +183,14 @@ enum {
 moe_status moe_timer_start(int32_t kernel, int32_t capacity);
 moe_status moe_timer_read(float* ms, int32_t capacity, int32_t* count);
 
+/* Benchmark support: the achievable-bandwidth reference. Reads `bytes` bytes
+ * (a positive multiple of 16) of the device buffer `buf` once, with coalesced
+ * 16-byte non-temporal loads spread over the whole GPU, and writes nothing.
+ * It is the plain streaming read that a gathered kernel moving the same bytes
+ * is compared with, next to the HBM peak. Errors: MOE_ERR_INVALID_ARG for a
+ * null or misaligned buf or a bad size. */
+moe_status moe_stream_read(const void* buf, int64_t bytes, void* stream);
+
 /* Static description of a status code. */
 const char* moe_status_str(moe_status s);
 

@@ -27,7 +27,8 @@ MOE_FLAG_RENORM, MOE_FLAG_PATH_GATHER, MOE_FLAG_PATH_GEMM = 1, 2, 4
 
 # Every function the header declares; the library must export all of them.
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_group", "moe_gather_qmm_forward", "moe_layer_forward",
-           "moe_quantize", "moe_timer_start", "moe_timer_read", "moe_status_str", "moe_last_error")
+           "moe_quantize", "moe_timer_start", "moe_timer_read", "moe_stream_read", "moe_status_str",
+           "moe_last_error")
 
 (MOE_KERNEL_ROUTE_LOGITS, MOE_KERNEL_TOPK, MOE_KERNEL_GROUP, MOE_KERNEL_GATE_UP, MOE_KERNEL_DOWN, MOE_KERNEL_COMBINE,
  MOE_KERNEL_GEMM_GATE_UP, MOE_KERNEL_GEMM_DOWN, MOE_KERNEL_QUANTIZE) = range(9)
@@ -66,6 +67,7 @@ def lib() -> ctypes.CDLL:
             "moe_quantize": ([P, I64, I32, I32, P, P, P], ctypes.c_int),
             "moe_timer_start": ([I32, I32], ctypes.c_int),
             "moe_timer_read": ([P, I32, P], ctypes.c_int),
+            "moe_stream_read": ([P, I64, P], ctypes.c_int),
             "moe_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "moe_last_error": ([], ctypes.c_char_p),
         }
@@ -170,6 +172,13 @@ def moe_quantize(w: torch.Tensor, scheme: int, stream=None):
     scales = torch.empty(w.shape[:-1] + (K // 32,), dtype=torch.int16, device=w.device)
     _check("moe_quantize", lib().moe_quantize(_p(w), rows, K, scheme, _p(codes), _p(scales), _stream(stream)))
     return codes, scales
+
+
+def moe_stream_read(buf: torch.Tensor, nbytes: int | None = None, stream=None) -> None:
+    """Plain streaming read of the first nbytes bytes of buf (the bandwidth reference)."""
+    _device_tensor(buf, "buf")
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check("moe_stream_read", lib().moe_stream_read(_p(buf), n, _stream(stream)))
 
 
 def moe_route(x: torch.Tensor, router_w: torch.Tensor, k: int, flags: int = MOE_FLAG_RENORM,

@@ -429,8 +429,15 @@ struct DmaTile {
   static __device__ __forceinline__ int swz_a(int row) { return SPR == 8 ? (row >> 1) & 7 : row & 15; }
 };
 
+// Waves per SIMD the register allocation must leave room for.
+template <int SCHEME, int MT>
+__host__ __device__ constexpr int gemm_dma_waves() {
+  return 1;
+}
+
 template <int SCHEME, int MODE, int MT, int NS, int LB>
-__global__ __launch_bounds__(256) void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gemm_dma_waves<SCHEME, MT>(), 8)))
+void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k,
                                                   const int32_t* __restrict__ uniq,
                                                   const int32_t* __restrict__ n_uniq,
                                                   const int32_t* __restrict__ counts,

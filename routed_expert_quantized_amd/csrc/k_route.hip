@@ -85,24 +85,22 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   if (t >= T) return;
   const float* row = logits + (int64_t)t * E;
   if (nsplit > 1) {
-    // loads of four planes for all of the lane's logits go out together, then
-    // are added in plane order
+    // the loads of every plane for all of the lane's logits go out together,
+    // then are added in plane order
     const int64_t plane = (int64_t)T * E;
+    float p[kMaxLogitSplits][VPL];
+#pragma unroll
+    for (int q = 0; q < kMaxLogitSplits; ++q)
+#pragma unroll
+      for (int j = 0; j < VPL; ++j)
+        p[q][j] = (q < nsplit && lane + 64 * j < E) ? row[q * plane + lane + 64 * j] : 0.0f;
     float v[VPL];
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) v[j] = lane + 64 * j < E ? row[lane + 64 * j] : 0.0f;
-    for (int sp = 1; sp < nsplit; sp += 4) {
-      float p[4][VPL];
+    for (int j = 0; j < VPL; ++j) {
+      v[j] = p[0][j];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int j = 0; j < VPL; ++j)
-          p[q][j] = (sp + q < nsplit && lane + 64 * j < E) ? row[(sp + q) * plane + lane + 64 * j] : 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int j = 0; j < VPL; ++j)
-          if (sp + q < nsplit) v[j] += p[q][j];
+      for (int q = 1; q < kMaxLogitSplits; ++q)
+        if (q < nsplit) v[j] += p[q][j];
     }
 #pragma unroll
     for (int j = 0; j < VPL; ++j)
@@ -215,6 +213,54 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
   const int c = t >> 6, bit = t & 63;
   const uint64_t below = bit ? (mask[(int64_t)c * E + e] & ((1ull << bit) - 1ull)) : 0ull;
   perm[base[(int64_t)c * E + e] + __popcll(below)] = (int32_t)f;
+}
+
+// The same grouping in one workgroup when the chunk masks fit in LDS
+// (ceil(T/64) * E <= kGroupLdsCells): the bitmasks and per-chunk bases live in
+// LDS, so the three steps need no round trips through memory and one launch.
+// Outputs are identical to the three-kernel form.
+__global__ __launch_bounds__(1024) void k_group_fused(const int32_t* __restrict__ idx, int T, int k, int E,
+                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm, int32_t* __restrict__ uniq,
+                                                      int32_t* __restrict__ n_uniq) {
+  __shared__ unsigned long long m[kGroupLdsCells];
+  __shared__ int base[kGroupLdsCells];
+  __shared__ int smem[64];
+  const int tid = (int)threadIdx.x;
+  const int C = (T + 63) / 64, cells = C * E, n = T * k;
+  for (int i = tid; i < cells; i += 1024) m[i] = 0ull;
+  __syncthreads();
+  for (int f = tid; f < n; f += 1024) {
+    const int t = f / k;
+    atomicOr(&m[(t >> 6) * E + idx[f]], 1ull << (t & 63));
+  }
+  __syncthreads();
+  const int e = tid;
+  int cnt = 0;
+  if (e < E) {
+    for (int c = 0; c < C; ++c) {
+      base[c * E + e] = cnt;
+      cnt += __popcll(m[c * E + e]);
+    }
+    counts[e] = cnt;
+  }
+  int total;
+  const int off = block_exclusive_scan_1024(cnt, smem, total);
+  if (e < E) {
+    offsets[e] = off;
+    for (int c = 0; c < C; ++c) base[c * E + e] += off;
+  }
+  if (e == 0) offsets[E] = total;
+  int nu;
+  const int pos = block_exclusive_scan_1024(cnt > 0 ? 1 : 0, smem, nu);
+  if (e < E && cnt > 0) uniq[pos] = e;
+  if (e == 0) *n_uniq = nu;
+  __syncthreads();  // every expert's bases are in LDS
+  for (int f = tid; f < n; f += 1024) {
+    const int t = f / k, cell = (t >> 6) * E + idx[f], bit = t & 63;
+    const unsigned long long below = bit ? (m[cell] & ((1ull << bit) - 1ull)) : 0ull;
+    perm[base[cell] + __popcll(below)] = f;
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -379,6 +425,11 @@ hipError_t launch_topk(const float* logits, int nsplit, int T, int E, int k, int
 
 hipError_t launch_group(const int32_t* idx, int T, int k, int E, const GroupBufs& g, hipStream_t s) {
   const int C = (T + 63) / 64;
+  if ((int64_t)C * E <= kGroupLdsCells) {
+    MOE_LAUNCH(MOE_KERNEL_GROUP, k_group_fused, dim3(1), dim3(1024), 0, s, idx, T, k, E, g.counts, g.offsets, g.perm,
+               g.uniq, g.n_uniq);
+    return hipGetLastError();
+  }
   MOE_LAUNCH(MOE_KERNEL_GROUP, k_group_mask, dim3(C), dim3(256), 0, s, idx, T, k, E, g.mask);
   MOE_LAUNCH(MOE_KERNEL_GROUP, k_group_scan, dim3(1), dim3(1024), 0, s, g.mask, C, E, g.base, g.counts, g.offsets, g.uniq,
                      g.n_uniq);

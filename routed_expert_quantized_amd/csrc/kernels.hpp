@@ -25,6 +25,8 @@ bool timer_take(int kid, hipEvent_t* start, hipEvent_t* stop);
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
 constexpr int kMfmaLogitsMinT = 16;  // from this many tokens the router logits run on the matrix cores
+constexpr int kMaxLogitSplits = 8;   // split-K partial planes of the batch router, at most
+constexpr int kGroupLdsCells = 8192; // chunk x expert cells of the one-workgroup grouping (96 KiB of LDS)
 
 
 // Device buffers of the token-by-expert grouping.
@@ -52,7 +54,7 @@ struct ExpertsDev {
 inline int logits_max_splits(int64_t T, int64_t E) {
   if (T < kMfmaLogitsMinT) return 1;
   int64_t s = (1 << 20) / (T * E);
-  return (int)(s < 1 ? 1 : s > 8 ? 8 : s);
+  return (int)(s < 1 ? 1 : s > kMaxLogitSplits ? kMaxLogitSplits : s);
 }
 // Writes *nsplit partial planes logits[s][T][E] (one for T < kMfmaLogitsMinT).
 hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R, int E, float* logits,
@@ -70,6 +72,9 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
                             const float* logits, const int32_t* idx_in, const float* gate_in,
                             int32_t* idx_ws, float* gate_ws, int32_t* idx_user, float* gate_user,
                             float* h, float* y, hipStream_t s);
+
+// Plain streaming read of `bytes` bytes (benchmark reference).
+hipError_t launch_stream_read(const void* buf, int64_t bytes, hipStream_t s);
 
 // Grouped decode for T > 1 (after launch_group): h[T*k][I], ys[T*k][H], y.
 hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsDev& ex, int k,

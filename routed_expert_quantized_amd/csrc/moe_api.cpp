@@ -311,6 +311,13 @@ moe_status moe_quantize(const float* w, int64_t rows, int32_t K, int32_t scheme,
                     "quantize");
 }
 
+moe_status moe_stream_read(const void* buf, int64_t bytes, void* stream) {
+  if (!buf || !aligned(buf, 16)) return fail(MOE_ERR_INVALID_ARG, "buf is NULL or not 16-byte aligned");
+  if (bytes <= 0 || bytes % 16 || bytes > ((int64_t)1 << 40))
+    return fail(MOE_ERR_INVALID_ARG, "bytes=%lld: must be a positive multiple of 16, at most 2^40", (long long)bytes);
+  return hip_status(moe::launch_stream_read(buf, bytes, static_cast<hipStream_t>(stream)), "stream read");
+}
+
 const char* moe_status_str(moe_status s) {
   switch (s) {
     case MOE_OK: return "ok";

@@ -30,6 +30,13 @@ def test_exports_every_declared_function(L):
         assert hasattr(L, name), name
 
 
+def test_stream_read_validation(L):
+    assert L.moe_stream_read(None, 1024, None) == rq.MOE_ERR_INVALID_ARG
+    assert L.moe_stream_read(FAKE, 0, None) == rq.MOE_ERR_INVALID_ARG
+    assert L.moe_stream_read(FAKE, 1000, None) == rq.MOE_ERR_INVALID_ARG
+    assert L.moe_stream_read(ctypes.c_void_p(FAKE.value + 8), 1024, None) == rq.MOE_ERR_INVALID_ARG
+
+
 def test_status_strings(L):
     for s in range(5):
         assert L.moe_status_str(s)

@@ -98,7 +98,9 @@ def test_route_exact_ties_go_to_lower_ids(E, k):
 
 # ---------------------------------------------------------------- grouping
 @pytest.mark.parametrize("T,k,E", [(1, 8, 256), (63, 10, 512), (64, 10, 512), (65, 3, 8), (16, 10, 512),
-                                   (2048, 8, 256), (300, 16, 1024), (5, 4, 4)])
+                                   (2048, 8, 256), (300, 16, 1024), (5, 4, 4),
+                                   # chunk masks beyond the one-workgroup form's LDS: three kernels
+                                   (2048, 4, 1024), (520, 2, 1024)])
 def test_group_bit_exact(T, k, E):
     g = np.random.default_rng(T * 31 + k)
     idx = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
@@ -217,3 +219,11 @@ def test_single_token_paths_agree_with_oracle(name):
             assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
             assert rel_norm_err(y.cpu().numpy(), ref) <= Y_REL_NORM
             outs.append(y.cpu().numpy())
+
+
+def test_stream_read_runs_on_ragged_sizes():
+    """The bandwidth reference reads whole buffers and ragged tails without error."""
+    buf = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    for n in (16, 1040, 4096 * 16 + 48, 1 << 20):
+        rq.moe_stream_read(buf, n)
+    torch.cuda.synchronize()
