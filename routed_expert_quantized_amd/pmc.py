@@ -3,6 +3,9 @@
     python -m routed_expert_quantized_amd.pmc reduce <counter_collection.csv> [...]
         prints one JSON object: {kernel: {counter: mean value per dispatch, "dispatches": n}}
 
+    python -m routed_expert_quantized_amd.pmc stats <kernel_stats.csv>
+        prints a markdown table of per-kernel calls and average/min/max durations
+
     python -m routed_expert_quantized_amd.pmc traffic --fetch F.json --write W.json
         --kernel NAME_SUBSTRING --calib NAME_SUBSTRING --calib-bytes B [--sha S]
         converts the kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into bytes
@@ -21,7 +24,7 @@ from collections import defaultdict
 
 
 def _short(name: str) -> str:
-    name = name.strip()
+    name = name.strip().replace("(anonymous namespace)", "{anon}")
     if name.startswith("void "):
         name = name[5:]
     # drop the argument list, keep template arguments
@@ -81,7 +84,27 @@ def traffic(fetch, write, kernel, calib, calib_bytes, sha=None):
     return res
 
 
+def stats_table(path, top=12):
+    """Markdown table of a rocprofv3 kernel_stats.csv: calls and per-launch
+    average / min / max in microseconds, longest total time first."""
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append((_short(r["Name"]), int(r["Calls"]), float(r["TotalDurationNs"]),
+                         float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"])))
+    rows.sort(key=lambda r: -r[2])
+    out = ["| kernel | calls | avg (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for name, calls, _, avg, mn, mx in rows[:top]:
+        if not name.startswith("moe::") and "<" in name:
+            name = name[:name.index("<")] + "<…>"  # library kernels other than this one: base name only
+        out.append(f"| `{name}` | {calls} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} |")
+    return "\n".join(out)
+
+
 def main(argv):
+    if len(argv) >= 2 and argv[0] == "stats":
+        print(stats_table(argv[1]))
+        return 0
     if len(argv) >= 2 and argv[0] == "reduce":
         print(json.dumps(reduce(argv[1:]), indent=1))
         return 0
