@@ -377,12 +377,14 @@ __device__ __forceinline__ void wave_topk_sorted(const float* logits, int E, int
     key[j] = e < E ? logit_key(v[j]) : 0u;
     id[j] = e;
   }
-  // insertion network; (key, id) pairs compared lexicographically
+  // Insertion network, larger key first. A lane's ids grow with j, and an entry
+  // only moves past strictly smaller keys, so equal keys keep the lower id
+  // first without comparing ids.
 #pragma unroll
   for (int a = 1; a < VPL; ++a)
 #pragma unroll
     for (int b = a; b > 0; --b) {
-      const bool sw = key[b] > key[b - 1] || (key[b] == key[b - 1] && id[b] < id[b - 1]);
+      const bool sw = key[b] > key[b - 1];
       const uint32_t k0 = key[b - 1], k1 = key[b];
       const int i0 = id[b - 1], i1 = id[b];
       key[b - 1] = sw ? k1 : k0; key[b] = sw ? k0 : k1;
@@ -391,21 +393,30 @@ __device__ __forceinline__ void wave_topk_sorted(const float* logits, int E, int
   my_idx = -1;
   my_gate = 0.0f;
   uint32_t my_key = 0, kmax = 0;
+  // The sorted entries stay in place: `head` counts the lane's entries already
+  // taken, and each round reads the new head with one compare and two selects
+  // per entry. (Shifting the arrays on every pop is turned by the compiler into
+  // selects over every position, several times the work.) An exhausted lane
+  // offers key 0, below every logit.
+  int head = 0;
+  uint32_t hk = key[0];
+  int hid = id[0];
   for (int s = 0; s < rounds; ++s) {
-    const uint32_t m = wave_max_u32(key[0]);
-    const uint64_t tie = __ballot(key[0] == m);
+    const uint32_t m = wave_max_u32(hk);
+    const uint64_t tie = __ballot(hk == m);
     int win;
-    if (__popcll(tie) == 1) win = __builtin_amdgcn_readlane(id[0], (int)__builtin_ctzll(tie));
-    else win = wave_min_i(key[0] == m ? id[0] : 0x7FFFFFFF);
+    if (__popcll(tie) == 1) win = __builtin_amdgcn_readlane(hid, (int)__builtin_ctzll(tie));
+    else win = wave_min_i(hk == m ? hid : 0x7FFFFFFF);
     if (s == 0) kmax = m;
     if (lane == s) { my_idx = win; my_key = m; }
-    const bool pop = id[0] == win;
+    head += hid == win ? 1 : 0;
+    hk = 0u;
+    hid = 0x7FFFFFFF;
 #pragma unroll
-    for (int j = 0; j + 1 < VPL; ++j) {
-      key[j] = pop ? key[j + 1] : key[j];
-      id[j] = pop ? id[j + 1] : id[j];
+    for (int j = 0; j < VPL; ++j) {
+      hk = head == j ? key[j] : hk;
+      hid = head == j ? id[j] : hid;
     }
-    key[VPL - 1] = pop ? 0u : key[VPL - 1];
   }
   if (!with_gates) return;
   const float lmax = key_logit(kmax);
@@ -429,7 +440,7 @@ template <int VPL>
 __device__ __forceinline__ void wave_topk(const float* logits, int E, int k, bool renorm, int& my_idx,
                                           float& my_gate, int rounds = -1) {
   if (rounds < 0) rounds = k;
-  if constexpr (VPL <= 4) wave_topk_sorted<VPL>(logits, E, k, renorm, my_idx, my_gate, rounds, rounds == k);
+  if constexpr (VPL <= 8) wave_topk_sorted<VPL>(logits, E, k, renorm, my_idx, my_gate, rounds, rounds == k);
   else wave_topk_scan<VPL>(logits, E, k, renorm, my_idx, my_gate);
 }
 

@@ -488,6 +488,7 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
         };
         if (!from_logits) with_h(IC<0>{}, IC<1>{});
         else if (ex.E <= 256) with_h(IC<1>{}, IC<4>{});
+        else if (ex.E <= 512) with_h(IC<1>{}, IC<8>{});
         else with_h(IC<1>{}, IC<16>{});
       };
       if (nbj <= 1) go(IC<1>{}, IC<1>{});

@@ -219,6 +219,8 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
 // (ceil(T/64) * E <= kGroupLdsCells): the bitmasks and per-chunk bases live in
 // LDS, so the three steps need no round trips through memory and one launch.
 // Outputs are identical to the three-kernel form.
+constexpr int kGroupBatch = 16;
+
 __global__ __launch_bounds__(1024) void k_group_fused(const int32_t* __restrict__ idx, int T, int k, int E,
                                                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ perm, int32_t* __restrict__ uniq,
@@ -230,9 +232,23 @@ __global__ __launch_bounds__(1024) void k_group_fused(const int32_t* __restrict_
   const int C = (T + 63) / 64, cells = C * E, n = T * k;
   for (int i = tid; i < cells; i += 1024) m[i] = 0ull;
   __syncthreads();
-  for (int f = tid; f < n; f += 1024) {
-    const int t = f / k;
-    atomicOr(&m[(t >> 6) * E + idx[f]], 1ull << (t & 63));
+  // assignments go kGroupBatch per thread at a time: their expert ids are all
+  // requested before the first is used
+  for (int f0 = 0; f0 < n; f0 += 1024 * kGroupBatch) {
+    int ev[kGroupBatch];
+#pragma unroll
+    for (int j = 0; j < kGroupBatch; ++j) {
+      const int f = f0 + 1024 * j + tid;
+      ev[j] = f < n ? idx[f] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kGroupBatch; ++j) {
+      const int f = f0 + 1024 * j + tid;
+      if (f < n) {
+        const int t = f / k;
+        atomicOr(&m[(t >> 6) * E + ev[j]], 1ull << (t & 63));
+      }
+    }
   }
   __syncthreads();
   const int e = tid;
@@ -256,10 +272,22 @@ __global__ __launch_bounds__(1024) void k_group_fused(const int32_t* __restrict_
   if (e < E && cnt > 0) uniq[pos] = e;
   if (e == 0) *n_uniq = nu;
   __syncthreads();  // every expert's bases are in LDS
-  for (int f = tid; f < n; f += 1024) {
-    const int t = f / k, cell = (t >> 6) * E + idx[f], bit = t & 63;
-    const unsigned long long below = bit ? (m[cell] & ((1ull << bit) - 1ull)) : 0ull;
-    perm[base[cell] + __popcll(below)] = f;
+  for (int f0 = 0; f0 < n; f0 += 1024 * kGroupBatch) {
+    int ev[kGroupBatch];
+#pragma unroll
+    for (int j = 0; j < kGroupBatch; ++j) {
+      const int f = f0 + 1024 * j + tid;
+      ev[j] = f < n ? idx[f] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kGroupBatch; ++j) {
+      const int f = f0 + 1024 * j + tid;
+      if (f < n) {
+        const int t = f / k, cell = (t >> 6) * E + ev[j], bit = t & 63;
+        const unsigned long long below = bit ? (m[cell] & ((1ull << bit) - 1ull)) : 0ull;
+        perm[base[cell] + __popcll(below)] = f;
+      }
+    }
   }
 }
 

@@ -77,7 +77,7 @@ def test_route_many_experts_and_max_k():
         assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
 
 
-@pytest.mark.parametrize("E,k", [(16, 4), (256, 8), (64, 16), (1000, 10)])
+@pytest.mark.parametrize("E,k", [(16, 4), (256, 8), (64, 16), (512, 10), (1000, 10)])
 def test_route_exact_ties_go_to_lower_ids(E, k):
     g = np.random.default_rng(E + k)
     R = (g.standard_normal((E, 64)) * 0.3).astype(np.float32)
@@ -227,3 +227,30 @@ def test_stream_read_runs_on_ragged_sizes():
     for n in (16, 1040, 4096 * 16 + 48, 1 << 20):
         rq.moe_stream_read(buf, n)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("E,k", [(256, 8), (512, 10), (1000, 10)])
+def test_single_token_layer_exact_ties(E, k):
+    """One token through the fused single-token path (top-k inside the gate/up
+    kernel): exact logit ties go to the lower expert id, as in the oracle."""
+    H, I = 128, 64
+    g = np.random.default_rng(E * 7 + k)
+    R = (g.standard_normal((E, H)) * 0.3).astype(np.float32)
+    wgu = torch.from_numpy((g.standard_normal((E, 2 * I, H)) * 0.02).astype(np.float32)).cuda()
+    wd = torch.from_numpy((g.standard_normal((E, H, I)) * 0.02).astype(np.float32)).cuda()
+    ex = rq.quantize_experts(wgu, wd, rq.MOE_Q_SYM8)
+    # zero activations: every logit is 0, so ids 0..k-1 win with equal gates and y = 0
+    y, idx, gate = rq.moe_layer_forward(torch.zeros((1, H), device="cuda"), torch.from_numpy(R).cuda(), ex, k)
+    assert (idx.cpu().numpy() == np.arange(k)).all()
+    assert np.allclose(gate.cpu().numpy(), 1.0 / k, atol=GATE_ATOL)
+    assert not y.abs().max().item()
+    # duplicated router rows: each copy ties with its original, the lower id first
+    x = g.standard_normal((1, H)).astype(np.float32)
+    R2 = R.copy()
+    ridx0, _ = oracle.route(x, R, k)
+    for j, e in enumerate(ridx0[0][:3]):
+        R2[E - 1 - j] = R2[e]
+    ridx, rgate = oracle.route(x, R2, k)
+    _, gi, gg = rq.moe_layer_forward(torch.from_numpy(x).cuda(), torch.from_numpy(R2).cuda(), ex, k)
+    assert np.array_equal(gi.cpu().numpy(), ridx)
+    assert np.abs(gg.cpu().numpy() - rgate).max() <= GATE_ATOL
