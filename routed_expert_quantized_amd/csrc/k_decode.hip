@@ -59,10 +59,23 @@ __global__ __launch_bounds__(256) void k_gate_up_t1(const void* __restrict__ x, 
   // Every load below is unconditional (block and row indices are clamped in
   // bounds, surplus lanes get a zero scale) so the scheduler can issue them all
   // before the arithmetic.
-  // activations do not depend on the routing: load them first
+  // Activations do not depend on the routing: they are requested first. fp16
+  // activations with the routing step come through LDS, one 16-byte piece per
+  // thread, behind the barrier that shares the routing (one read of x per
+  // workgroup instead of one per wave); otherwise each wave loads its blocks.
+  constexpr bool kStageX = XT == MOE_F16 && FROM_LOGITS;
+  __shared__ uint4 xs[kStageX ? NBJ * 256 : 1];
   XReg<SCHEME, XT> xr[NBJ];
+  if constexpr (kStageX) {
 #pragma unroll
-  for (int j = 0; j < NBJ; ++j) load_xreg<SCHEME, XT>(xr[j], x, 0, min(lane + 64 * j, NB - 1));
+    for (int j = 0; j < NBJ; ++j) {
+      const int i = (int)threadIdx.x + 256 * j;
+      if (i < H / 8) xs[i] = reinterpret_cast<const uint4*>(x)[i];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NBJ; ++j) load_xreg<SCHEME, XT>(xr[j], x, 0, min(lane + 64 * j, NB - 1));
+  }
   __builtin_amdgcn_sched_barrier(0);
   int e;
   if constexpr (FROM_LOGITS) {
@@ -104,6 +117,19 @@ __global__ __launch_bounds__(256) void k_gate_up_t1(const void* __restrict__ x, 
       cu[r][j] = load_block<SCHEME>(ex.wgu + urow * rb, b);
       sg[r][j] = f16_bits_to_f32(ex.sgu[grow * NB + b]);
       su[r][j] = f16_bits_to_f32(ex.sgu[urow * NB + b]);
+    }
+  }
+  if constexpr (kStageX) {
+#pragma unroll
+    for (int j = 0; j < NBJ; ++j) {
+      const int b = min(lane + 64 * j, NB - 1);
+      uint32_t nat[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = xs[4 * b + i];
+        nat[4 * i] = v.x; nat[4 * i + 1] = v.y; nat[4 * i + 2] = v.z; nat[4 * i + 3] = v.w;
+      }
+      xr[j].h = xblock_from_pairs<SCHEME>(nat);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
