@@ -38,6 +38,9 @@ static void with_xtype(int xt, F&& f) {
 
 
 // ------------------------------------------------------------------ T = 1
+// Waves per workgroup of the single-token gate/up kernel (each owns one row pair).
+constexpr int kGateUpWaves = 4;
+
 // Grid: k slots x blocks_per_slot. A wave computes RP (gate row n, up row I+n)
 // pairs of its slot's expert and writes h[slot][n] = silu(gate) * up.
 // With FROM_LOGITS wave 0 of each workgroup first picks the top k from the
@@ -47,7 +50,7 @@ static void with_xtype(int xt, F&& f) {
 // With H16 the activation is stored as fp16 (round to nearest even) for the
 // slot-parallel down kernel, else as fp32.
 template <int SCHEME, int XT, int NBJ, int RP, bool FROM_LOGITS, int VPL, bool H16>
-__global__ __launch_bounds__(256) void k_gate_up_t1(const void* __restrict__ x, ExpertsDev ex, int k, int renorm,
+__global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1(const void* __restrict__ x, ExpertsDev ex, int k, int renorm,
                                                     const float* __restrict__ logits,
                                                     const int32_t* __restrict__ idx_in,
                                                     int32_t* __restrict__ idx_ws, float* __restrict__ gate_ws,
@@ -64,12 +67,13 @@ __global__ __launch_bounds__(256) void k_gate_up_t1(const void* __restrict__ x, 
   // thread, behind the barrier that shares the routing (one read of x per
   // workgroup instead of one per wave); otherwise each wave loads its blocks.
   constexpr bool kStageX = XT == MOE_F16 && FROM_LOGITS;
+  constexpr int kThreads = 64 * kGateUpWaves;
   __shared__ uint4 xs[kStageX ? NBJ * 256 : 1];
   XReg<SCHEME, XT> xr[NBJ];
   if constexpr (kStageX) {
 #pragma unroll
-    for (int j = 0; j < NBJ; ++j) {
-      const int i = (int)threadIdx.x + 256 * j;
+    for (int j = 0; j < (NBJ * 256 + kThreads - 1) / kThreads; ++j) {
+      const int i = (int)threadIdx.x + kThreads * j;
       if (i < H / 8) xs[i] = reinterpret_cast<const uint4*>(x)[i];
     }
   } else {
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(256) void k_gate_up_t1(const void* __restrict__ x, 
   } else {
     e = idx_in[slot];
   }
-  const int n0 = (blk * 4 + wave) * RP;
+  const int n0 = (blk * kGateUpWaves + wave) * RP;
   const int64_t rb = row_bytes<SCHEME>(H);
   Block<SCHEME> cg[RP][NBJ], cu[RP][NBJ];
   float sg[RP][NBJ], su[RP][NBJ];
@@ -500,12 +504,12 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
       constexpr int SC = decltype(S)::value, XT = decltype(X)::value;
       auto go = [&](auto NBJc, auto RPc) {
         constexpr int NBJ = decltype(NBJc)::value, RP = decltype(RPc)::value;
-        const int bps = (ex.I + 4 * RP - 1) / (4 * RP);
+        const int bps = (ex.I + kGateUpWaves * RP - 1) / (kGateUpWaves * RP);
         dim3 grid(k * bps);
         auto launch = [&](auto FLc, auto VPLc, auto H16c) {
           constexpr bool FL = decltype(FLc)::value != 0, H16 = decltype(H16c)::value != 0;
           constexpr int VPL = decltype(VPLc)::value;
-          MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_t1<SC, XT, NBJ, RP, FL, VPL, H16>), grid, dim3(256), 0, s, x, ex,
+          MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_t1<SC, XT, NBJ, RP, FL, VPL, H16>), grid, dim3(64 * kGateUpWaves), 0, s, x, ex,
                      k, renorm, logits, idx_in, idx_ws, gate_ws, idx_user, gate_user, h, bps);
         };
         auto with_h = [&](auto FLc, auto VPLc) {
