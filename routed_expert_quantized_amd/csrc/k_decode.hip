@@ -455,12 +455,14 @@ __global__ __launch_bounds__(256) void k_down_grouped(ExpertsDev ex, int k, cons
   }
 }
 
-// y[t][m] = sum over slots s, in order, of gate[t][s] * ys[t*k+s][m].
+// y[t][m] = sum over slots s, in order, of gate[t][s] * ys[t*k+s][m], with the
+// per-slot rows in fp32 (ys) or, with HALF, fp16 (ys16: the grouped GEMM's).
 // Four consecutive outputs of one token per thread; every slot's loads are
 // issued before the fused multiply-adds, which run in slot order (KMAX >= k).
-template <int KMAX>
+template <int KMAX, bool HALF>
 __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const float* __restrict__ gate,
-                                                 const float* __restrict__ ys, float* __restrict__ y) {
+                                                 const float* __restrict__ ys, const uint16_t* __restrict__ ys16,
+                                                 float* __restrict__ y) {
   const int nbx = (H / 4 + 255) / 256;
   const int t = blockIdx.x / nbx;
   const int m = ((blockIdx.x % nbx) * 256 + threadIdx.x) * 4;
@@ -470,7 +472,14 @@ __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const floa
 #pragma unroll
   for (int s = 0; s < KMAX; ++s) {
     const int sc = min(s, k - 1);
-    v[s] = *reinterpret_cast<const float4*>(ys + ((int64_t)t * k + sc) * H + m);
+    const int64_t off = ((int64_t)t * k + sc) * H + m;
+    if constexpr (HALF) {
+      const uint2 u = *reinterpret_cast<const uint2*>(ys16 + off);
+      const half2v lo = as_h2(u.x), hi = as_h2(u.y);
+      v[s] = make_float4((float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]);
+    } else {
+      v[s] = *reinterpret_cast<const float4*>(ys + off);
+    }
     g[s] = gate[(int64_t)t * k + sc];
   }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -593,14 +602,25 @@ hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsD
     else if (nbi <= 4) go(IC<4>{});
     else go(IC<8>{});
   });
-  if (gate) return launch_combine(T, ex.H, k, gate, ys, y, s);
+  if (gate) return launch_combine(T, ex.H, k, gate, ys, nullptr, y, s);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(int T, int H, int k, const float* gate, const float* ys, float* y, hipStream_t s) {
+hipError_t launch_combine(int T, int H, int k, const float* gate, const float* ys, const uint16_t* ys16, float* y,
+                          hipStream_t s) {
   const dim3 cg((unsigned)((int64_t)T * ((H / 4 + 255) / 256)));
-  if (k <= 8) MOE_LAUNCH(MOE_KERNEL_COMBINE, k_combine<8>, cg, dim3(256), 0, s, T, H, k, gate, ys, y);
-  else MOE_LAUNCH(MOE_KERNEL_COMBINE, k_combine<16>, cg, dim3(256), 0, s, T, H, k, gate, ys, y);
+  auto go = [&](auto KM, auto HF) {
+    constexpr int K_ = decltype(KM)::value;
+    constexpr bool H_ = decltype(HF)::value != 0;
+    MOE_LAUNCH(MOE_KERNEL_COMBINE, (k_combine<K_, H_>), cg, dim3(256), 0, s, T, H, k, gate, ys, ys16, y);
+  };
+  if (ys16) {
+    if (k <= 8) go(IC<8>{}, IC<1>{});
+    else go(IC<16>{}, IC<1>{});
+  } else {
+    if (k <= 8) go(IC<8>{}, IC<0>{});
+    else go(IC<16>{}, IC<0>{});
+  }
   return hipGetLastError();
 }
 

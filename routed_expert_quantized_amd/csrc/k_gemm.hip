@@ -3,7 +3,8 @@
 // After the token-by-expert grouping each routed expert e has n_e assignments.
 // GEMM1: U_e[n_e][2I] = X_e[n_e][H] . W_gu[e]^T, then h = silu(gate) * up
 //        (gate columns n and up columns I + n in the same workgroup), stored fp16.
-// GEMM2: Y_e[n_e][H] = h_e[n_e][I] . W_d[e]^T, stored fp32 per assignment (ys).
+// GEMM2: Y_e[n_e][H] = h_e[n_e][I] . W_d[e]^T, stored per assignment (ys): fp16
+//        (round to nearest even) ahead of the combine, fp32 when it is the output.
 // Each expert's weights are read once per pass over its assignments
 // ("鳴かぬなら、カスタムカーネル、ほととぎす", section 4: only routed experts are read;
 // section 7: each slot's down projection takes that slot's own activation).
@@ -119,7 +120,7 @@ __device__ __forceinline__ uint4 load8_f16(const uint8_t* row, int i) {
 // MODE 0 (gate/up): wave w owns gate rows n0+16w.. and up rows I+n0+16w.., a
 //   workgroup owns 64 gate/up pairs; output h16[f][n] = fp16(silu(g) * u).
 // MODE 1 (down): wave w owns rows n0+32w .. n0+32w+31 of W_d[e]; a workgroup
-//   owns 128 rows; output ys[f][n] (fp32).
+//   owns 128 rows; output ys16[f][n] (fp16) when ys16 is set, else ys[f][n] (fp32).
 // The expert's assignments are taken 16*MT at a time (one pass each).
 template <int SCHEME, int XT, int MODE, int MT>
 __global__ __launch_bounds__(256) void k_gemm_grouped(const void* __restrict__ act, ExpertsDev ex, int k,
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(256) void k_gemm_grouped(const void* __restrict__ a
                                                       const int32_t* __restrict__ counts,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ perm, uint16_t* __restrict__ h16,
-                                                      float* __restrict__ ys) {
+                                                      float* __restrict__ ys, uint16_t* __restrict__ ys16) {
   constexpr int BPG = gemm_bpg<SCHEME>(), KC = gemm_kc<SCHEME>(), AROW = gemm_arow<SCHEME>();
   constexpr int NJ = KC / 32;  // MFMAs per chunk per output tile
   __shared__ __attribute__((aligned(16))) uint8_t As[16 * MT * AROW];
@@ -267,7 +268,10 @@ __global__ __launch_bounds__(256) void k_gemm_grouped(const void* __restrict__ a
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const int n = col[c] + r16;
-            if (n < lim) ys[(int64_t)f * H + n] = acc[mt][c][i];
+            if (n < lim) {
+              if (ys16) ys16[(int64_t)f * H + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[mt][c][i]);
+              else ys[(int64_t)f * H + n] = acc[mt][c][i];
+            }
           }
         }
       }
@@ -443,7 +447,7 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k,
                                                   const int32_t* __restrict__ counts,
                                                   const int32_t* __restrict__ offsets,
                                                   const int32_t* __restrict__ perm, uint16_t* __restrict__ h16,
-                                                  float* __restrict__ ys, int ncb) {
+                                                  float* __restrict__ ys, uint16_t* __restrict__ ys16, int ncb) {
   using D = DmaTile<SCHEME, MT, LB>;
   static_assert((NS - 2) * D::NI < 64, "in-flight loads exceed vmcnt");
   // One LDS array per stage, always addressed with a compile-time stage index.
@@ -661,7 +665,10 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k,
   #pragma unroll
             for (int c = 0; c < 2; ++c) {
               const int n = n0 + wave * 32 + 16 * c + r16;
-              if (n < lim) ys[(int64_t)f * H + n] = acc[mt][c][i];
+              if (n < lim) {
+                if (ys16) ys16[(int64_t)f * H + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[mt][c][i]);
+                else ys[(int64_t)f * H + n] = acc[mt][c][i];
+              }
             }
           }
         }
@@ -694,27 +701,30 @@ static int resident_workgroups(K kernel) {
 
 template <int SCHEME, int MODE, int MT, int NS, int LB>
 static void launch_dma(int ncb, int maxu8, const uint16_t* act, const ExpertsDev& ex, int k, const GroupBufs& g,
-                       uint16_t* h16, float* ys, hipStream_t s) {
+                       uint16_t* h16, float* ys, uint16_t* ys16, hipStream_t s) {
   auto kernel = k_gemm_dma<SCHEME, MODE, MT, NS, LB>;
   static const int resident = resident_workgroups(kernel);  // per kernel, first call
   const int grid = std::min(resident, ncb * maxu8);
   MOE_LAUNCH(MODE == 0 ? MOE_KERNEL_GEMM_GATE_UP : MOE_KERNEL_GEMM_DOWN, kernel, dim3(grid), dim3(256), 0, s, act,
-             ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h16, ys, ncb);
+             ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h16, ys, ys16, ncb);
 }
 
 // gate/up then down with one tuning (M tiles per pass, stages, line bytes per stage)
 template <int SCHEME, int MT, int NS, int LB>
 static void launch_dma_pair(int maxu8, const uint16_t* act, const ExpertsDev& ex, int k, const GroupBufs& g,
-                            uint16_t* h16, float* ys, float* out, hipStream_t s) {
-  launch_dma<SCHEME, 0, MT, NS, LB>((ex.I + 63) / 64, maxu8, act, ex, k, g, h16, ys, s);
-  launch_dma<SCHEME, 1, MT, NS, LB>((ex.H + 127) / 128, maxu8, h16, ex, k, g, h16, out, s);
+                            uint16_t* h16, float* out, uint16_t* out16, hipStream_t s) {
+  launch_dma<SCHEME, 0, MT, NS, LB>((ex.I + 63) / 64, maxu8, act, ex, k, g, h16, nullptr, nullptr, s);
+  launch_dma<SCHEME, 1, MT, NS, LB>((ex.H + 127) / 128, maxu8, h16, ex, k, g, h16, out, out16, s);
 }
 
 hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev& ex, int k, const GroupBufs& g,
                                const float* gate, uint16_t* h16, uint16_t* x16, float* ys, float* y, hipStream_t s) {
   const int maxu = (int)std::min<int64_t>((int64_t)ex.E, (int64_t)T * k);
   const double avg = (double)T * k / ex.E;
-  float* out = gate ? ys : y;
+  // down output: fp16 per-slot rows ahead of the combine, or the caller's
+  // fp32 per-slot output when no gates are given
+  float* out = gate ? nullptr : y;
+  uint16_t* out16 = gate ? reinterpret_cast<uint16_t*>(ys) : nullptr;
   if (ex.H % 64 == 0 && ex.I % 64 == 0) {
     // activations as fp16 rows
     const uint16_t* act = static_cast<const uint16_t*>(x);
@@ -734,16 +744,16 @@ hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev
     // stages (taller passes measured no faster at ~256 assignments per expert).
     // int4 four-tile passes use half lines (whole lines exceed the registers).
     if (ex.scheme == MOE_Q_SYM8) {
-      if (avg > 24) launch_dma_pair<MOE_Q_SYM8, 6, 3, 64>(maxu8, act, ex, k, g, h16, ys, out, s);
-      else if (avg > 6) launch_dma_pair<MOE_Q_SYM8, 4, 2, 128>(maxu8, act, ex, k, g, h16, ys, out, s);
-      else launch_dma_pair<MOE_Q_SYM8, 1, 2, 128>(maxu8, act, ex, k, g, h16, ys, out, s);
+      if (avg > 24) launch_dma_pair<MOE_Q_SYM8, 6, 3, 64>(maxu8, act, ex, k, g, h16, out, out16, s);
+      else if (avg > 6) launch_dma_pair<MOE_Q_SYM8, 4, 2, 128>(maxu8, act, ex, k, g, h16, out, out16, s);
+      else launch_dma_pair<MOE_Q_SYM8, 1, 2, 128>(maxu8, act, ex, k, g, h16, out, out16, s);
     } else {
-      if (avg > 6) launch_dma_pair<MOE_Q_INT4, 4, 2, 64>(maxu8, act, ex, k, g, h16, ys, out, s);
-      else launch_dma_pair<MOE_Q_INT4, 1, 2, 128>(maxu8, act, ex, k, g, h16, ys, out, s);
+      if (avg > 6) launch_dma_pair<MOE_Q_INT4, 4, 2, 64>(maxu8, act, ex, k, g, h16, out, out16, s);
+      else launch_dma_pair<MOE_Q_INT4, 1, 2, 128>(maxu8, act, ex, k, g, h16, out, out16, s);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (gate) return launch_combine(T, ex.H, k, gate, ys, y, s);
+    if (gate) return launch_combine(T, ex.H, k, gate, nullptr, out16, y, s);
     return hipGetLastError();
   }
   // rows with an odd number of 32-element blocks: register-staged kernel
@@ -751,9 +761,10 @@ hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev
     constexpr int S_ = decltype(SC)::value, X_ = decltype(XC)::value, MT_ = decltype(MTc)::value;
     dim3 g1((ex.I + 63) / 64, maxu), g2((ex.H + 127) / 128, maxu);
     MOE_LAUNCH(MOE_KERNEL_GEMM_GATE_UP, (k_gemm_grouped<S_, X_, 0, MT_>), g1, dim3(256), 0, s, x, ex, k, g.uniq,
-               g.n_uniq, g.counts, g.offsets, g.perm, h16, ys);
+               g.n_uniq, g.counts, g.offsets, g.perm, h16, static_cast<float*>(nullptr),
+               static_cast<uint16_t*>(nullptr));
     MOE_LAUNCH(MOE_KERNEL_GEMM_DOWN, (k_gemm_grouped<S_, MOE_F16, 1, MT_>), g2, dim3(256), 0, s,
-               (const void*)h16, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h16, out);
+               (const void*)h16, ex, k, g.uniq, g.n_uniq, g.counts, g.offsets, g.perm, h16, out, out16);
   };
   auto with_mt = [&](auto SC, auto XC) {
     if (avg > 24) run(SC, XC, ICg<8>{});
@@ -767,7 +778,7 @@ hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev
   };
   if (ex.scheme == MOE_Q_SYM8) with_x(ICg<MOE_Q_SYM8>{});
   else with_x(ICg<MOE_Q_INT4>{});
-  if (gate) return launch_combine(T, ex.H, k, gate, ys, y, s);
+  if (gate) return launch_combine(T, ex.H, k, gate, nullptr, out16, y, s);
   return hipGetLastError();
 }
 

@@ -82,7 +82,10 @@ hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsD
                                  hipStream_t s);
 
 // Gate-weighted combine y[t] = sum_s gate[t][s] * ys[t*k+s] (T > 1 paths).
-hipError_t launch_combine(int T, int H, int k, const float* gate, const float* ys, float* y, hipStream_t s);
+// y[t] = sum over slots s (in order) of gate[t][s] * ys[t][s], per-slot rows
+// fp32 (ys) or fp16 (ys16, when non-null).
+hipError_t launch_combine(int T, int H, int k, const float* gate, const float* ys, const uint16_t* ys16, float* y,
+                          hipStream_t s);
 
 // Grouped MFMA GEMM path (after launch_group): gate/up + SwiGLU into fp16 h,
 // down into ys (or y itself in per-slot mode), then the combine.
