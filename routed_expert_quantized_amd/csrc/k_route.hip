@@ -373,13 +373,122 @@ __global__ __launch_bounds__(1024) void k_logits_mfma(const void* __restrict__ x
   }
 }
 
+// Router logits for bf16 activations on the bf16 matrix cores, at fp32 product
+// accuracy. Each fp32 router weight is split exactly into three bf16 parts
+// (hi: the top 8 significand bits, mid: the next 8 of the remainder, lo: the
+// rest, at most 8 bits), so x * w = x * hi + x * mid + x * lo with every
+// product exact; the MFMA adds them in fp32 like the fp32 kernel. The split
+// runs once per call over the router (k_split_router), the products take three
+// v_mfma_f32_16x16x32_bf16 per 32 K values instead of eight 16x16x4 fp32 MFMAs.
+// Tiles, split-K planes and the output mapping are those of k_logits_mfma; lane
+// (r = l%16, g = l/16) holds A[r][8g..8g+7] (a token row) and B[8g..8g+7][r] (an
+// expert row), D[4g+i][r].
+__global__ __launch_bounds__(256) void k_split_router(const float* __restrict__ R, int64_t n4,
+                                                      uint16_t* __restrict__ r3, int64_t plane) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const float4 w = reinterpret_cast<const float4*>(R)[i];
+  const float wv[4] = {w.x, w.y, w.z, w.w};
+  uint16_t hi[4], mid[4], lo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t hb = __builtin_bit_cast(uint32_t, wv[j]) & 0xFFFF0000u;
+    const float r1 = wv[j] - __builtin_bit_cast(float, hb);  // exact: the low 16 significand bits
+    const uint32_t mb = __builtin_bit_cast(uint32_t, r1) & 0xFFFF0000u;
+    const float r2 = r1 - __builtin_bit_cast(float, mb);     // exact, at most 8 significant bits
+    hi[j] = (uint16_t)(hb >> 16);
+    mid[j] = (uint16_t)(mb >> 16);
+    lo[j] = (uint16_t)(__builtin_bit_cast(uint32_t, r2) >> 16);
+  }
+  auto pack = [](const uint16_t (&v)[4]) {
+    return make_uint2((uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16));
+  };
+  reinterpret_cast<uint2*>(r3)[i] = pack(hi);
+  reinterpret_cast<uint2*>(r3 + plane)[i] = pack(mid);
+  reinterpret_cast<uint2*>(r3 + 2 * plane)[i] = pack(lo);
+}
+
+typedef __bf16 bf16x8_r __attribute__((ext_vector_type(8)));
+
+template <int MTT, int NTT>
+__global__ __launch_bounds__(1024) void k_logits_bf16x3(const uint16_t* __restrict__ x, int T, int H,
+                                                        const uint16_t* __restrict__ r3, int E,
+                                                        float* __restrict__ logits, int kw) {
+  extern __shared__ float red[];  // [waves][MTT*NTT*4][64]
+  logits += (int64_t)blockIdx.z * T * E;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * 16 * MTT, e0 = blockIdx.y * 16 * NTT;
+  const int64_t plane = (int64_t)E * H;
+  int64_t xrow[MTT], rrow[NTT];
+#pragma unroll
+  for (int mt = 0; mt < MTT; ++mt) xrow[mt] = (int64_t)min(t0 + 16 * mt + r, T - 1) * H;
+#pragma unroll
+  for (int nt = 0; nt < NTT; ++nt) rrow[nt] = (int64_t)min(e0 + 16 * nt + r, E - 1) * H;
+  float4v_r acc[MTT][NTT];
+#pragma unroll
+  for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTT; ++nt) acc[mt][nt] = float4v_r{0.f, 0.f, 0.f, 0.f};
+  const int kb = (blockIdx.z * nw + w) * kw;
+#pragma unroll 2
+  for (int k = kb; k < kb + kw; k += 32) {
+    bf16x8_r a[MTT], b[3][NTT];
+#pragma unroll
+    for (int mt = 0; mt < MTT; ++mt) a[mt] = *reinterpret_cast<const bf16x8_r*>(x + xrow[mt] + k + 8 * g);
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int nt = 0; nt < NTT; ++nt)
+        b[p][nt] = *reinterpret_cast<const bf16x8_r*>(r3 + p * plane + rrow[nt] + k + 8 * g);
+#pragma unroll
+    for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTT; ++nt)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b[p][nt], acc[mt][nt], 0, 0, 0);
+  }
+  constexpr int NO = MTT * NTT * 4 * 64;
+  auto store = [&](int o, float v) {
+    const int l = o & 63, i = (o >> 6) & 3, tile = o >> 8;
+    const int mt = tile / NTT, nt = tile % NTT;
+    const int t = t0 + 16 * mt + 4 * (l >> 4) + i, e = e0 + 16 * nt + (l & 15);
+    if (t < T && e < E) logits[(int64_t)t * E + e] = v;
+  };
+  if (nw == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store(((mt * NTT + nt) * 4 + i) * 64 + lane, acc[mt][nt][i]);
+    return;
+  }
+#pragma unroll
+  for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[w * NO + ((mt * NTT + nt) * 4 + i) * 64 + lane] = acc[mt][nt][i];
+  __syncthreads();
+  for (int o = threadIdx.x; o < NO; o += blockDim.x) {
+    float v = 0.f;
+    for (int j = 0; j < nw; ++j) v += red[j * NO + o];  // waves in K order
+    store(o, v);
+  }
+}
+
 // Waves per expert row in the few-token router kernel.
 constexpr int kLogitsWaves = 4;
 
 hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R, int E, float* logits,
-                         int* nsplit, hipStream_t s) {
+                         int* nsplit, uint16_t* r3, hipStream_t s) {
   *nsplit = 1;
   if (T >= kMfmaLogitsMinT) {
+    // bf16 activations of a large batch: the split-weight bf16 kernel
+    const bool split3 = xtype == MOE_BF16 && r3 != nullptr && T >= kSplitRouterMinT;
+    const int kstep = split3 ? 32 : 16;
     // tile shape and split-K: aim for about two waves per SIMD (2048 waves)
     const int mtt = T >= 32 && (int64_t)((T + 31) / 32) * ((E + 31) / 32) >= 128 ? 2 : 1;
     const int ntt = E >= 32 && (int64_t)((T + 16 * mtt - 1) / (16 * mtt)) * ((E + 31) / 32) >= 128 ? 2 : 1;
@@ -388,17 +497,28 @@ hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R,
     // waves per workgroup (up to 4), then K splits across workgroups, while the
     // total stays within about 2048 waves and every wave keeps >= 64 of K
     int nw = 1, ns = 1;
-    auto fits = [&](int w, int sp) { return tiles * w * sp <= 2048 && H % (16 * w * sp) == 0 && H / (w * sp) >= 64; };
+    auto fits = [&](int w, int sp) {
+      return tiles * w * sp <= 2048 && H % (kstep * w * sp) == 0 && H / (w * sp) >= 64;
+    };
     while (nw < 4 && fits(nw * 2, ns)) nw *= 2;
     while (ns < logits_max_splits(T, E) && fits(nw, ns * 2)) ns *= 2;
     grid.z = ns;
     *nsplit = ns;
     const int kw = H / (nw * ns);
     const size_t lds = nw > 1 ? (size_t)nw * mtt * ntt * 256 * sizeof(float) : 0;
+    if (split3) {
+      const int64_t n4 = (int64_t)E * H / 4;
+      hipLaunchKernelGGL(k_split_router, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, R, n4, r3,
+                         (int64_t)E * H);
+    }
     auto go = [&](auto XC, auto MC, auto NC) {
       constexpr int X_ = decltype(XC)::value, M_ = decltype(MC)::value, N_ = decltype(NC)::value;
-      MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_mfma<X_, M_, N_>), grid, dim3(64 * nw), lds, s, x, T, H, R, E,
-                 logits, kw);
+      if (split3)
+        MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_bf16x3<M_, N_>), grid, dim3(64 * nw), lds, s,
+                   static_cast<const uint16_t*>(x), T, H, static_cast<const uint16_t*>(r3), E, logits, kw);
+      else
+        MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_mfma<X_, M_, N_>), grid, dim3(64 * nw), lds, s, x, T, H, R, E,
+                   logits, kw);
     };
     auto with_tile = [&](auto XC) {
       if (mtt == 2 && ntt == 2) go(XC, std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});

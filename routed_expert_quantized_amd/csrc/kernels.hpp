@@ -26,6 +26,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
 constexpr int kMfmaLogitsMinT = 16;  // from this many tokens the router logits run on the matrix cores
 constexpr int kMaxLogitSplits = 8;   // split-K partial planes of the batch router, at most
+constexpr int kSplitRouterMinT = 128;  // from this many bf16 tokens the router runs on bf16 MFMA (split weights)
 constexpr int kGroupLdsCells = 8192; // chunk x expert cells of the one-workgroup grouping (96 KiB of LDS)
 
 
@@ -57,8 +58,10 @@ inline int logits_max_splits(int64_t T, int64_t E) {
   return (int)(s < 1 ? 1 : s > kMaxLogitSplits ? kMaxLogitSplits : s);
 }
 // Writes *nsplit partial planes logits[s][T][E] (one for T < kMfmaLogitsMinT).
+// r3: scratch for the router split into three bf16 planes [3][E][H] (used for
+// bf16 activations from kSplitRouterMinT tokens; may be null below that).
 hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R, int E, float* logits,
-                         int* nsplit, hipStream_t s);
+                         int* nsplit, uint16_t* r3, hipStream_t s);
 hipError_t launch_topk(const float* logits, int nsplit, int T, int E, int k, int renorm, int32_t* idx, float* gate,
                        int32_t* idx2, float* gate2, hipStream_t s);
 hipError_t launch_group(const int32_t* idx, int T, int k, int E, const GroupBufs& g, hipStream_t s);

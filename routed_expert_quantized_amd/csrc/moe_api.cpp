@@ -39,7 +39,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 // Scratch regions inside the caller's workspace, each 256-byte aligned.
 struct Layout {
-  size_t logits, idx, gate, mask, base, counts, offsets, perm, uniq, n_uniq, h, ys, x16, total;
+  size_t logits, idx, gate, mask, base, counts, offsets, perm, uniq, n_uniq, h, ys, x16, r3, total;
 };
 
 Layout layout(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
@@ -64,6 +64,7 @@ Layout layout(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
   L.h = take(T * k * I * 4);
   L.ys = take(T * k * H * 4);
   L.x16 = take(T * H * 2);
+  L.r3 = take(T >= moe::kSplitRouterMinT ? 3 * E * H * 2 : 0);  // router split into bf16 planes
   L.total = off;
   return L;
 }
@@ -222,7 +223,8 @@ moe_status moe_route(const void* x, int32_t xtype, int32_t T, int32_t H, const f
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* logits = at<float>(ws, L.logits);
   int nsplit = 1;
-  hipError_t e = moe::launch_logits(x, xtype, T, H, router_w, E, logits, &nsplit, s);
+  hipError_t e = moe::launch_logits(x, xtype, T, H, router_w, E, logits, &nsplit,
+                                    T >= moe::kSplitRouterMinT ? at<uint16_t>(ws, L.r3) : nullptr, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
   return hip_status(moe::launch_topk(logits, nsplit, T, E, k, (flags & MOE_FLAG_RENORM) ? 1 : 0, topk_idx, topk_gate,
                                      nullptr, nullptr, s),
@@ -288,7 +290,8 @@ moe_status moe_layer_forward(const void* x, int32_t xtype, int32_t T, const floa
   int32_t* idx = at<int32_t>(ws, L.idx);
   float* gate = at<float>(ws, L.gate);
   int nsplit = 1;
-  hipError_t e = moe::launch_logits(x, xtype, T, d.H, router_w, d.E, logits, &nsplit, s);
+  hipError_t e = moe::launch_logits(x, xtype, T, d.H, router_w, d.E, logits, &nsplit,
+                                    T >= moe::kSplitRouterMinT ? at<uint16_t>(ws, L.r3) : nullptr, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
   if (T == 1 && !(flags & MOE_FLAG_PATH_GEMM))
     return hip_status(moe::launch_decode_t1(x, xtype, d, k, renorm, logits, nullptr, nullptr, idx, gate,

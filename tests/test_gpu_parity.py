@@ -47,8 +47,9 @@ def test_quantize_bit_exact(scheme):
 
 
 # ---------------------------------------------------------------- router
+# prefill at T >= 128 takes the split-weight bf16 router (T = 128 is the first such batch)
 ROUTE_CASES = [("tiny", None), ("decode40", None), ("batched_int4", None), ("large_int4", None),
-               ("prefill", None), ("prefill", 130), ("batched_int4", 3)]
+               ("prefill", None), ("prefill", 130), ("prefill", 128), ("prefill", 127), ("batched_int4", 3)]
 
 
 @pytest.mark.parametrize("name,T", ROUTE_CASES)
