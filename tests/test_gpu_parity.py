@@ -255,3 +255,37 @@ def test_single_token_layer_exact_ties(E, k):
     _, gi, gg = rq.moe_layer_forward(torch.from_numpy(x).cuda(), torch.from_numpy(R2).cuda(), ex, k)
     assert np.array_equal(gi.cpu().numpy(), ridx)
     assert np.abs(gg.cpu().numpy() - rgate).max() <= GATE_ATOL
+
+
+# one token through moe_layer_forward at edge shapes of the single-token kernels:
+# one expert; k = 16 (a 1024-thread down workgroup); H = 4096 (two 16-byte pieces of
+# x per thread through LDS); I = 1024 (two blocks per lane in the down kernel);
+# I = 2048 (the fp32-activation down kernel); E = 512 (eight logits per lane)
+T1_EDGE = [(1, 32, 32, 1), (16, 64, 32, 16), (64, 4096, 64, 8), (32, 256, 1024, 10), (512, 64, 32, 10),
+           (8, 256, 2048, 3), (300, 160, 96, 5)]
+
+
+@pytest.mark.parametrize("E,H,I,k", T1_EDGE)
+@pytest.mark.parametrize("scheme", [rq.MOE_Q_SYM8, rq.MOE_Q_INT4])
+@pytest.mark.parametrize("xtype", [synth.F32, synth.F16, synth.BF16])
+def test_single_token_layer_edge_shapes(E, H, I, k, scheme, xtype):
+    from tests.cases import gap_failures
+    say(f"one token E={E} H={H} I={I} k={k} scheme={scheme} xtype={xtype}")
+    g = np.random.default_rng(E * 31 + H + I + k + 7 * scheme + xtype)
+    R = (g.standard_normal((E, H)) / np.sqrt(H)).astype(np.float32)
+    bf16 = xtype == synth.BF16
+    for _ in range(64):  # a token whose routing has margin (the oracle decides ties in fp64)
+        x = synth.encode_x(g.standard_normal((1, H)).astype(np.float32), xtype)
+        if k == E or len(gap_failures(x, R, k, bf16)) == 0:
+            break
+    else:
+        pytest.fail("no token with a routing margin")
+    wgu = (g.standard_normal((E, 2 * I, H)) * 0.02).astype(np.float32)
+    wd = (g.standard_normal((E, H, I)) * 0.02).astype(np.float32)
+    ex = rq.quantize_experts(torch.from_numpy(wgu).cuda(), torch.from_numpy(wd).cuda(), scheme)
+    ridx, rgate = oracle.route(x, R, k, bf16=bf16)
+    y, idx, gate = rq.moe_layer_forward(to_dev_x(x, xtype), torch.from_numpy(R).cuda(), ex, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
+    ref = oracle.gather_forward(x, oracle.quantize_experts(wgu, wd, scheme), ridx, rgate, bf16=bf16)
+    assert rel_norm_err(y.cpu().numpy(), ref) <= Y_REL_NORM
