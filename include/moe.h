@@ -183,6 +183,37 @@ enum {
 moe_status moe_timer_start(int32_t kernel, int32_t capacity);
 moe_status moe_timer_read(float* ms, int32_t capacity, int32_t* count);
 
+/* Expert-cache miss policies, replayed over a sequence of routings (host code).
+ * "Which Expert Misses Are Worth Waiting For? Substitution and Caching for
+ * Mixture-of-Experts Inference on a Consumer GPU" (gist.science), section 手法
+ * (method): a routed expert that is not resident is fetched synchronously or
+ * substituted by a resident one; MOE_MISS_FETCH_ALL fetches every miss,
+ * MOE_MISS_RULE fetches a miss that is the first choice (slot 0) or has gate >=
+ * `threshold` (0.15 on the page), MOE_MISS_FIRST_CHOICE fetches first-choice misses
+ * only. With admit_beta > 0 each substituted expert's gates accumulate and it is
+ * admitted in the background once the sum reaches admit_beta (0.5 on the page,
+ * section 主な貢献と知見, item 5, with frequency-based eviction).
+ * Cache: `capacity` slots (k <= capacity <= E), initially empty; an admission into
+ * a full cache evicts the resident expert selected least often so far (lower id on
+ * ties), never one the current token selected; an admission resets the expert's
+ * accumulator.
+ * Inputs: HOST arrays topk_idx [T][k] (slot order, ids in [0, E), distinct per
+ * token) and topk_gate [T][k] (the normalised gates). Outputs, HOST arrays: m [T]
+ * (substituted gate mass of each token), sync_fetches [T], bg_fetches [T] (experts
+ * admitted in the background after each token) and, if non-null, resident [E]
+ * (1 for the experts resident at the end). Deterministic. Errors:
+ * MOE_ERR_INVALID_ARG for null arrays, shapes outside 1 <= k <= capacity <= E <=
+ * 1 << 20 and T >= 0, ids out of range or repeated within a token;
+ * MOE_ERR_UNSUPPORTED for an unknown policy. */
+typedef enum {
+  MOE_MISS_FETCH_ALL = 0,
+  MOE_MISS_RULE = 1,
+  MOE_MISS_FIRST_CHOICE = 2
+} moe_miss_policy;
+moe_status moe_miss_replay(const int32_t* topk_idx, const float* topk_gate, int32_t T, int32_t k, int32_t E,
+                           int32_t capacity, int32_t policy, float threshold, float admit_beta, float* m,
+                           int32_t* sync_fetches, int32_t* bg_fetches, uint8_t* resident);
+
 /* Benchmark support: the achievable-bandwidth reference. Reads `bytes` bytes
  * (a positive multiple of 16) of the device buffer `buf` once, with coalesced
  * 16-byte non-temporal loads spread over the whole GPU, and writes nothing.

@@ -27,8 +27,8 @@ MOE_FLAG_RENORM, MOE_FLAG_PATH_GATHER, MOE_FLAG_PATH_GEMM = 1, 2, 4
 
 # Every function the header declares; the library must export all of them.
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_group", "moe_gather_qmm_forward", "moe_layer_forward",
-           "moe_quantize", "moe_timer_start", "moe_timer_read", "moe_stream_read", "moe_status_str",
-           "moe_last_error")
+           "moe_quantize", "moe_timer_start", "moe_timer_read", "moe_stream_read", "moe_miss_replay",
+           "moe_status_str", "moe_last_error")
 
 (MOE_KERNEL_ROUTE_LOGITS, MOE_KERNEL_TOPK, MOE_KERNEL_GROUP, MOE_KERNEL_GATE_UP, MOE_KERNEL_DOWN, MOE_KERNEL_COMBINE,
  MOE_KERNEL_GEMM_GATE_UP, MOE_KERNEL_GEMM_DOWN, MOE_KERNEL_QUANTIZE) = range(9)
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
             "moe_timer_start": ([I32, I32], ctypes.c_int),
             "moe_timer_read": ([P, I32, P], ctypes.c_int),
             "moe_stream_read": ([P, I64, P], ctypes.c_int),
+            "moe_miss_replay": ([P, P, I32, I32, I32, I32, I32, ctypes.c_float, ctypes.c_float, P, P, P, P],
+                                ctypes.c_int),
             "moe_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "moe_last_error": ([], ctypes.c_char_p),
         }
@@ -172,6 +174,30 @@ def moe_quantize(w: torch.Tensor, scheme: int, stream=None):
     scales = torch.empty(w.shape[:-1] + (K // 32,), dtype=torch.int16, device=w.device)
     _check("moe_quantize", lib().moe_quantize(_p(w), rows, K, scheme, _p(codes), _p(scales), _stream(stream)))
     return codes, scales
+
+
+MOE_MISS_FETCH_ALL, MOE_MISS_RULE, MOE_MISS_FIRST_CHOICE = 0, 1, 2
+
+
+def moe_miss_replay(topk_idx, topk_gate, E: int, capacity: int, policy: int, threshold: float = 0.15,
+                    admit_beta: float = 0.0):
+    """Replay the expert-cache miss policy over a sequence of routings (host arrays
+    [T][k] in slot order). Returns (m float32 [T], sync_fetches int32 [T],
+    bg_fetches int32 [T], resident bool [E])."""
+    import numpy as np
+    idx = np.ascontiguousarray(np.asarray(topk_idx), dtype=np.int32)
+    gate = np.ascontiguousarray(np.asarray(topk_gate), dtype=np.float32)
+    if idx.ndim != 2 or gate.shape != idx.shape:
+        raise ValueError("topk_idx and topk_gate must be [T][k] arrays of one shape")
+    T, k = idx.shape
+    m = np.empty(T, dtype=np.float32)
+    sync = np.empty(T, dtype=np.int32)
+    bg = np.empty(T, dtype=np.int32)
+    res = np.empty(E, dtype=np.uint8)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    _check("moe_miss_replay", lib().moe_miss_replay(ptr(idx), ptr(gate), T, k, E, capacity, policy, threshold,
+                                                    admit_beta, ptr(m), ptr(sync), ptr(bg), ptr(res)))
+    return m, sync, bg, res.astype(bool)
 
 
 def moe_stream_read(buf: torch.Tensor, nbytes: int | None = None, stream=None) -> None:

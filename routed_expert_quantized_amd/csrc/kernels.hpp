@@ -76,6 +76,10 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
                             int32_t* idx_ws, float* gate_ws, int32_t* idx_user, float* gate_user,
                             float* h, float* y, hipStream_t s);
 
+// Host replay of the expert-cache miss policies (arguments checked by the caller).
+void miss_replay(const int32_t* idx, const float* gate, int T, int k, int E, int capacity, int policy,
+                 float threshold, float beta, float* m, int32_t* sync, int32_t* bg, uint8_t* resident);
+
 // Plain streaming read of `bytes` bytes (benchmark reference).
 hipError_t launch_stream_read(const void* buf, int64_t bytes, hipStream_t s);
 

@@ -314,6 +314,28 @@ moe_status moe_quantize(const float* w, int64_t rows, int32_t K, int32_t scheme,
                     "quantize");
 }
 
+moe_status moe_miss_replay(const int32_t* topk_idx, const float* topk_gate, int32_t T, int32_t k, int32_t E,
+                           int32_t capacity, int32_t policy, float threshold, float admit_beta, float* m,
+                           int32_t* sync_fetches, int32_t* bg_fetches, uint8_t* resident) {
+  if (!topk_idx || !topk_gate || !m || !sync_fetches || !bg_fetches)
+    return fail(MOE_ERR_INVALID_ARG, "topk_idx, topk_gate, m, sync_fetches or bg_fetches is NULL");
+  if (T < 0 || k < 1 || capacity < k || E < capacity || E > (1 << 20))
+    return fail(MOE_ERR_INVALID_ARG, "T=%d k=%d capacity=%d E=%d: need T >= 0 and 1 <= k <= capacity <= E <= 2^20",
+                T, k, capacity, E);
+  if (policy != MOE_MISS_FETCH_ALL && policy != MOE_MISS_RULE && policy != MOE_MISS_FIRST_CHOICE)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown miss policy %d", policy);
+  for (int64_t t = 0; t < T; ++t)
+    for (int s = 0; s < k; ++s) {
+      const int32_t e = topk_idx[t * k + s];
+      if (e < 0 || e >= E) return fail(MOE_ERR_INVALID_ARG, "token %lld slot %d: expert %d out of [0, %d)", (long long)t, s, e, E);
+      for (int j = 0; j < s; ++j)
+        if (topk_idx[t * k + j] == e) return fail(MOE_ERR_INVALID_ARG, "token %lld: expert %d selected twice", (long long)t, e);
+    }
+  moe::miss_replay(topk_idx, topk_gate, T, k, E, capacity, policy, threshold, admit_beta, m, sync_fetches, bg_fetches,
+                   resident);
+  return ok();
+}
+
 moe_status moe_stream_read(const void* buf, int64_t bytes, void* stream) {
   if (!buf || !aligned(buf, 16)) return fail(MOE_ERR_INVALID_ARG, "buf is NULL or not 16-byte aligned");
   if (bytes <= 0 || bytes % 16 || bytes > ((int64_t)1 << 40))
