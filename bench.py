@@ -91,6 +91,53 @@ def dtype_name(w, gemm: bool) -> str:
     return f"gate/up {gu}; down {down}; f32 router, combine"
 
 
+def miss_policies(w, xs, router, pool, rq, torch) -> dict:
+    """Expert-cache miss policies replayed (moe_miss_replay) over the routing of
+    the workload's distinct tokens, in order, through one layer's router: a
+    quarter of the experts resident, as on the pages. Fetched bytes count the
+    synchronous fetches and background admissions at the expert's packed size.
+    Also times moe_stage_experts filling a stack of that many slots from the
+    pool (HBM to HBM; the pages fetch from SSD or host memory instead)."""
+    import numpy as np
+    idx, gate = [], []
+    for x in xs:
+        i, g = rq.moe_route(x, router, w.k, rq.MOE_FLAG_RENORM)
+        idx.append(i.cpu().numpy())
+        gate.append(g.cpu().numpy())
+    idx, gate = np.concatenate(idx), np.concatenate(gate)
+    C = max(w.k, w.E // 4)
+    out = {"tokens": int(idx.shape[0]), "capacity": C, "expert_bytes": expert_bytes(w)}
+    for name, pol, beta in (("fetch_all", rq.MOE_MISS_FETCH_ALL, 0.0), ("quality_first", rq.MOE_MISS_RULE, 0.5),
+                            ("speed_first", rq.MOE_MISS_FIRST_CHOICE, 0.5)):
+        t0 = time.perf_counter()
+        m, sync, bg, _ = rq.moe_miss_replay(idx, gate, w.E, C, pol, 0.15, beta)
+        dt = time.perf_counter() - t0
+        fetched = float(np.mean(sync + bg))
+        out[name] = {"mean_m": round(float(np.mean(m)), 5), "max_m": round(float(np.max(m)), 5),
+                     "sync_fetches_per_token": round(float(np.mean(sync)), 4),
+                     "bg_fetches_per_token": round(float(np.mean(bg)), 4),
+                     "fetched_bytes_per_token": int(round(fetched * expert_bytes(w))),
+                     "replay_us_per_token": round(dt * 1e6 / idx.shape[0], 3)}
+    out["fetch_all_hit_rate"] = round(1.0 - out["fetch_all"]["sync_fetches_per_token"] / w.k, 4)
+    stack = rq.empty_stack(pool, C)
+    experts = torch.randperm(w.E, device="cuda")[:C].to(torch.int32)
+    slots = torch.arange(C, device="cuda", dtype=torch.int32)
+    rq.moe_stage_experts(pool, stack, experts, slots)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(8):
+        rq.moe_stage_experts(pool, stack, experts, slots)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 8
+    nbytes = C * expert_bytes(w)
+    out["stage_all_slots"] = {"bytes": nbytes, "us": round(us, 2),
+                              "gbps_copied": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    del stack
+    return out
+
+
 def stream_ceiling(nbytes: int, rq, torch) -> dict:
     """A plain streaming read of one layer's routed bytes (moe_stream_read), as
     back-to-back launches in a HIP graph over distinct buffers that together far
@@ -325,6 +372,7 @@ def main():
     mfma_tflops = gu_flops / (gu_us * 1e-6) / 1e12
 
     ceiling = stream_ceiling(int(round(routed_bytes)), rq, torch)
+    miss = miss_policies(w, [xs[i] for i in range(nx)], routers[0], pools[0], rq, torch) if w.T <= 64 else None
 
     traffic = None
     tf = os.path.join(ROOT, "profiles", f"traffic_{dom}_{w.name}.json")
@@ -360,6 +408,7 @@ def main():
         "routed_hbm_gbps": round(routed_gbps, 1),
         "routed_hbm_frac": round(routed_gbps / HBM_PEAK_GBPS, 4),
         "stream_read_ceiling": {**ceiling, "layer_vs_ceiling": round(routed_gbps / ceiling["gbps"], 4)},
+        **({"miss_policies": miss} if miss else {}),
         "kernel_us": {n: round(v, 3) for n, v in kern_us.items()},
         "roofline": {"kernel": kname, "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

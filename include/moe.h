@@ -214,6 +214,31 @@ moe_status moe_miss_replay(const int32_t* topk_idx, const float* topk_gate, int3
                            int32_t capacity, int32_t policy, float threshold, float admit_beta, float* m,
                            int32_t* sync_fetches, int32_t* bg_fetches, uint8_t* resident);
 
+/* Staged decode: a resident stack of experts behind a slot table.
+ * "The Other Half of the Memory Wall: Serving 35B MoEs from SSD with Trained
+ * Routing Prediction" (xyznot.com), 重要用語 (glossary): expert indices are mapped
+ * through a slot table on the GPU into a fixed set of expert slots (no allocation
+ * per step), and the stacked expert tensor is updated in place by rewriting only
+ * the slots whose expert changed.
+ *
+ * moe_stage_experts copies, for i < n, expert experts[i] of `pool` (its gate/up
+ * codes and scales, its down codes and scales) into slot slots[i] of `stack`.
+ * `stack` is an expert set of the same H, I and codec whose E is its slot count.
+ * experts [n] and slots [n] are DEVICE int32 arrays, trusted to lie in [0, pool->E)
+ * and [0, stack->E), with distinct slots. All eight weight and scale pointers must
+ * be 16-byte aligned. Asynchronous on `stream`.
+ *
+ * moe_remap_ids writes out[i] = slot_of[idx[i]] for i < n (DEVICE arrays; idx
+ * trusted to lie in [0, E), slot_of [E] holding each resident expert's slot), so a
+ * routing can be run on the stack with moe_gather_qmm_forward.
+ *
+ * Errors: MOE_ERR_INVALID_ARG for null or misaligned pointers, n < 0, stacks whose
+ * H, I or codec differ from the pool's; MOE_ERR_HIP for a failed launch. */
+moe_status moe_stage_experts(const moe_experts* pool, const moe_experts* stack, const int32_t* experts,
+                             const int32_t* slots, int32_t n, void* stream);
+moe_status moe_remap_ids(const int32_t* idx, int64_t n, const int32_t* slot_of, int32_t E, int32_t* out,
+                         void* stream);
+
 /* Benchmark support: the achievable-bandwidth reference. Reads `bytes` bytes
  * (a positive multiple of 16) of the device buffer `buf` once, with coalesced
  * 16-byte non-temporal loads spread over the whole GPU, and writes nothing.

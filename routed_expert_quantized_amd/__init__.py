@@ -28,7 +28,7 @@ MOE_FLAG_RENORM, MOE_FLAG_PATH_GATHER, MOE_FLAG_PATH_GEMM = 1, 2, 4
 # Every function the header declares; the library must export all of them.
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_group", "moe_gather_qmm_forward", "moe_layer_forward",
            "moe_quantize", "moe_timer_start", "moe_timer_read", "moe_stream_read", "moe_miss_replay",
-           "moe_status_str", "moe_last_error")
+           "moe_stage_experts", "moe_remap_ids", "moe_status_str", "moe_last_error")
 
 (MOE_KERNEL_ROUTE_LOGITS, MOE_KERNEL_TOPK, MOE_KERNEL_GROUP, MOE_KERNEL_GATE_UP, MOE_KERNEL_DOWN, MOE_KERNEL_COMBINE,
  MOE_KERNEL_GEMM_GATE_UP, MOE_KERNEL_GEMM_DOWN, MOE_KERNEL_QUANTIZE) = range(9)
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
             "moe_timer_start": ([I32, I32], ctypes.c_int),
             "moe_timer_read": ([P, I32, P], ctypes.c_int),
             "moe_stream_read": ([P, I64, P], ctypes.c_int),
+            "moe_stage_experts": ([E, E, P, P, I32, P], ctypes.c_int),
+            "moe_remap_ids": ([P, I64, P, I32, P, P], ctypes.c_int),
             "moe_miss_replay": ([P, P, I32, I32, I32, I32, I32, ctypes.c_float, ctypes.c_float, P, P, P, P],
                                 ctypes.c_int),
             "moe_status_str": ([ctypes.c_int], ctypes.c_char_p),
@@ -174,6 +176,36 @@ def moe_quantize(w: torch.Tensor, scheme: int, stream=None):
     scales = torch.empty(w.shape[:-1] + (K // 32,), dtype=torch.int16, device=w.device)
     _check("moe_quantize", lib().moe_quantize(_p(w), rows, K, scheme, _p(codes), _p(scales), _stream(stream)))
     return codes, scales
+
+
+def empty_stack(pool: "Experts", slots: int) -> "Experts":
+    """A resident stack of `slots` expert slots shaped like `pool` (uninitialised)."""
+    def like(t):
+        return torch.empty((slots,) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)
+    return Experts(slots, pool.H, pool.I, pool.scheme, like(pool.w_gate_up), like(pool.s_gate_up), like(pool.w_down),
+                   like(pool.s_down))
+
+
+def moe_stage_experts(pool: "Experts", stack: "Experts", experts: torch.Tensor, slots: torch.Tensor,
+                      stream=None) -> None:
+    """Copy pool experts `experts` (device int32 [n]) into stack slots `slots` (device int32 [n])."""
+    _device_tensor(experts, "experts")
+    _device_tensor(slots, "slots")
+    assert experts.dtype == torch.int32 and slots.dtype == torch.int32 and experts.shape == slots.shape
+    cp, cs = pool.c(), stack.c()
+    _check("moe_stage_experts", lib().moe_stage_experts(ctypes.byref(cp), ctypes.byref(cs), _p(experts), _p(slots),
+                                                        experts.numel(), _stream(stream)))
+
+
+def moe_remap_ids(idx: torch.Tensor, slot_of: torch.Tensor, stream=None) -> torch.Tensor:
+    """out[...] = slot_of[idx[...]] on the device (int32)."""
+    _device_tensor(idx, "idx")
+    _device_tensor(slot_of, "slot_of")
+    assert idx.dtype == torch.int32 and slot_of.dtype == torch.int32
+    out = torch.empty_like(idx)
+    _check("moe_remap_ids", lib().moe_remap_ids(_p(idx), idx.numel(), _p(slot_of), slot_of.numel(), _p(out),
+                                                _stream(stream)))
+    return out
 
 
 MOE_MISS_FETCH_ALL, MOE_MISS_RULE, MOE_MISS_FIRST_CHOICE = 0, 1, 2

@@ -76,6 +76,11 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
                             int32_t* idx_ws, float* gate_ws, int32_t* idx_user, float* gate_user,
                             float* h, float* y, hipStream_t s);
 
+// Staged decode: copy experts[i] of pool into slot slots[i] of stack; out = slot_of[idx].
+hipError_t launch_stage_experts(const ExpertsDev& pool, const ExpertsDev& stack, const int32_t* experts,
+                                const int32_t* slots, int n, hipStream_t s);
+hipError_t launch_remap_ids(const int32_t* idx, int64_t n, const int32_t* slot_of, int32_t* out, hipStream_t s);
+
 // Host replay of the expert-cache miss policies (arguments checked by the caller).
 void miss_replay(const int32_t* idx, const float* gate, int T, int k, int E, int capacity, int policy,
                  float threshold, float beta, float* m, int32_t* sync, int32_t* bg, uint8_t* resident);

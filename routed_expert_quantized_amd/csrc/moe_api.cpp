@@ -336,6 +336,32 @@ moe_status moe_miss_replay(const int32_t* topk_idx, const float* topk_gate, int3
   return ok();
 }
 
+moe_status moe_stage_experts(const moe_experts* pool, const moe_experts* stack, const int32_t* experts,
+                             const int32_t* slots, int32_t n, void* stream) {
+  moe_status st;
+  moe::ExpertsDev p, q;
+  if ((st = check_experts(pool, &p))) return st;
+  if ((st = check_experts(stack, &q))) return st;
+  if (p.H != q.H || p.I != q.I || p.scheme != q.scheme)
+    return fail(MOE_ERR_INVALID_ARG, "stack (H=%d, I=%d, codec %d) differs from the pool (H=%d, I=%d, codec %d)",
+                q.H, q.I, q.scheme, p.H, p.I, p.scheme);
+  if ((st = check_shape(1, p.E, p.H, p.I, 1))) return st;
+  if (q.E < 1 || q.E > p.E) return fail(MOE_ERR_INVALID_ARG, "stack slots E=%d outside [1, %d]", q.E, p.E);
+  if (!aligned(pool->s_gate_up, 16) || !aligned(pool->s_down, 16) || !aligned(stack->s_gate_up, 16) ||
+      !aligned(stack->s_down, 16))
+    return fail(MOE_ERR_INVALID_ARG, "scales must be 16-byte aligned for staging");
+  if (n < 0 || (n > 0 && (!experts || !slots))) return fail(MOE_ERR_INVALID_ARG, "n=%d, experts or slots NULL", n);
+  return hip_status(moe::launch_stage_experts(p, q, experts, slots, n, static_cast<hipStream_t>(stream)),
+                    "stage experts");
+}
+
+moe_status moe_remap_ids(const int32_t* idx, int64_t n, const int32_t* slot_of, int32_t E, int32_t* out,
+                         void* stream) {
+  if (n < 0 || E < 1) return fail(MOE_ERR_INVALID_ARG, "n=%lld E=%d", (long long)n, E);
+  if (n > 0 && (!idx || !slot_of || !out)) return fail(MOE_ERR_INVALID_ARG, "idx, slot_of or out is NULL");
+  return hip_status(moe::launch_remap_ids(idx, n, slot_of, out, static_cast<hipStream_t>(stream)), "remap ids");
+}
+
 moe_status moe_stream_read(const void* buf, int64_t bytes, void* stream) {
   if (!buf || !aligned(buf, 16)) return fail(MOE_ERR_INVALID_ARG, "buf is NULL or not 16-byte aligned");
   if (bytes <= 0 || bytes % 16 || bytes > ((int64_t)1 << 40))

@@ -125,3 +125,17 @@ def test_group_and_quantize_validation(L):
     assert L.moe_quantize(FAKE, 4, 64, 2, FAKE, FAKE, None) == rq.MOE_ERR_UNSUPPORTED
     assert L.moe_quantize(None, 4, 64, 0, FAKE, FAKE, None) == rq.MOE_ERR_INVALID_ARG
     assert L.moe_quantize(FAKE, -1, 64, 0, FAKE, FAKE, None) == rq.MOE_ERR_INVALID_ARG
+
+
+def test_stage_and_remap_validation(L):
+    pool = rq._Experts(8, 64, 32, rq.MOE_Q_SYM8, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    wrong = rq._Experts(4, 64, 64, rq.MOE_Q_SYM8, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    big = rq._Experts(9, 64, 32, rq.MOE_Q_SYM8, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    odd = rq._Experts(4, 64, 32, rq.MOE_Q_SYM8, FAKE.value, FAKE.value + 2, FAKE.value, FAKE.value)
+    assert L.moe_stage_experts(ctypes.byref(pool), ctypes.byref(wrong), FAKE, FAKE, 1, None) == rq.MOE_ERR_INVALID_ARG
+    assert L.moe_stage_experts(ctypes.byref(pool), ctypes.byref(big), FAKE, FAKE, 1, None) == rq.MOE_ERR_INVALID_ARG
+    assert L.moe_stage_experts(ctypes.byref(pool), ctypes.byref(odd), FAKE, FAKE, 1, None) == rq.MOE_ERR_INVALID_ARG
+    assert L.moe_stage_experts(ctypes.byref(pool), ctypes.byref(pool), None, FAKE, 1, None) == rq.MOE_ERR_INVALID_ARG
+    assert L.moe_stage_experts(ctypes.byref(pool), ctypes.byref(pool), FAKE, FAKE, -1, None) == rq.MOE_ERR_INVALID_ARG
+    assert L.moe_remap_ids(None, 4, FAKE, 8, FAKE, None) == rq.MOE_ERR_INVALID_ARG
+    assert L.moe_remap_ids(FAKE, -1, FAKE, 8, FAKE, None) == rq.MOE_ERR_INVALID_ARG

@@ -289,3 +289,42 @@ def test_single_token_layer_edge_shapes(E, H, I, k, scheme, xtype):
     assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
     ref = oracle.gather_forward(x, oracle.quantize_experts(wgu, wd, scheme), ridx, rgate, bf16=bf16)
     assert rel_norm_err(y.cpu().numpy(), ref) <= Y_REL_NORM
+
+
+@pytest.mark.parametrize("scheme", [rq.MOE_Q_SYM8, rq.MOE_Q_INT4])
+@pytest.mark.parametrize("T", [1, 5])
+def test_staged_stack_matches_pool(scheme, T):
+    """Staged decode: experts copied into stack slots (a full fill, then three
+    slots rewritten in place) hold the pool's bytes, the slot table maps the
+    routing, and the layer on the stack equals the layer on the pool."""
+    E, H, I, k, S = 24, 256, 128, 4, 8
+    g = np.random.default_rng(40 + scheme + T)
+    wgu = torch.from_numpy((g.standard_normal((E, 2 * I, H)) * 0.02).astype(np.float32)).cuda()
+    wd = torch.from_numpy((g.standard_normal((E, H, I)) * 0.02).astype(np.float32)).cuda()
+    pool = rq.quantize_experts(wgu, wd, scheme)
+    stack = rq.empty_stack(pool, S)
+    first = g.choice(E, S, replace=False).astype(np.int32)
+    slots1 = g.permutation(S).astype(np.int32)
+    rq.moe_stage_experts(pool, stack, torch.from_numpy(first).cuda(), torch.from_numpy(slots1).cuda())
+    slot_expert = np.empty(S, dtype=np.int32)
+    slot_expert[slots1] = first
+    newcomers = g.choice(np.setdiff1d(np.arange(E), first), 3, replace=False).astype(np.int32)
+    slots2 = g.choice(S, 3, replace=False).astype(np.int32)
+    rq.moe_stage_experts(pool, stack, torch.from_numpy(newcomers).cuda(), torch.from_numpy(slots2).cuda())
+    slot_expert[slots2] = newcomers
+    torch.cuda.synchronize()
+    sel = torch.from_numpy(slot_expert.astype(np.int64)).cuda()
+    for name in ("w_gate_up", "s_gate_up", "w_down", "s_down"):
+        assert torch.equal(getattr(stack, name), getattr(pool, name)[sel]), name
+    slot_of = np.full(E, 0, dtype=np.int32)
+    slot_of[slot_expert] = np.arange(S, dtype=np.int32)
+    idx = np.stack([g.choice(slot_expert, k, replace=False) for _ in range(T)]).astype(np.int32)
+    gate = g.random((T, k)).astype(np.float32)
+    sidx = rq.moe_remap_ids(torch.from_numpy(idx).cuda(), torch.from_numpy(slot_of).cuda())
+    assert np.array_equal(sidx.cpu().numpy(), slot_of[idx])
+    x = torch.from_numpy(g.standard_normal((T, H)).astype(np.float16)).cuda()
+    gd = torch.from_numpy(gate).cuda()
+    y_stack = rq.moe_gather_qmm_forward(x, stack, sidx, gd)
+    y_pool = rq.moe_gather_qmm_forward(x, pool, torch.from_numpy(idx).cuda(), gd)
+    torch.cuda.synchronize()
+    assert rel_norm_err(y_stack.cpu().numpy(), y_pool.cpu().numpy()) <= 1e-6
