@@ -10,6 +10,8 @@ through ctypes. Page keys:
 
   [LR] "QwenのMoEルーターを観測してホットエキスパートを先読みしても速くならなかった" (lilting.ch)
   [QK] "鳴かぬなら、カスタムカーネル、ほととぎす" (qiita.com, john-rocky)
+  [MW] "The Other Half of the Memory Wall: Serving 35B MoEs from SSD with
+       Trained Routing Prediction" (xyznot.com)
 """
 from __future__ import annotations
 
@@ -77,6 +79,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "oref_logits": ([P, I32, I32, I32, P, I32, P], ctypes.c_int),
         "oref_route": ([P, I32, I32, I32, P, I32, I32, U32, P, P], ctypes.c_int),
         "oref_group": ([P, I32, I32, I32, P, P, P, P, P], ctypes.c_int),
+        "oref_prerouter": ([P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, I32, U32, P, P, P], ctypes.c_int),
         "oref_gather_forward": ([P, I32, I32, ctypes.POINTER(_Experts), I32, P, P, P], ctypes.c_int),
         "oref_layer_forward": ([P, I32, I32, P, ctypes.POINTER(_Experts), I32, U32, P, P, P], ctypes.c_int),
         "oref_dense_forward": ([P, I32, I32, ctypes.POINTER(_Experts), P, P], ctypes.c_int),
@@ -189,6 +192,53 @@ def route(x: np.ndarray, R: np.ndarray, k: int, flags: int = RENORM, bf16: bool 
     _check(lib().oref_route(_ptr(x), _xtype(x, bf16), T, H, _ptr(R), E, k, flags, _ptr(idx), _ptr(gate)),
            "oref_route")
     return idx, gate
+
+
+@dataclass
+class PrerouterHead:
+    """Prerouter head weights, fp32, in the page's layout: the input feature is
+    [hidden (H) ; k-hot current routing (E) ; k-hot previous routing (E)].
+
+    w1 [F][H+2E] and b1 [F] (fc1), w2 [E][F] and b2 [E] (fc2), wl [E][H+2E] (the
+    linear residual path). b1 and b2 may be None (no bias)."""
+    w1: np.ndarray
+    b1: np.ndarray | None
+    w2: np.ndarray
+    b2: np.ndarray | None
+    wl: np.ndarray
+
+    @property
+    def E(self) -> int:
+        return self.w2.shape[0]
+
+    @property
+    def F(self) -> int:
+        return self.w1.shape[0]
+
+    @property
+    def H(self) -> int:
+        return self.w1.shape[1] - 2 * self.E
+
+
+def prerouter(x: np.ndarray, head: PrerouterHead, cur: np.ndarray | None, prev: np.ndarray | None, k: int,
+              flags: int = RENORM, bf16: bool = False):
+    """Head logits (fp64), then the router's softmax/top-k on them [MW "prerouter head
+    architecture"]. Returns (idx [T][k] int32, gate [T][k] fp32, logits [T][E] fp64)."""
+    x = np.ascontiguousarray(x)
+    T, H = x.shape
+    E, F = head.E, head.F
+    assert head.H == H and head.wl.shape == (E, H + 2 * E) and head.w2.shape == (E, F)
+    f32 = lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+    i32 = lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.int32).reshape(T, k)
+    w1, b1, w2, b2, wl = f32(head.w1), f32(head.b1), f32(head.w2), f32(head.b2), f32(head.wl)
+    cur, prev = i32(cur), i32(prev)
+    idx = np.empty((T, k), dtype=np.int32)
+    gate = np.empty((T, k), dtype=np.float32)
+    lg = np.empty((T, E), dtype=np.float64)
+    _check(lib().oref_prerouter(_ptr(x), _xtype(x, bf16), T, H, E, F, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
+                                _ptr(wl), _ptr(cur), _ptr(prev), k, flags, _ptr(idx), _ptr(gate), _ptr(lg)),
+           "oref_prerouter")
+    return idx, gate, lg
 
 
 def group(idx: np.ndarray, E: int):

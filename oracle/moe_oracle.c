@@ -6,6 +6,8 @@
  * library. Page citations use the keys defined in moe_oracle.h:
  *   [LR] "QwenのMoEルーターを観測してホットエキスパートを先読みしても速くならなかった" (lilting.ch)
  *   [QK] "鳴かぬなら、カスタムカーネル、ほととぎす" (qiita.com, john-rocky)
+ *   [MW] "The Other Half of the Memory Wall: Serving 35B MoEs from SSD with
+ *        Trained Routing Prediction" (xyznot.com)
  *
  * Precision: activations are upcast exactly; weights are code * scale, which is
  * exact in fp32; every sum runs in fp64 and results are rounded to fp32 once.
@@ -183,6 +185,43 @@ int oref_logits(const void* x, int32_t xtype, int32_t T, int32_t H,
   return 0;
 }
 
+/* Softmax over the E logits of one token, then the top k [LR "hooking the
+ * router"]: k rounds of "largest fp32-rounded logit not yet taken, lowest id on
+ * ties"; each chosen expert's probability, divided by the sum over the k when
+ * flags has OREF_RENORM. Returns nonzero when out of memory. */
+static int softmax_topk_row(const double* l, int32_t E, int32_t k, uint32_t flags,
+                            int32_t* idx, float* gate) {
+  /* softmax over all E experts, in fp64 (max subtracted first) */
+  double mx = l[0];
+  for (int32_t e = 1; e < E; ++e) if (l[e] > mx) mx = l[e];
+  double* p = (double*)malloc(sizeof(double) * (size_t)E);
+  char* taken = (char*)calloc((size_t)E, 1);
+  if (!p || !taken) { free(p); free(taken); return 1; }
+  double z = 0.0;
+  for (int32_t e = 0; e < E; ++e) { p[e] = exp(l[e] - mx); z += p[e]; }
+  for (int32_t e = 0; e < E; ++e) p[e] /= z;
+  double psum = 0.0;
+  for (int32_t s = 0; s < k; ++s) {
+    int32_t best = -1;
+    float bv = 0.0f;
+    for (int32_t e = 0; e < E; ++e) {
+      if (taken[e]) continue;
+      const float v = (float)l[e];
+      if (best < 0 || v > bv) { best = e; bv = v; }
+    }
+    taken[best] = 1;
+    idx[s] = best;
+    psum += p[best];
+  }
+  for (int32_t s = 0; s < k; ++s) {
+    const double ps = p[idx[s]];
+    gate[s] = (float)((flags & OREF_RENORM) ? ps / psum : ps);
+  }
+  free(p);
+  free(taken);
+  return 0;
+}
+
 int oref_route(const void* x, int32_t xtype, int32_t T, int32_t H,
                const float* R, int32_t E, int32_t k, uint32_t flags,
                int32_t* idx, float* gate) {
@@ -193,39 +232,64 @@ int oref_route(const void* x, int32_t xtype, int32_t T, int32_t H,
   if (rc) { free(lg); return rc; }
   int fail = 0;
   #pragma omp parallel for schedule(static)
-  for (int32_t t = 0; t < T; ++t) {
-    const double* l = lg + (int64_t)t * E;
-    /* softmax over all E experts, in fp64 (max subtracted first) */
-    double mx = l[0];
-    for (int32_t e = 1; e < E; ++e) if (l[e] > mx) mx = l[e];
-    double* p = (double*)malloc(sizeof(double) * (size_t)E);
-    char* taken = (char*)calloc((size_t)E, 1);
-    if (!p || !taken) { free(p); free(taken); fail = 1; continue; }
-    double z = 0.0;
-    for (int32_t e = 0; e < E; ++e) { p[e] = exp(l[e] - mx); z += p[e]; }
-    for (int32_t e = 0; e < E; ++e) p[e] /= z;
-    /* top-k: k rounds of "largest fp32 logit not yet taken, lowest id on ties" */
-    double psum = 0.0;
-    for (int32_t s = 0; s < k; ++s) {
-      int32_t best = -1;
-      float bv = 0.0f;
-      for (int32_t e = 0; e < E; ++e) {
-        if (taken[e]) continue;
-        const float v = (float)l[e];
-        if (best < 0 || v > bv) { best = e; bv = v; }
-      }
-      taken[best] = 1;
-      idx[(int64_t)t * k + s] = best;
-      psum += p[best];
-    }
-    for (int32_t s = 0; s < k; ++s) {
-      const double ps = p[idx[(int64_t)t * k + s]];
-      gate[(int64_t)t * k + s] = (float)((flags & OREF_RENORM) ? ps / psum : ps);
-    }
-    free(p);
-    free(taken);
-  }
+  for (int32_t t = 0; t < T; ++t)
+    if (softmax_topk_row(lg + (int64_t)t * E, E, k, flags, idx + (int64_t)t * k, gate + (int64_t)t * k))
+      fail = 1;
   free(lg);
+  return fail ? -3 : 0;
+}
+
+/* ---------------- prerouter head ---------------- */
+
+/* erf-form GELU: z * Phi(z), Phi the standard normal CDF, written with erf
+ * [MW "Prerouterヘッドのアーキテクチャ" (prerouter head architecture)]. */
+static double gelu_erf(double z) { return 0.5 * z * (1.0 + erf(z / sqrt(2.0))); }
+
+int oref_prerouter(const void* x, int32_t xtype, int32_t T, int32_t H, int32_t E, int32_t F,
+                   const float* w1, const float* b1, const float* w2, const float* b2,
+                   const float* wl, const int32_t* cur, const int32_t* prev, int32_t k,
+                   uint32_t flags, int32_t* idx, float* gate, double* logits) {
+  if (!x || !w1 || !w2 || !wl || !idx || !gate || !logits || T < 0 || H <= 0 || E <= 0 || F <= 0 ||
+      k < 1 || k > E) return -1;
+  if (xtype < OREF_F32 || xtype > OREF_BF16) return -2;
+  const int32_t D = H + 2 * E;
+  int bad = 0;
+  for (int64_t i = 0; i < (int64_t)T * k; ++i) {
+    if (cur && (cur[i] < 0 || cur[i] >= E)) bad = 1;
+    if (prev && (prev[i] < 0 || prev[i] >= E)) bad = 1;
+  }
+  if (bad) return -1;
+  int fail = 0;
+  #pragma omp parallel for schedule(static)
+  for (int32_t t = 0; t < T; ++t) {
+    /* the input feature: hidden state, then the k-hot routing vector of the
+     * current token, then that of the previous token (dim = d_model + 2E) */
+    double* f = (double*)calloc((size_t)D, sizeof(double));
+    double* a = (double*)malloc(sizeof(double) * (size_t)F);
+    if (!f || !a) { free(f); free(a); fail = 1; continue; }
+    for (int32_t i = 0; i < H; ++i) f[i] = x_elem(x, xtype, (int64_t)t * H + i);
+    for (int32_t s = 0; s < k; ++s) {
+      if (cur) f[H + cur[(int64_t)t * k + s]] = 1.0;
+      if (prev) f[H + E + prev[(int64_t)t * k + s]] = 1.0;
+    }
+    /* a = erf-gelu(fc1(f)) */
+    for (int32_t j = 0; j < F; ++j) {
+      double z = b1 ? (double)b1[j] : 0.0;
+      for (int32_t i = 0; i < D; ++i) z += (double)w1[(int64_t)j * D + i] * f[i];
+      a[j] = gelu_erf(z);
+    }
+    /* head = fc2(a) + l(f), l the bias-free linear residual path */
+    double* l = logits + (int64_t)t * E;
+    for (int32_t e = 0; e < E; ++e) {
+      double acc = b2 ? (double)b2[e] : 0.0;
+      for (int32_t j = 0; j < F; ++j) acc += (double)w2[(int64_t)e * F + j] * a[j];
+      for (int32_t i = 0; i < D; ++i) acc += (double)wl[(int64_t)e * D + i] * f[i];
+      l[e] = acc;
+    }
+    free(f);
+    free(a);
+    if (softmax_topk_row(l, E, k, flags, idx + (int64_t)t * k, gate + (int64_t)t * k)) fail = 1;
+  }
   return fail ? -3 : 0;
 }
 

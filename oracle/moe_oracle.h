@@ -16,6 +16,9 @@
  *   [QK] "鳴かぬなら、カスタムカーネル、ほととぎす" (qiita.com, john-rocky).
  *        Sections: §1 (what MoE buys), §4 (custom kernel gather_qmm),
  *        §6 (quality check), §7 (pitfalls).
+ *   [MW] "The Other Half of the Memory Wall: Serving 35B MoEs from SSD with
+ *        Trained Routing Prediction" (xyznot.com). Section 手法 (method),
+ *        "Prerouterヘッドのアーキテクチャ" (prerouter head architecture).
  *
  * Conventions:
  *   - All pointers are host pointers, owned by the caller, never retained.
@@ -73,6 +76,20 @@ int oref_logits(const void* x, int32_t xtype, int32_t T, int32_t H,
 int oref_route(const void* x, int32_t xtype, int32_t T, int32_t H,
                const float* R, int32_t E, int32_t k, uint32_t flags,
                int32_t* idx, float* gate);
+
+/* Prerouter head [MW "prerouter head architecture"], per token t:
+ *   f = [x_t ; khot(cur_t) ; khot(prev_t)]   (H + 2E values; khot(ids) has a 1
+ *       at each of the k ids and 0 elsewhere, all 0 when the array is NULL)
+ *   a = gelu(w1 f + b1),  gelu(z) = z/2 * (1 + erf(z / sqrt 2))   (F values)
+ *   logits_t = w2 a + b2 + wl f                                   (E values)
+ * then the router's softmax and top-k (as oref_route) on logits_t.
+ * Shapes: w1 [F][H+2E], b1 [F] or NULL, w2 [E][F], b2 [E] or NULL,
+ * wl [E][H+2E] (the linear residual path, no bias); cur, prev [T][k] ids in
+ * [0, E) or NULL. Outputs idx [T][k], gate [T][k], logits [T][E] (fp64). */
+int oref_prerouter(const void* x, int32_t xtype, int32_t T, int32_t H, int32_t E, int32_t F,
+                   const float* w1, const float* b1, const float* w2, const float* b2,
+                   const float* wl, const int32_t* cur, const int32_t* prev, int32_t k,
+                   uint32_t flags, int32_t* idx, float* gate, double* logits);
 
 /* Token-by-expert grouping of the T*k flat assignments f = t*k + s:
  * counts[e], offsets[E+1] (exclusive prefix sum), perm[T*k] = the flat ids
