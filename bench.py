@@ -65,6 +65,7 @@ def parse():
                     help="override the workload's top-k (for the bytes-read-versus-k counter sweep)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run a plain fp32 copy kernel over this many MiB (counter calibration)")
+    ap.add_argument("--no-prerouter", action="store_true", help="skip the prerouted (prediction-as-routing) step")
     ap.add_argument("--path", choices=["auto", "gather", "gemm"], default="auto",
                     help="expert path: the library's choice, the gathered matvec or the grouped MFMA GEMM")
     return ap.parse_args()
@@ -136,6 +137,122 @@ def miss_policies(w, xs, router, pool, rq, torch) -> dict:
                               "gbps_copied": round(nbytes / (us * 1e-6) / 1e9, 1)}
     del stack
     return out
+
+
+def prerouted_step(w, xs, nl, pools, routers, ws, seed, K, W, path_flag, rq, synth, torch) -> dict:
+    """Prediction as routing: layer 0 runs its router; every later layer runs its
+    experts (moe_experts_from_logits) on the logits that the previous layer's
+    prerouter head predicted one token earlier. Each layer but the last then runs
+    its head (moe_prerouter_forward, logits only) on the layer input and its own
+    routing at this token and the previous one. No other router runs. Heads are
+    seeded random weights (F = synth.PREROUTER_F). Timed twice, each as HIP
+    graphs (one per parity of the step, for the double-buffered routing): heads
+    in line on the layer stream, then on a second graph branch that waits only
+    for its own layer's expert call."""
+    import numpy as np
+    F, T, k = synth.PREROUTER_F, w.T, w.k
+    heads = []
+    for l in range(nl - 1):
+        d = synth.draw_prerouter(seed, w.wid, l, w.H, w.E, F, w.router_std)
+        heads.append(rq.Prerouter(*(torch.from_numpy(d[n]).cuda() for n in ("w1", "b1", "w2", "b2", "wl"))))
+    # per layer, two generations of the predicted logits and of the routing taken
+    lgs = [[torch.empty((T, w.E), dtype=torch.float32, device="cuda") for _ in range(2)] for _ in range(nl)]
+    idxs = [[torch.empty((T, k), dtype=torch.int32, device="cuda") for _ in range(2)] for _ in range(nl)]
+    gates = [torch.empty((T, k), dtype=torch.float32, device="cuda") for _ in range(nl)]
+    hws = rq.Workspace()
+    hws.get(rq.moe_prerouter_workspace_bytes(T, w.E, F))
+    xbuf = torch.empty_like(xs[0])
+    xbuf.copy_(xs[0])
+    for l in range(nl):  # starting predictions: the router's logits, via a warm-start head
+        for g in range(2):
+            i, _ = rq.moe_route(xs[0], routers[l], k, rq.MOE_FLAG_RENORM)
+            idxs[l][g].copy_(i)
+    for l in range(1, nl):
+        D = w.H + 2 * w.E
+        wl = torch.zeros((w.E, D), dtype=torch.float32, device="cuda")
+        wl[:, :w.H] = routers[l]
+        warm = rq.Prerouter(torch.zeros((F, D), dtype=torch.float32, device="cuda"), None,
+                            torch.zeros((w.E, F), dtype=torch.float32, device="cuda"), None, wl)
+        for g in range(2):
+            rq.moe_prerouter_forward(xs[0], warm, None, None, k, ws=hws, logits_out=lgs[l][g], topk=False)
+    torch.cuda.synchronize()
+    ys = [torch.empty((T, w.H), dtype=torch.float32, device="cuda") for _ in range(nl)]
+    side = torch.cuda.Stream()
+
+    def run(gen, overlap):
+        cur, other = gen % 2, 1 - gen % 2
+        main = torch.cuda.current_stream()
+        for l in range(nl):
+            if l == 0:
+                rq.moe_layer_forward(xbuf, routers[0], pools[0], k, rq.MOE_FLAG_RENORM | path_flag, ws=ws,
+                                     out=ys[0], routing_out=(idxs[0][cur], gates[0]))
+            else:
+                rq.moe_experts_from_logits(xbuf, lgs[l][cur], pools[l], k, rq.MOE_FLAG_RENORM | path_flag, ws=ws,
+                                           out=ys[l], routing_out=(idxs[l][cur], gates[l]))
+            if l + 1 < nl:
+                hs = side if overlap else main
+                if overlap:
+                    side.wait_stream(main)
+                with torch.cuda.stream(hs):
+                    rq.moe_prerouter_forward(xbuf, heads[l], idxs[l][cur], idxs[l][other], k, ws=hws,
+                                             logits_out=lgs[l + 1][other], topk=False, stream=hs)
+        if overlap:
+            main.wait_stream(side)
+
+    for gen in range(2):
+        run(gen, False)
+    torch.cuda.synchronize()
+    nx = xs.shape[0]
+    out = {}
+    for overlap in (False, True):
+        graphs = []
+        for gen in range(2):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run(gen, overlap)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        def step(s):
+            xbuf.copy_(xs[s % nx])
+            graphs[s % 2].replay()
+
+        for s in range(W):
+            step(s)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(K):
+            step(W + s)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        out["overlapped" if overlap else "serial"] = {"us_per_layer": round(ms * 1e3 / (K * nl), 3),
+                                                      "step_tokens_per_s": round(T / (ms * 1e-3 / K), 1)}
+        del graphs
+    # head kernels alone, per launch (eager): stage 1 (fc1 + GELU, residual
+    # path), stage 2 (fc2); the top-k runs inside the next layer's expert call
+    with rq.KernelTimer(rq.MOE_KERNEL_HEAD, 2 * (nl - 1) * 4 + 8) as t:
+        for s in range(4):
+            xbuf.copy_(xs[s % nx])
+            run(s, False)
+    torch.cuda.synchronize()
+    s1_us = float(np.mean(t.ms[0::2])) * 1e3
+    s2_us = float(np.mean(t.ms[1::2])) * 1e3
+    xb = T * w.H * (4 if w.xtype == 0 else 2)
+    H, E = w.H, w.E
+    # algorithmic bytes: stage 1 reads the hidden columns of fc1 and of the
+    # residual path, 2k routed entries per row, biases, x and the routing ids,
+    # and writes fc1's outputs and the partial logits; stage 2 reads fc2,
+    # fc1's outputs and the partials and writes the logits
+    ids = 4 * T * 2 * k
+    s1_bytes = 4 * ((F + E) * H + 2 * k * (F + E) + F + E) + xb + ids + 4 * T * (F + E)
+    s2_bytes = 4 * (E * F + T * F + 2 * T * E)
+    return {"F": F, "layers": nl, "heads": nl - 1, "steps": K, **out,
+            "head_kernel_us": {"stage1_fc1_residual": round(s1_us, 3), "stage2_fc2": round(s2_us, 3)},
+            "head_bytes": {"stage1_fc1_residual": s1_bytes, "stage2_fc2": s2_bytes},
+            "head_gbps": {"stage1_fc1_residual": round(s1_bytes / (s1_us * 1e-6) / 1e9, 1),
+                          "stage2_fc2": round(s2_bytes / (s2_us * 1e-6) / 1e9, 1)}}
 
 
 def stream_ceiling(nbytes: int, rq, torch) -> dict:
@@ -373,6 +490,11 @@ def main():
 
     ceiling = stream_ceiling(int(round(routed_bytes)), rq, torch)
     miss = miss_policies(w, [xs[i] for i in range(nx)], routers[0], pools[0], rq, torch) if w.T <= 64 else None
+    pre = None
+    if w.T <= 64 and not args.no_prerouter:
+        log("prerouted step ...")
+        pre = prerouted_step(w, xs, nl, pools, routers, ws, args.seed, K, W, path_flag, rq, synth, torch)
+        pre["routed_us_per_layer"] = round(t_layer_s * 1e6, 3)
 
     traffic = None
     tf = os.path.join(ROOT, "profiles", f"traffic_{dom}_{w.name}.json")
@@ -409,6 +531,7 @@ def main():
         "routed_hbm_frac": round(routed_gbps / HBM_PEAK_GBPS, 4),
         "stream_read_ceiling": {**ceiling, "layer_vs_ceiling": round(routed_gbps / ceiling["gbps"], 4)},
         **({"miss_policies": miss} if miss else {}),
+        **({"prerouted": pre} if pre else {}),
         "kernel_us": {n: round(v, 3) for n, v in kern_us.items()},
         "roofline": {"kernel": kname, "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -149,6 +149,19 @@ moe_status moe_layer_forward(const void* x, int32_t xtype, int32_t T, const floa
                              int32_t* topk_idx_out, float* topk_gate_out,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* The expert layer from given router logits: moe_layer_forward after its gate
+ * linear, for logits that come from elsewhere, such as moe_prerouter_forward
+ * predicting this layer's routing (prediction as routing: "The Other Half of the
+ * Memory Wall: Serving 35B MoEs from SSD with Trained Routing Prediction"
+ * (xyznot.com), section 主なアイデア). The softmax and top-k run on `logits`
+ * ([T][E] fp32, DEVICE, 16-byte aligned) exactly as moe_route's, then the routed
+ * experts as moe_gather_qmm_forward's. For one token the top-k runs inside the
+ * gate/up kernel. Other arguments and errors as moe_layer_forward's. */
+moe_status moe_experts_from_logits(const void* x, int32_t xtype, int32_t T, const float* logits,
+                                   const moe_experts* ex, int32_t k, uint32_t flags, float* y,
+                                   int32_t* topk_idx_out, float* topk_gate_out,
+                                   void* ws, size_t ws_bytes, void* stream);
+
 /* Block quantiser for the codecs above [QK §6]: w [rows][K] fp32 to codes and
  * scales. Per block of 32: s = binary16(amax / qmax), with the division in
  * fp32, rounded to nearest even and saturated at the largest finite value;
@@ -178,7 +191,8 @@ enum {
   MOE_KERNEL_GEMM_GATE_UP = 6,  /* grouped MFMA GEMM, gate/up + SwiGLU */
   MOE_KERNEL_GEMM_DOWN = 7,     /* grouped MFMA GEMM, down */
   MOE_KERNEL_QUANTIZE = 8,      /* block quantiser */
-  MOE_KERNEL_COUNT = 9
+  MOE_KERNEL_HEAD = 9,          /* prerouter head rows (fc1 + GELU; fc2 + residual path) */
+  MOE_KERNEL_COUNT = 10
 };
 moe_status moe_timer_start(int32_t kernel, int32_t capacity);
 moe_status moe_timer_read(float* ms, int32_t capacity, int32_t* count);
@@ -238,6 +252,57 @@ moe_status moe_stage_experts(const moe_experts* pool, const moe_experts* stack, 
                              const int32_t* slots, int32_t n, void* stream);
 moe_status moe_remap_ids(const int32_t* idx, int64_t n, const int32_t* slot_of, int32_t E, int32_t* out,
                          void* stream);
+
+/* Prerouter head, run at one layer to give the next layer's routing for the
+ * next token. "The Other Half of the Memory Wall: Serving 35B MoEs from SSD with
+ * Trained Routing Prediction" (xyznot.com), section 手法 (method), "Prerouterヘッド
+ * のアーキテクチャ" (prerouter head architecture): the input is the hidden state
+ * joined with the top-k one-hot routing vectors of the current and the previous
+ * token, H + 2E values, and the head is fc2(erf-gelu(fc1(input))) plus a linear
+ * residual path warm-started from the next layer's router. Section 主なアイデア
+ * (main ideas), prediction as routing: the head's top-k is used as the routing.
+ *
+ * Per token t, with f = [x_t ; khot(cur_t) ; khot(prev_t)] (khot(ids): 1 at each of
+ * the k ids, 0 elsewhere; all 0 for a NULL array):
+ *   a = gelu(w1 f + b1), gelu(z) = z/2 * (1 + erf(z / sqrt 2))   (F values, fp32)
+ *   logits_t = w2 a + b2 + wl f                                   (E values, fp32)
+ * then moe_route's softmax and top-k on logits_t.
+ * Weights, DEVICE fp32 arrays in this layout (16-byte aligned; b1, b2 may be NULL
+ * for no bias):
+ *   w1 [F][H+2E], b1 [F], w2 [E][F], b2 [E], wl [E][H+2E] (no bias; at warm start
+ *   its first H columns are the next layer's router weights).
+ * Limits: H and F multiples of 32 in [32, 4096]; E even, in [2, 1024]; k as for
+ * moe_route, and the k of cur/prev equals the output k. */
+typedef struct moe_prerouter {
+  int32_t H, E, F;
+  const float* w1;
+  const float* b1;
+  const float* w2;
+  const float* b2;
+  const float* wl;
+} moe_prerouter;
+
+/* Workspace for moe_prerouter_forward: fc1 activations [T][F], residual-path
+ * partial sums and head logits [T][E] each (fp32). Returns 0 for sizes outside
+ * the limits. */
+size_t moe_prerouter_workspace_bytes(int32_t T, int32_t E, int32_t F);
+
+/*   x:          [T][H] activations of type xtype (16-byte aligned).
+ *   cur, prev:  [T][k] int32 routed ids of the current and previous token, or
+ *               NULL (a zero vector, e.g. the first token). Ids must lie in
+ *               [0, E) and be distinct per token, as moe_route produces them;
+ *               they are not checked on the device.
+ *   topk_idx, topk_gate: out [T][k], as moe_route's (flags: MOE_FLAG_RENORM);
+ *               both NULL to skip the top-k (logits must then be given, e.g.
+ *               for moe_experts_from_logits, which runs the top-k itself).
+ *   logits:     out [T][E] fp32 head logits (16-byte aligned), or NULL.
+ * Errors: MOE_ERR_INVALID_ARG for NULL or misaligned pointers and sizes outside
+ * the limits; MOE_ERR_UNSUPPORTED for an unknown xtype or flag;
+ * MOE_ERR_WORKSPACE, MOE_ERR_HIP as elsewhere. */
+moe_status moe_prerouter_forward(const void* x, int32_t xtype, int32_t T, const moe_prerouter* head,
+                                 const int32_t* cur, const int32_t* prev, int32_t k, uint32_t flags,
+                                 int32_t* topk_idx, float* topk_gate, float* logits, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* Benchmark support: the achievable-bandwidth reference. Reads `bytes` bytes
  * (a positive multiple of 16) of the device buffer `buf` once, with coalesced

@@ -7,7 +7,7 @@ kernels. There is no fallback: if libmoe.so is missing or the GPU is absent,
 the calls raise.
 
 Entry points mirror the C names: moe_route, moe_group, moe_gather_qmm_forward,
-moe_layer_forward, moe_quantize, moe_workspace_bytes.
+moe_layer_forward, moe_quantize, moe_workspace_bytes, moe_prerouter_forward.
 """
 from __future__ import annotations
 
@@ -28,10 +28,12 @@ MOE_FLAG_RENORM, MOE_FLAG_PATH_GATHER, MOE_FLAG_PATH_GEMM = 1, 2, 4
 # Every function the header declares; the library must export all of them.
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_group", "moe_gather_qmm_forward", "moe_layer_forward",
            "moe_quantize", "moe_timer_start", "moe_timer_read", "moe_stream_read", "moe_miss_replay",
-           "moe_stage_experts", "moe_remap_ids", "moe_status_str", "moe_last_error")
+           "moe_stage_experts", "moe_remap_ids", "moe_prerouter_workspace_bytes", "moe_prerouter_forward",
+           "moe_experts_from_logits",
+           "moe_status_str", "moe_last_error")
 
 (MOE_KERNEL_ROUTE_LOGITS, MOE_KERNEL_TOPK, MOE_KERNEL_GROUP, MOE_KERNEL_GATE_UP, MOE_KERNEL_DOWN, MOE_KERNEL_COMBINE,
- MOE_KERNEL_GEMM_GATE_UP, MOE_KERNEL_GEMM_DOWN, MOE_KERNEL_QUANTIZE) = range(9)
+ MOE_KERNEL_GEMM_GATE_UP, MOE_KERNEL_GEMM_DOWN, MOE_KERNEL_QUANTIZE, MOE_KERNEL_HEAD) = range(10)
 
 
 class MoeError(RuntimeError):
@@ -44,6 +46,12 @@ class _Experts(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("scheme", ctypes.c_int32),
                 ("w_gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
                 ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+
+
+class _Prerouter(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("E", ctypes.c_int32), ("F", ctypes.c_int32),
+                ("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p), ("wl", ctypes.c_void_p)]
 
 
 _lib = None
@@ -72,6 +80,10 @@ def lib() -> ctypes.CDLL:
             "moe_remap_ids": ([P, I64, P, I32, P, P], ctypes.c_int),
             "moe_miss_replay": ([P, P, I32, I32, I32, I32, I32, ctypes.c_float, ctypes.c_float, P, P, P, P],
                                 ctypes.c_int),
+            "moe_prerouter_workspace_bytes": ([I32, I32, I32], SZ),
+            "moe_prerouter_forward": ([P, I32, I32, ctypes.POINTER(_Prerouter), P, P, I32, U32, P, P, P, P, SZ, P],
+                                      ctypes.c_int),
+            "moe_experts_from_logits": ([P, I32, I32, P, E, I32, U32, P, P, P, P, SZ, P], ctypes.c_int),
             "moe_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "moe_last_error": ([], ctypes.c_char_p),
         }
@@ -239,6 +251,106 @@ def moe_stream_read(buf: torch.Tensor, nbytes: int | None = None, stream=None) -
     _check("moe_stream_read", lib().moe_stream_read(_p(buf), n, _stream(stream)))
 
 
+@dataclass
+class Prerouter:
+    """Prerouter head weights on the device, fp32 (layout in include/moe.h):
+    w1 [F][H+2E], b1 [F] or None, w2 [E][F], b2 [E] or None, wl [E][H+2E]."""
+    w1: torch.Tensor
+    b1: torch.Tensor | None
+    w2: torch.Tensor
+    b2: torch.Tensor | None
+    wl: torch.Tensor
+
+    @property
+    def E(self) -> int:
+        return self.w2.shape[0]
+
+    @property
+    def F(self) -> int:
+        return self.w1.shape[0]
+
+    @property
+    def H(self) -> int:
+        return self.w1.shape[1] - 2 * self.E
+
+    def c(self) -> _Prerouter:
+        for n in ("w1", "b1", "w2", "b2", "wl"):
+            t = getattr(self, n)
+            if t is not None:
+                _device_tensor(t, n)
+                if t.dtype != torch.float32:
+                    raise ValueError(f"{n} must be float32")
+        ptr = lambda t: None if t is None else t.data_ptr()
+        return _Prerouter(self.H, self.E, self.F, ptr(self.w1), ptr(self.b1), ptr(self.w2), ptr(self.b2),
+                          ptr(self.wl))
+
+
+def moe_prerouter_workspace_bytes(T: int, E: int, F: int) -> int:
+    return int(lib().moe_prerouter_workspace_bytes(T, E, F))
+
+
+def moe_prerouter_forward(x: torch.Tensor, head: Prerouter, cur: torch.Tensor | None, prev: torch.Tensor | None,
+                          k: int, flags: int = MOE_FLAG_RENORM, want_logits: bool = False,
+                          ws: Workspace | None = None, stream=None, out=None, logits_out: torch.Tensor | None = None,
+                          topk: bool = True):
+    """Prerouter head: the next layer's routing for the next token.
+    Returns (topk_idx int32 [T][k], topk_gate fp32 [T][k]) and, with want_logits,
+    also the head logits fp32 [T][E]. `out` may pass (idx, gate) tensors to fill,
+    `logits_out` a [T][E] fp32 tensor. With topk=False only the logits are made
+    (returned alone; for moe_experts_from_logits)."""
+    _device_tensor(x, "x")
+    T = x.shape[0]
+    for n, t in (("cur", cur), ("prev", prev)):
+        if t is not None:
+            _device_tensor(t, n)
+            if t.dtype != torch.int32 or t.shape != (T, k):
+                raise ValueError(f"{n} must be int32 [T][k]")
+    if not topk:
+        idx = gate = None
+        want_logits = True
+    elif out is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        gate = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    else:
+        idx, gate = out
+    lg = logits_out
+    if lg is None and want_logits:
+        lg = torch.empty((T, head.E), dtype=torch.float32, device=x.device)
+    hc = head.c()
+    nb = moe_prerouter_workspace_bytes(T, head.E, head.F)
+    w = _ws(ws, nb, x.device)
+    _check("moe_prerouter_forward",
+           lib().moe_prerouter_forward(_p(x), _xtype(x), T, ctypes.byref(hc), _p(cur), _p(prev), k, flags, _p(idx),
+                                       _p(gate), _p(lg), _p(w), w.numel(), _stream(stream)))
+    if not topk:
+        return lg
+    return (idx, gate, lg) if want_logits else (idx, gate)
+
+
+def moe_experts_from_logits(x: torch.Tensor, logits: torch.Tensor, ex: "Experts", k: int,
+                            flags: int = MOE_FLAG_RENORM, ws: Workspace | None = None, stream=None,
+                            out: torch.Tensor | None = None, return_routing: bool = False, routing_out=None):
+    """Expert layer on given router logits [T][E] fp32 (top-k, then the routed experts).
+    Returns y [T][H] (and topk_idx, topk_gate with return_routing). routing_out
+    may pass (idx, gate) tensors that receive the routing."""
+    _device_tensor(x, "x")
+    _device_tensor(logits, "logits")
+    T = x.shape[0]
+    y = out if out is not None else torch.empty((T, ex.H), dtype=torch.float32, device=x.device)
+    if routing_out is not None:
+        idx, gate = routing_out
+    else:
+        idx = torch.empty((T, k), dtype=torch.int32, device=x.device) if return_routing else None
+        gate = torch.empty((T, k), dtype=torch.float32, device=x.device) if return_routing else None
+    nb = moe_workspace_bytes(T, ex.E, ex.H, ex.I, k, ex.scheme)
+    w = _ws(ws, nb, x.device)
+    c = ex.c()
+    _check("moe_experts_from_logits",
+           lib().moe_experts_from_logits(_p(x), _xtype(x), T, _p(logits), ctypes.byref(c), k, flags, _p(y), _p(idx),
+                                         _p(gate), _p(w), w.numel(), _stream(stream)))
+    return (y, idx, gate) if return_routing else y
+
+
 def moe_route(x: torch.Tensor, router_w: torch.Tensor, k: int, flags: int = MOE_FLAG_RENORM,
               ws: Workspace | None = None, stream=None):
     """Router: returns (topk_idx int32 [T][k], topk_gate fp32 [T][k])."""
@@ -291,14 +403,17 @@ def moe_gather_qmm_forward(x: torch.Tensor, ex: Experts, topk_idx: torch.Tensor,
 
 def moe_layer_forward(x: torch.Tensor, router_w: torch.Tensor, ex: Experts, k: int, flags: int = MOE_FLAG_RENORM,
                       ws: Workspace | None = None, stream=None, out: torch.Tensor | None = None,
-                      return_routing: bool = True):
-    """Router + routed-only experts. Returns y [T][H] (and topk_idx, topk_gate)."""
+                      return_routing: bool = True, routing_out=None):
+    """Router + routed-only experts. Returns y [T][H] (and topk_idx, topk_gate).
+    routing_out may pass (idx, gate) tensors that receive the routing."""
     _device_tensor(x, "x")
     _device_tensor(router_w, "router_w")
     T = x.shape[0]
     y = out if out is not None else torch.empty((T, ex.H), dtype=torch.float32, device=x.device)
     idx = gate = None
-    if return_routing:
+    if routing_out is not None:
+        idx, gate = routing_out
+    elif return_routing:
         idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
         gate = torch.empty((T, k), dtype=torch.float32, device=x.device)
     nb = moe_workspace_bytes(T, ex.E, ex.H, ex.I, k, ex.scheme)

@@ -105,6 +105,22 @@ hipError_t launch_combine(int T, int H, int k, const float* gate, const float* y
 hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev& ex, int k, const GroupBufs& g,
                                const float* gate, uint16_t* h16, uint16_t* x16, float* ys, float* y, hipStream_t s);
 
+// Prerouter head weights as the kernels see them (fp32, the page's layout:
+// w1 [F][H+2E], b1 [F] or null, w2 [E][F], b2 [E] or null, wl [E][H+2E]).
+struct HeadDev {
+  int H, E, F;
+  const float* w1;
+  const float* b1;
+  const float* w2;
+  const float* b2;
+  const float* wl;
+};
+// fc1 + GELU into act [T][F] and the residual path + fc2's bias into part
+// [T][E]; then part + fc2 into logits [T][E] and the router's top-k into
+// idx/gate [T][k]. cur/prev [T][k] or null.
+hipError_t launch_prerouter(const void* x, int xtype, int T, const HeadDev& hd, const int32_t* cur,
+                            const int32_t* prev, int k, int renorm, float* act, float* part, float* logits,
+                            int32_t* idx, float* gate, hipStream_t s);
 hipError_t launch_quantize(const float* w, int64_t rows, int K, int scheme, uint8_t* codes, uint16_t* scales,
                            hipStream_t s);
 

@@ -170,6 +170,41 @@ bool timer_take(int kid, hipEvent_t* start, hipEvent_t* stop) {
 }
 }  // namespace moe
 
+namespace {
+// The expert layer after the router's gate linear: top-k on `logits` ([nsplit]
+// partial planes of [T][E]), then the routed experts.
+moe_status layer_from_logits(const void* x, int32_t xtype, int32_t T, const moe::ExpertsDev& d, int32_t k,
+                             uint32_t flags, const float* logits, int nsplit, float* y, int32_t* topk_idx_out,
+                             float* topk_gate_out, void* ws, const Layout& L, hipStream_t s) {
+  const int renorm = (flags & MOE_FLAG_RENORM) ? 1 : 0;
+  int32_t* idx = at<int32_t>(ws, L.idx);
+  float* gate = at<float>(ws, L.gate);
+  if (T == 1 && !(flags & MOE_FLAG_PATH_GEMM))
+    return hip_status(moe::launch_decode_t1(x, xtype, d, k, renorm, logits, nullptr, nullptr, idx, gate,
+                                            topk_idx_out, topk_gate_out, at<float>(ws, L.h), y, s),
+                      "decode (one token)");
+  hipError_t e = moe::launch_topk(logits, nsplit, T, d.E, k, renorm, idx, gate, topk_idx_out, topk_gate_out, s);
+  if (e != hipSuccess) return hip_status(e, "top-k");
+  return run_experts(x, xtype, T, d, k, idx, gate, y, flags, ws, L, s);
+}
+
+moe_status check_layer_args(const void* x, int32_t xtype, int32_t T, const moe_experts* ex, int32_t k, uint32_t flags,
+                            const float* y, void* ws, size_t ws_bytes, moe::ExpertsDev* d, Layout* L) {
+  moe_status st;
+  if ((st = check_x(x, xtype))) return st;
+  if ((st = check_experts(ex, d))) return st;
+  if ((st = check_shape(T, d->E, d->H, d->I, k))) return st;
+  if (!y) return fail(MOE_ERR_INVALID_ARG, "y is NULL");
+  if (!aligned(y, 16)) return fail(MOE_ERR_INVALID_ARG, "y is not 16-byte aligned");
+  if ((flags & MOE_FLAG_PATH_GATHER) && (flags & MOE_FLAG_PATH_GEMM))
+    return fail(MOE_ERR_INVALID_ARG, "both path flags are set");
+  if (flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_PATH_GATHER | MOE_FLAG_PATH_GEMM))
+    return fail(MOE_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  *L = layout(T, d->E, d->H, d->I, k);
+  return check_ws(ws, ws_bytes, *L);
+}
+}  // namespace
+
 extern "C" {
 
 moe_status moe_timer_start(int32_t kernel, int32_t capacity) {
@@ -272,34 +307,30 @@ moe_status moe_layer_forward(const void* x, int32_t xtype, int32_t T, const floa
                              void* ws, size_t ws_bytes, void* stream) {
   moe_status st;
   moe::ExpertsDev d;
-  if ((st = check_x(x, xtype))) return st;
-  if ((st = check_experts(ex, &d))) return st;
-  if ((st = check_shape(T, d.E, d.H, d.I, k))) return st;
-  if (!router_w || !y) return fail(MOE_ERR_INVALID_ARG, "router_w or y is NULL");
-  if (!aligned(router_w, 16) || !aligned(y, 16))
-    return fail(MOE_ERR_INVALID_ARG, "router_w and y must be 16-byte aligned");
-  if ((flags & MOE_FLAG_PATH_GATHER) && (flags & MOE_FLAG_PATH_GEMM))
-    return fail(MOE_ERR_INVALID_ARG, "both path flags are set");
-  if (flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_PATH_GATHER | MOE_FLAG_PATH_GEMM))
-    return fail(MOE_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
-  const Layout L = layout(T, d.E, d.H, d.I, k);
-  if ((st = check_ws(ws, ws_bytes, L))) return st;
+  Layout L;
+  if ((st = check_layer_args(x, xtype, T, ex, k, flags, y, ws, ws_bytes, &d, &L))) return st;
+  if (!router_w) return fail(MOE_ERR_INVALID_ARG, "router_w is NULL");
+  if (!aligned(router_w, 16)) return fail(MOE_ERR_INVALID_ARG, "router_w is not 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int renorm = (flags & MOE_FLAG_RENORM) ? 1 : 0;
   float* logits = at<float>(ws, L.logits);
-  int32_t* idx = at<int32_t>(ws, L.idx);
-  float* gate = at<float>(ws, L.gate);
   int nsplit = 1;
   hipError_t e = moe::launch_logits(x, xtype, T, d.H, router_w, d.E, logits, &nsplit,
                                     T >= moe::kSplitRouterMinT ? at<uint16_t>(ws, L.r3) : nullptr, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
-  if (T == 1 && !(flags & MOE_FLAG_PATH_GEMM))
-    return hip_status(moe::launch_decode_t1(x, xtype, d, k, renorm, logits, nullptr, nullptr, idx, gate,
-                                            topk_idx_out, topk_gate_out, at<float>(ws, L.h), y, s),
-                      "decode (one token)");
-  e = moe::launch_topk(logits, nsplit, T, d.E, k, renorm, idx, gate, topk_idx_out, topk_gate_out, s);
-  if (e != hipSuccess) return hip_status(e, "top-k");
-  return run_experts(x, xtype, T, d, k, idx, gate, y, flags, ws, L, s);
+  return layer_from_logits(x, xtype, T, d, k, flags, logits, nsplit, y, topk_idx_out, topk_gate_out, ws, L, s);
+}
+
+moe_status moe_experts_from_logits(const void* x, int32_t xtype, int32_t T, const float* logits,
+                                   const moe_experts* ex, int32_t k, uint32_t flags, float* y, int32_t* topk_idx_out,
+                                   float* topk_gate_out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st;
+  moe::ExpertsDev d;
+  Layout L;
+  if ((st = check_layer_args(x, xtype, T, ex, k, flags, y, ws, ws_bytes, &d, &L))) return st;
+  if (!logits) return fail(MOE_ERR_INVALID_ARG, "logits is NULL");
+  if (!aligned(logits, 16)) return fail(MOE_ERR_INVALID_ARG, "logits is not 16-byte aligned");
+  return layer_from_logits(x, xtype, T, d, k, flags, logits, 1, y, topk_idx_out, topk_gate_out, ws, L,
+                           static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_quantize(const float* w, int64_t rows, int32_t K, int32_t scheme, void* codes, uint16_t* scales,
@@ -360,6 +391,54 @@ moe_status moe_remap_ids(const int32_t* idx, int64_t n, const int32_t* slot_of, 
   if (n < 0 || E < 1) return fail(MOE_ERR_INVALID_ARG, "n=%lld E=%d", (long long)n, E);
   if (n > 0 && (!idx || !slot_of || !out)) return fail(MOE_ERR_INVALID_ARG, "idx, slot_of or out is NULL");
   return hip_status(moe::launch_remap_ids(idx, n, slot_of, out, static_cast<hipStream_t>(stream)), "remap ids");
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static bool head_shape_ok(int64_t T, int64_t E, int64_t F) {
+  return T >= 1 && T <= 65536 && E >= 2 && E <= moe::kMaxE && E % 2 == 0 && F >= 32 && F <= 4096 && F % 32 == 0;
+}
+
+size_t moe_prerouter_workspace_bytes(int32_t T, int32_t E, int32_t F) {
+  if (!head_shape_ok(T, E, F)) return 0;
+  // fc1 activations [T][F], residual-path partials [T][E], logits [T][E]
+  return align256((size_t)T * F * 4) + 2 * align256((size_t)T * E * 4);
+}
+
+moe_status moe_prerouter_forward(const void* x, int32_t xtype, int32_t T, const moe_prerouter* head,
+                                 const int32_t* cur, const int32_t* prev, int32_t k, uint32_t flags,
+                                 int32_t* topk_idx, float* topk_gate, float* logits, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  moe_status st;
+  if ((st = check_x(x, xtype))) return st;
+  if (!head) return fail(MOE_ERR_INVALID_ARG, "prerouter struct is NULL");
+  const int64_t H = head->H, E = head->E, F = head->F;
+  if ((st = check_shape(T, E, H, 32, k))) return st;
+  if (E < 2 || E % 2) return fail(MOE_ERR_INVALID_ARG, "E=%lld must be even and >= 2 for the prerouter", (long long)E);
+  if (F < 32 || F > 4096 || F % 32)
+    return fail(MOE_ERR_INVALID_ARG, "F=%lld must be a multiple of 32 in [32, 4096]", (long long)F);
+  if (!head->w1 || !head->w2 || !head->wl) return fail(MOE_ERR_INVALID_ARG, "w1, w2 or wl is NULL");
+  if (!aligned(head->w1, 16) || !aligned(head->w2, 16) || !aligned(head->wl, 16) ||
+      (head->b1 && !aligned(head->b1, 4)) || (head->b2 && !aligned(head->b2, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "head weights must be 16-byte aligned and biases 4-byte aligned");
+  if ((cur && !aligned(cur, 4)) || (prev && !aligned(prev, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "cur or prev is not 4-byte aligned");
+  if (!topk_idx != !topk_gate) return fail(MOE_ERR_INVALID_ARG, "only one of topk_idx and topk_gate is NULL");
+  if (!topk_idx && !logits) return fail(MOE_ERR_INVALID_ARG, "topk_idx, topk_gate and logits are all NULL");
+  if (logits && !aligned(logits, 16)) return fail(MOE_ERR_INVALID_ARG, "logits is not 16-byte aligned");
+  if (flags & ~(uint32_t)MOE_FLAG_RENORM) return fail(MOE_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace pointer is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  const size_t need = moe_prerouter_workspace_bytes(T, (int32_t)E, (int32_t)F);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  const size_t o_part = align256((size_t)T * F * 4), o_lg = o_part + align256((size_t)T * E * 4);
+  float* act = at<float>(ws, 0);
+  float* part = at<float>(ws, o_part);
+  float* lg = logits ? logits : at<float>(ws, o_lg);
+  const moe::HeadDev hd{(int)H, (int)E, (int)F, head->w1, head->b1, head->w2, head->b2, head->wl};
+  return hip_status(moe::launch_prerouter(x, xtype, T, hd, cur, prev, k, (flags & MOE_FLAG_RENORM) ? 1 : 0, act, part,
+                                          lg, topk_idx, topk_gate, static_cast<hipStream_t>(stream)),
+                    "prerouter head");
 }
 
 moe_status moe_stream_read(const void* buf, int64_t bytes, void* stream) {

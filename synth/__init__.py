@@ -191,6 +191,35 @@ def redraw_tokens(x32: np.ndarray, tokens, seed: int, workload: int, layer: int,
             x32[t, -1] = 1.0
 
 
+def draw_routing(g: np.random.Generator, T: int, E: int, k: int) -> np.ndarray:
+    """[T][k] int32 expert ids, distinct within each token, uniform."""
+    return np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32).reshape(T, k)
+
+
+# Prerouter head width (fc1 outputs). The pages give the input width (H + 2E)
+# but not this one; the measured head takes F = E.
+PREROUTER_F = 256
+
+
+def draw_prerouter(seed: int, workload: int, layer: int, H: int, E: int, F: int, router_std: float,
+                   bias: bool = True) -> dict:
+    """fp32 prerouter head weights in the layout [F][H+2E] (fc1), [E][F] (fc2),
+    [E][H+2E] (linear residual path). The residual path's hidden columns are a
+    router draw (the warm start from the next layer's router); the rest are
+    Gaussian, scaled by fan-in. Biases are None when bias is False."""
+    g = rng(seed, workload, layer, 0, 2000)
+    D = H + 2 * E
+    std1 = np.float32(1.0 / np.sqrt(D))
+    w1 = (g.standard_normal((F, D), dtype=np.float32) * std1).astype(np.float32)
+    b1 = (g.standard_normal(F, dtype=np.float32) * np.float32(0.1)).astype(np.float32) if bias else None
+    w2 = (g.standard_normal((E, F), dtype=np.float32) * np.float32(0.5 / np.sqrt(F))).astype(np.float32)
+    b2 = (g.standard_normal(E, dtype=np.float32) * np.float32(0.1)).astype(np.float32) if bias else None
+    wl = np.empty((E, D), dtype=np.float32)
+    wl[:, :H] = draw_router(g, E, H, router_std)
+    wl[:, H:] = g.standard_normal((E, 2 * E), dtype=np.float32) * np.float32(0.5)
+    return {"w1": w1, "b1": b1, "w2": w2, "b2": b2, "wl": wl}
+
+
 def draw_step_x(w: Workload, seed: int, step: int, T: int | None = None) -> np.ndarray:
     """Activations of one decode/prefill step, with the workload's structure
     (constant channel under a popularity skew, token reuse), encoded."""

@@ -139,3 +139,64 @@ def test_stage_and_remap_validation(L):
     assert L.moe_stage_experts(ctypes.byref(pool), ctypes.byref(pool), FAKE, FAKE, -1, None) == rq.MOE_ERR_INVALID_ARG
     assert L.moe_remap_ids(None, 4, FAKE, 8, FAKE, None) == rq.MOE_ERR_INVALID_ARG
     assert L.moe_remap_ids(FAKE, -1, FAKE, 8, FAKE, None) == rq.MOE_ERR_INVALID_ARG
+
+
+def test_prerouter_workspace_and_validation(L):
+    n1 = L.moe_prerouter_workspace_bytes(1, 256, 256)
+    n64 = L.moe_prerouter_workspace_bytes(64, 256, 512)
+    assert n1 >= 256 * 4 * 2 and n64 >= 64 * (256 + 512) * 4 and n1 % 256 == 0
+    for bad in [(0, 256, 256), (1, 255, 256), (1, 2048, 256), (1, 256, 100), (1, 256, 8192), (1, 0, 256)]:
+        assert L.moe_prerouter_workspace_bytes(*bad) == 0, bad
+
+    def head(H=2048, E=256, F=256, w1=FAKE, w2=FAKE, wl=FAKE, b1=None, b2=None):
+        v = lambda p: None if p is None else p.value
+        return rq._Prerouter(H, E, F, v(w1), v(b1), v(w2), v(b2), v(wl))
+
+    def call(x=FAKE, xt=rq.MOE_BF16, T=1, hd="default", cur=FAKE, prev=FAKE, k=8, flags=1, idx=FAKE, gate=FAKE,
+             lg=None, ws=FAKE, nws=1 << 30):
+        hd = head() if hd == "default" else hd
+        return L.moe_prerouter_forward(x, xt, T, ctypes.byref(hd) if hd is not None else None, cur, prev, k, flags,
+                                       idx, gate, lg, ws, nws, None)
+
+    assert call(x=None) == rq.MOE_ERR_INVALID_ARG
+    assert call(xt=5) == rq.MOE_ERR_UNSUPPORTED
+    assert call(hd=None) == rq.MOE_ERR_INVALID_ARG
+    assert call(T=0) == rq.MOE_ERR_INVALID_ARG
+    assert call(hd=head(E=255), k=8) == rq.MOE_ERR_INVALID_ARG
+    assert b"even" in L.moe_last_error()
+    assert call(hd=head(E=2048)) == rq.MOE_ERR_INVALID_ARG
+    assert call(hd=head(H=2050)) == rq.MOE_ERR_INVALID_ARG
+    assert call(hd=head(F=100)) == rq.MOE_ERR_INVALID_ARG
+    assert call(hd=head(F=8192)) == rq.MOE_ERR_INVALID_ARG
+    assert call(k=17) == rq.MOE_ERR_INVALID_ARG
+    assert call(hd=head(w1=None)) == rq.MOE_ERR_INVALID_ARG
+    assert call(hd=head(wl=ctypes.c_void_p(0x10008))) == rq.MOE_ERR_INVALID_ARG
+    assert call(hd=head(b1=ctypes.c_void_p(0x10002))) == rq.MOE_ERR_INVALID_ARG
+    assert call(cur=ctypes.c_void_p(0x10002)) == rq.MOE_ERR_INVALID_ARG
+    assert call(idx=None) == rq.MOE_ERR_INVALID_ARG
+    assert call(flags=2) == rq.MOE_ERR_UNSUPPORTED
+    assert call(ws=None) == rq.MOE_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x10010)) == rq.MOE_ERR_WORKSPACE
+    assert call(nws=1024) == rq.MOE_ERR_WORKSPACE
+    assert b"needed" in L.moe_last_error()
+    assert call(idx=None, gate=None) == rq.MOE_ERR_INVALID_ARG     # nothing to write
+    assert call(lg=ctypes.c_void_p(0x10008)) == rq.MOE_ERR_INVALID_ARG
+
+
+def test_experts_from_logits_validation(L):
+    ex = _experts()
+
+    def call(x=FAKE, xt=rq.MOE_F16, T=1, lg=FAKE, e=ex, k=8, flags=1, y=FAKE, ws=FAKE, nws=1 << 30):
+        return L.moe_experts_from_logits(x, xt, T, lg, ctypes.byref(e) if e is not None else None, k, flags, y,
+                                         None, None, ws, nws, None)
+
+    assert call(lg=None) == rq.MOE_ERR_INVALID_ARG
+    assert b"logits" in L.moe_last_error()
+    assert call(lg=ctypes.c_void_p(0x10004)) == rq.MOE_ERR_INVALID_ARG
+    assert call(x=None) == rq.MOE_ERR_INVALID_ARG
+    assert call(e=None) == rq.MOE_ERR_INVALID_ARG
+    assert call(y=None) == rq.MOE_ERR_INVALID_ARG
+    assert call(k=0) == rq.MOE_ERR_INVALID_ARG
+    assert call(flags=rq.MOE_FLAG_PATH_GATHER | rq.MOE_FLAG_PATH_GEMM) == rq.MOE_ERR_INVALID_ARG
+    assert call(flags=0x40) == rq.MOE_ERR_UNSUPPORTED
+    assert call(nws=16) == rq.MOE_ERR_WORKSPACE
