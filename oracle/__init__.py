@@ -79,6 +79,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "oref_logits": ([P, I32, I32, I32, P, I32, P], ctypes.c_int),
         "oref_route": ([P, I32, I32, I32, P, I32, I32, U32, P, P], ctypes.c_int),
         "oref_group": ([P, I32, I32, I32, P, P, P, P, P], ctypes.c_int),
+        "oref_qlinear_lora": ([P, I32, I32, I32, I32, I32, P, P, P, P, I32, ctypes.c_double, P], ctypes.c_int),
         "oref_prerouter": ([P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, I32, U32, P, P, P], ctypes.c_int),
         "oref_gather_forward": ([P, I32, I32, ctypes.POINTER(_Experts), I32, P, P, P], ctypes.c_int),
         "oref_layer_forward": ([P, I32, I32, P, ctypes.POINTER(_Experts), I32, U32, P, P, P], ctypes.c_int),
@@ -239,6 +240,26 @@ def prerouter(x: np.ndarray, head: PrerouterHead, cur: np.ndarray | None, prev: 
                                 _ptr(wl), _ptr(cur), _ptr(prev), k, flags, _ptr(idx), _ptr(gate), _ptr(lg)),
            "oref_prerouter")
     return idx, gate, lg
+
+
+def qlinear_lora(x: np.ndarray, codes: np.ndarray, scales: np.ndarray, scheme: int, A: np.ndarray | None,
+                 B: np.ndarray | None, scale: float, bf16: bool = False) -> np.ndarray:
+    """y = W_q x + scale * B (A x) [MW "非マージアダプターの実行"]: codes/scales of W_q
+    [N][K] in the block format, A [r][K], B [N][r] fp32 (None for r = 0). Returns y [T][N] fp32."""
+    x = np.ascontiguousarray(x)
+    T, K = x.shape
+    N = scales.shape[0]
+    assert scales.shape == (N, K // 32)
+    r = 0 if A is None else A.shape[0]
+    if r:
+        A = np.ascontiguousarray(A, dtype=np.float32)
+        B = np.ascontiguousarray(B, dtype=np.float32)
+        assert A.shape == (r, K) and B.shape == (N, r)
+    y = np.empty((T, N), dtype=np.float32)
+    _check(lib().oref_qlinear_lora(_ptr(x), _xtype(x, bf16), T, N, K, scheme, _ptr(np.ascontiguousarray(codes)),
+                                   _ptr(np.ascontiguousarray(scales)), _ptr(A if r else None),
+                                   _ptr(B if r else None), r, float(scale), _ptr(y)), "oref_qlinear_lora")
+    return y
 
 
 def group(idx: np.ndarray, E: int):

@@ -293,6 +293,42 @@ int oref_prerouter(const void* x, int32_t xtype, int32_t T, int32_t H, int32_t E
   return fail ? -3 : 0;
 }
 
+/* ---------------- quantized linear with an unmerged LoRA delta ---------------- */
+
+/* [MW] section 手法, "非マージアダプターの実行" (running the unmerged adapter): the
+ * layer keeps its quantized base weights and runs the low-rank delta beside them,
+ * y = W_q x + (alpha / r) B A x, with W_q = code * scale [QK section 6]. */
+int oref_qlinear_lora(const void* x, int32_t xtype, int32_t T, int32_t N, int32_t K, int32_t scheme,
+                      const uint8_t* codes, const uint16_t* scales, const float* A, const float* B, int32_t r,
+                      double scale, float* y) {
+  if (!x || !codes || !scales || !y || T < 0 || N <= 0 || K <= 0 || K % 32 || r < 0) return -1;
+  if (r > 0 && (!A || !B)) return -1;
+  if (xtype < OREF_F32 || xtype > OREF_BF16) return -2;
+  if (scheme != OREF_SYM8 && scheme != OREF_INT4) return -2;
+  int fail = 0;
+  #pragma omp parallel for schedule(static)
+  for (int32_t t = 0; t < T; ++t) {
+    double* u = (double*)malloc(sizeof(double) * ((size_t)r + 1));
+    if (!u) { fail = 1; continue; }
+    /* u = A x_t, the adapter's down projection */
+    for (int32_t j = 0; j < r; ++j) {
+      double acc = 0.0;
+      for (int32_t i = 0; i < K; ++i) acc += (double)A[(int64_t)j * K + i] * x_elem(x, xtype, (int64_t)t * K + i);
+      u[j] = acc;
+    }
+    for (int32_t n = 0; n < N; ++n) {
+      double base = 0.0;
+      for (int32_t i = 0; i < K; ++i)
+        base += (double)weight_at(codes, scales, scheme, n, K, i) * x_elem(x, xtype, (int64_t)t * K + i);
+      double delta = 0.0;
+      for (int32_t j = 0; j < r; ++j) delta += (double)B[(int64_t)n * r + j] * u[j];
+      y[(int64_t)t * N + n] = (float)(base + scale * delta);
+    }
+    free(u);
+  }
+  return fail ? -3 : 0;
+}
+
 /* ---------------- token-by-expert grouping ---------------- */
 
 int oref_group(const int32_t* idx, int32_t T, int32_t k, int32_t E,

@@ -18,7 +18,8 @@
  *        §6 (quality check), §7 (pitfalls).
  *   [MW] "The Other Half of the Memory Wall: Serving 35B MoEs from SSD with
  *        Trained Routing Prediction" (xyznot.com). Section 手法 (method),
- *        "Prerouterヘッドのアーキテクチャ" (prerouter head architecture).
+ *        "Prerouterヘッドのアーキテクチャ" (prerouter head architecture) and
+ *        "非マージアダプターの実行" (running the unmerged adapter).
  *
  * Conventions:
  *   - All pointers are host pointers, owned by the caller, never retained.
@@ -90,6 +91,15 @@ int oref_prerouter(const void* x, int32_t xtype, int32_t T, int32_t H, int32_t E
                    const float* w1, const float* b1, const float* w2, const float* b2,
                    const float* wl, const int32_t* cur, const int32_t* prev, int32_t k,
                    uint32_t flags, int32_t* idx, float* gate, double* logits);
+
+/* Quantized linear with an unmerged LoRA delta [MW "非マージアダプターの実行"]:
+ * y[t][n] = sum_i W_q[n][i] x[t][i] + scale * sum_j B[n][j] (sum_i A[j][i] x[t][i]),
+ * W_q = code * scale of the codec (codes [N][K] or [N][K/2] for int4, scales
+ * [N][K/32]), A [r][K], B [N][r] fp32, scale = alpha / r. r = 0 (A, B unused)
+ * is the plain quantized linear. Sums in fp64, y rounded to fp32 once. */
+int oref_qlinear_lora(const void* x, int32_t xtype, int32_t T, int32_t N, int32_t K, int32_t scheme,
+                      const uint8_t* codes, const uint16_t* scales, const float* A, const float* B, int32_t r,
+                      double scale, float* y);
 
 /* Token-by-expert grouping of the T*k flat assignments f = t*k + s:
  * counts[e], offsets[E+1] (exclusive prefix sum), perm[T*k] = the flat ids
