@@ -66,6 +66,7 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run a plain fp32 copy kernel over this many MiB (counter calibration)")
     ap.add_argument("--no-prerouter", action="store_true", help="skip the prerouted (prediction-as-routing) step")
+    ap.add_argument("--no-lora", action="store_true", help="skip the quantized linear with a LoRA delta")
     ap.add_argument("--path", choices=["auto", "gather", "gemm"], default="auto",
                     help="expert path: the library's choice, the gathered matvec or the grouped MFMA GEMM")
     return ap.parse_args()
@@ -253,6 +254,60 @@ def prerouted_step(w, xs, nl, pools, routers, ws, seed, K, W, path_flag, rq, syn
             "head_bytes": {"stage1_fc1_residual": s1_bytes, "stage2_fc2": s2_bytes},
             "head_gbps": {"stage1_fc1_residual": round(s1_bytes / (s1_us * 1e-6) / 1e9, 1),
                           "stage2_fc2": round(s2_bytes / (s2_us * 1e-6) / 1e9, 1)}}
+
+
+def lora_linear(w, seed, rq, synth, torch) -> dict:
+    """Unmerged LoRA delta on a block-quantized projection (moe_qlinear_lora_forward):
+    an H x H matrix in the workload's codec at the workload's T, rank 16, scale
+    alpha / r = 2. Calls chain over enough distinct weight copies to exceed the
+    256 MB MALL, captured in a HIP graph; timed with the delta and without it."""
+    import numpy as np
+    T, N, K, r = w.T, w.H, w.H, 16
+    g = synth.rng(seed, w.wid, 0, 0, 3000)
+    W = torch.from_numpy((g.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)).astype(np.float32)).cuda()
+    codes, scales = rq.moe_quantize(W, w.scheme)
+    del W
+    wbytes = codes.numel() + scales.numel() * 2
+    copies = max(8, -(-(512 << 20) // wbytes))
+    qws = [rq.QWeight(N, K, w.scheme, codes.clone(), scales.clone()) for _ in range(copies)]
+    A = torch.from_numpy((g.standard_normal((r, K), dtype=np.float32) / np.float32(np.sqrt(K))).astype(np.float32)).cuda()
+    B = torch.from_numpy((g.standard_normal((N, r), dtype=np.float32) * np.float32(0.05)).astype(np.float32)).cuda()
+    x = to_dev(synth.encode_x(synth.draw_x(g, T, K), w.xtype), w.xtype, torch)
+    y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    ws = rq.Workspace()
+    ws.get(rq.lib().moe_qlinear_lora_workspace_bytes(T, r))
+    out = {"N": N, "K": K, "r": r, "T": T, "copies": copies, "weight_bytes": wbytes}
+    for name, a, b in (("base", None, None), ("with_lora", A, B)):
+        def run():
+            for q in qws:
+                rq.moe_qlinear_lora_forward(x, q, a, b, 2.0, ws=ws, out=y)
+        run()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            run()
+        gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 8
+        e0.record()
+        for _ in range(reps):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+        nbytes = wbytes + T * K * (4 if w.xtype == 0 else 2) + T * N * 4 + (4 * (r * K + N * r + 2 * T * r) if a is not None else 0)
+        out[name] = {"us_per_call": round(us, 3), "bytes": nbytes, "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del gr
+    with rq.KernelTimer(rq.MOE_KERNEL_LORA, 2 * 16 + 4) as t:
+        for q in qws[:16]:
+            rq.moe_qlinear_lora_forward(x, q, A, B, 2.0, ws=ws, out=y)
+    torch.cuda.synchronize()
+    out["kernel_us"] = {"lora_a": round(float(np.mean(t.ms[0::2])) * 1e3, 3),
+                        "qlinear_lora": round(float(np.mean(t.ms[1::2])) * 1e3, 3)}
+    out["lora_overhead"] = round(out["with_lora"]["us_per_call"] / out["base"]["us_per_call"] - 1.0, 4)
+    del qws
+    return out
 
 
 def stream_ceiling(nbytes: int, rq, torch) -> dict:
@@ -495,6 +550,10 @@ def main():
         log("prerouted step ...")
         pre = prerouted_step(w, xs, nl, pools, routers, ws, args.seed, K, W, path_flag, rq, synth, torch)
         pre["routed_us_per_layer"] = round(t_layer_s * 1e6, 3)
+    lora = None
+    if w.T <= 64 and not args.no_lora:
+        log("quantized linear with LoRA ...")
+        lora = lora_linear(w, args.seed, rq, synth, torch)
 
     traffic = None
     tf = os.path.join(ROOT, "profiles", f"traffic_{dom}_{w.name}.json")
@@ -532,6 +591,7 @@ def main():
         "stream_read_ceiling": {**ceiling, "layer_vs_ceiling": round(routed_gbps / ceiling["gbps"], 4)},
         **({"miss_policies": miss} if miss else {}),
         **({"prerouted": pre} if pre else {}),
+        **({"lora_linear": lora} if lora else {}),
         "kernel_us": {n: round(v, 3) for n, v in kern_us.items()},
         "roofline": {"kernel": kname, "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -192,7 +192,8 @@ enum {
   MOE_KERNEL_GEMM_DOWN = 7,     /* grouped MFMA GEMM, down */
   MOE_KERNEL_QUANTIZE = 8,      /* block quantiser */
   MOE_KERNEL_HEAD = 9,          /* prerouter head rows (fc1 + GELU; fc2 + residual path) */
-  MOE_KERNEL_COUNT = 10
+  MOE_KERNEL_LORA = 10,         /* quantized linear with LoRA delta (A x; W_q x + delta) */
+  MOE_KERNEL_COUNT = 11
 };
 moe_status moe_timer_start(int32_t kernel, int32_t capacity);
 moe_status moe_timer_read(float* ms, int32_t capacity, int32_t* count);
@@ -303,6 +304,35 @@ moe_status moe_prerouter_forward(const void* x, int32_t xtype, int32_t T, const 
                                  const int32_t* cur, const int32_t* prev, int32_t k, uint32_t flags,
                                  int32_t* topk_idx, float* topk_gate, float* logits, void* ws, size_t ws_bytes,
                                  void* stream);
+
+/* Block-quantized linear with an unmerged LoRA delta. "The Other Half of the
+ * Memory Wall: Serving 35B MoEs from SSD with Trained Routing Prediction"
+ * (xyznot.com), section 手法 (method), "非マージアダプターの実行" (running the
+ * unmerged adapter): the layer keeps its quantized base weights and runs the
+ * low-rank delta beside them, y = W_q x + (alpha / r) B A x; section よくある質問
+ * (FAQ): merged into 4-bit weights and re-quantised, the delta is mostly lost.
+ *
+ * moe_qweight: one matrix [N][K] in the experts' block format (codes [N][K]
+ * bytes for sym8, [N][K/2] for int4; scales [N][K/32] binary16).
+ *   y[t][n] = sum_i W_q[n][i] x[t][i] + scale * sum_j B[n][j] (sum_i A[j][i] x[t][i])
+ *   x:      [T][K] activations of type xtype (16-byte aligned).
+ *   lora_a: [r][K] fp32 (16-byte aligned), lora_b: [N][r] fp32; both ignored when
+ *           r == 0 (the plain quantized linear).
+ *   scale:  alpha / r.
+ *   y:      out [T][N] fp32.
+ * Limits: K a multiple of 32 in [32, 4096]; 1 <= N <= 65536; 0 <= r <= 64;
+ * 1 <= T <= 65536. `ws` holds moe_qlinear_lora_workspace_bytes(T, r) bytes
+ * (u = A x). Errors as elsewhere. */
+typedef struct moe_qweight {
+  int32_t N, K;
+  int32_t scheme;           /* moe_qscheme */
+  const void* codes;
+  const uint16_t* scales;
+} moe_qweight;
+size_t moe_qlinear_lora_workspace_bytes(int32_t T, int32_t r);
+moe_status moe_qlinear_lora_forward(const void* x, int32_t xtype, int32_t T, const moe_qweight* w,
+                                    const float* lora_a, const float* lora_b, int32_t r, float scale, float* y,
+                                    void* ws, size_t ws_bytes, void* stream);
 
 /* Benchmark support: the achievable-bandwidth reference. Reads `bytes` bytes
  * (a positive multiple of 16) of the device buffer `buf` once, with coalesced

@@ -29,11 +29,11 @@ MOE_FLAG_RENORM, MOE_FLAG_PATH_GATHER, MOE_FLAG_PATH_GEMM = 1, 2, 4
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_group", "moe_gather_qmm_forward", "moe_layer_forward",
            "moe_quantize", "moe_timer_start", "moe_timer_read", "moe_stream_read", "moe_miss_replay",
            "moe_stage_experts", "moe_remap_ids", "moe_prerouter_workspace_bytes", "moe_prerouter_forward",
-           "moe_experts_from_logits",
+           "moe_experts_from_logits", "moe_qlinear_lora_workspace_bytes", "moe_qlinear_lora_forward",
            "moe_status_str", "moe_last_error")
 
 (MOE_KERNEL_ROUTE_LOGITS, MOE_KERNEL_TOPK, MOE_KERNEL_GROUP, MOE_KERNEL_GATE_UP, MOE_KERNEL_DOWN, MOE_KERNEL_COMBINE,
- MOE_KERNEL_GEMM_GATE_UP, MOE_KERNEL_GEMM_DOWN, MOE_KERNEL_QUANTIZE, MOE_KERNEL_HEAD) = range(10)
+ MOE_KERNEL_GEMM_GATE_UP, MOE_KERNEL_GEMM_DOWN, MOE_KERNEL_QUANTIZE, MOE_KERNEL_HEAD, MOE_KERNEL_LORA) = range(11)
 
 
 class MoeError(RuntimeError):
@@ -46,6 +46,11 @@ class _Experts(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("scheme", ctypes.c_int32),
                 ("w_gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
                 ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+
+
+class _QWeight(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("K", ctypes.c_int32), ("scheme", ctypes.c_int32),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
 class _Prerouter(ctypes.Structure):
@@ -84,6 +89,9 @@ def lib() -> ctypes.CDLL:
             "moe_prerouter_forward": ([P, I32, I32, ctypes.POINTER(_Prerouter), P, P, I32, U32, P, P, P, P, SZ, P],
                                       ctypes.c_int),
             "moe_experts_from_logits": ([P, I32, I32, P, E, I32, U32, P, P, P, P, SZ, P], ctypes.c_int),
+            "moe_qlinear_lora_workspace_bytes": ([I32, I32], SZ),
+            "moe_qlinear_lora_forward": ([P, I32, I32, ctypes.POINTER(_QWeight), P, P, I32, ctypes.c_float, P, P, SZ,
+                                          P], ctypes.c_int),
             "moe_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "moe_last_error": ([], ctypes.c_char_p),
         }
@@ -349,6 +357,45 @@ def moe_experts_from_logits(x: torch.Tensor, logits: torch.Tensor, ex: "Experts"
            lib().moe_experts_from_logits(_p(x), _xtype(x), T, _p(logits), ctypes.byref(c), k, flags, _p(y), _p(idx),
                                          _p(gate), _p(w), w.numel(), _stream(stream)))
     return (y, idx, gate) if return_routing else y
+
+
+@dataclass
+class QWeight:
+    """One block-quantized matrix [N][K] on the device (codes uint8 [N][K] or [N][K/2],
+    scales int16 bits [N][K/32])."""
+    N: int
+    K: int
+    scheme: int
+    codes: torch.Tensor
+    scales: torch.Tensor
+
+    def c(self) -> _QWeight:
+        _device_tensor(self.codes, "codes")
+        _device_tensor(self.scales, "scales")
+        return _QWeight(self.N, self.K, self.scheme, self.codes.data_ptr(), self.scales.data_ptr())
+
+
+def moe_qlinear_lora_forward(x: torch.Tensor, w: QWeight, lora_a: torch.Tensor | None, lora_b: torch.Tensor | None,
+                             scale: float, ws: Workspace | None = None, stream=None,
+                             out: torch.Tensor | None = None) -> torch.Tensor:
+    """y [T][N] = W_q x + scale * B (A x); lora_a [r][K], lora_b [N][r] fp32 (None: no delta)."""
+    _device_tensor(x, "x")
+    T = x.shape[0]
+    r = 0
+    if lora_a is not None:
+        _device_tensor(lora_a, "lora_a")
+        _device_tensor(lora_b, "lora_b")
+        r = lora_a.shape[0]
+        if lora_a.shape != (r, w.K) or lora_b.shape != (w.N, r):
+            raise ValueError("lora_a must be [r][K] and lora_b [N][r]")
+    y = out if out is not None else torch.empty((T, w.N), dtype=torch.float32, device=x.device)
+    nb = int(lib().moe_qlinear_lora_workspace_bytes(T, r))
+    buf = _ws(ws, nb, x.device)
+    c = w.c()
+    _check("moe_qlinear_lora_forward",
+           lib().moe_qlinear_lora_forward(_p(x), _xtype(x), T, ctypes.byref(c), _p(lora_a), _p(lora_b), r, scale,
+                                          _p(y), _p(buf), buf.numel(), _stream(stream)))
+    return y
 
 
 def moe_route(x: torch.Tensor, router_w: torch.Tensor, k: int, flags: int = MOE_FLAG_RENORM,

@@ -121,6 +121,11 @@ struct HeadDev {
 hipError_t launch_prerouter(const void* x, int xtype, int T, const HeadDev& hd, const int32_t* cur,
                             const int32_t* prev, int k, int renorm, float* act, float* part, float* logits,
                             int32_t* idx, float* gate, hipStream_t s);
+// Quantized linear with an unmerged LoRA delta: u = A x into u [T][r] (when
+// r > 0), then y [T][N] = W_q x + c * B u.
+hipError_t launch_qlinear_lora(const void* x, int xtype, int T, int N, int K, int scheme, const uint8_t* codes,
+                               const uint16_t* scales, const float* A, const float* B, int r, float c, float* u,
+                               float* y, hipStream_t s);
 hipError_t launch_quantize(const float* w, int64_t rows, int K, int scheme, uint8_t* codes, uint16_t* scales,
                            hipStream_t s);
 

@@ -441,6 +441,40 @@ moe_status moe_prerouter_forward(const void* x, int32_t xtype, int32_t T, const 
                     "prerouter head");
 }
 
+size_t moe_qlinear_lora_workspace_bytes(int32_t T, int32_t r) {
+  if (T < 1 || T > 65536 || r < 0 || r > 64) return 0;
+  return align256((size_t)T * (size_t)(r > 0 ? r : 1) * 4);
+}
+
+moe_status moe_qlinear_lora_forward(const void* x, int32_t xtype, int32_t T, const moe_qweight* w,
+                                    const float* lora_a, const float* lora_b, int32_t r, float scale, float* y,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  moe_status st;
+  if ((st = check_x(x, xtype))) return st;
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weight struct is NULL");
+  if (w->scheme != MOE_Q_SYM8 && w->scheme != MOE_Q_INT4)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown weight codec %d", w->scheme);
+  if (T < 1 || T > 65536) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [1, 65536]", T);
+  if (w->N < 1 || w->N > 65536) return fail(MOE_ERR_INVALID_ARG, "N=%d outside [1, 65536]", w->N);
+  if (w->K < 32 || w->K > 4096 || w->K % 32)
+    return fail(MOE_ERR_INVALID_ARG, "K=%d must be a multiple of 32 in [32, 4096]", w->K);
+  if (r < 0 || r > 64) return fail(MOE_ERR_INVALID_ARG, "r=%d outside [0, 64]", r);
+  if (!w->codes || !w->scales || !y) return fail(MOE_ERR_INVALID_ARG, "codes, scales or y is NULL");
+  if (!aligned(w->codes, 16) || !aligned(w->scales, 2) || !aligned(y, 4))
+    return fail(MOE_ERR_INVALID_ARG, "codes must be 16-byte aligned, scales 2-byte and y 4-byte aligned");
+  if (r > 0 && (!lora_a || !lora_b)) return fail(MOE_ERR_INVALID_ARG, "lora_a or lora_b is NULL with r > 0");
+  if (r > 0 && (!aligned(lora_a, 16) || !aligned(lora_b, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "lora_a must be 16-byte aligned and lora_b 4-byte aligned");
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace pointer is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  const size_t need = moe_qlinear_lora_workspace_bytes(T, r);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return hip_status(moe::launch_qlinear_lora(x, xtype, T, w->N, w->K, w->scheme, static_cast<const uint8_t*>(w->codes),
+                                             w->scales, lora_a, lora_b, r, scale, at<float>(ws, 0), y,
+                                             static_cast<hipStream_t>(stream)),
+                    "quantized linear with LoRA");
+}
+
 moe_status moe_stream_read(const void* buf, int64_t bytes, void* stream) {
   if (!buf || !aligned(buf, 16)) return fail(MOE_ERR_INVALID_ARG, "buf is NULL or not 16-byte aligned");
   if (bytes <= 0 || bytes % 16 || bytes > ((int64_t)1 << 40))

@@ -200,3 +200,39 @@ def test_experts_from_logits_validation(L):
     assert call(flags=rq.MOE_FLAG_PATH_GATHER | rq.MOE_FLAG_PATH_GEMM) == rq.MOE_ERR_INVALID_ARG
     assert call(flags=0x40) == rq.MOE_ERR_UNSUPPORTED
     assert call(nws=16) == rq.MOE_ERR_WORKSPACE
+
+
+def test_qlinear_lora_validation(L):
+    assert L.moe_qlinear_lora_workspace_bytes(1, 16) == 256
+    assert L.moe_qlinear_lora_workspace_bytes(100, 64) == 25600
+    assert L.moe_qlinear_lora_workspace_bytes(3, 5) == 256
+    assert L.moe_qlinear_lora_workspace_bytes(1, 0) == 256
+    for bad in [(0, 8), (1, 65), (1, -1), (70000, 8)]:
+        assert L.moe_qlinear_lora_workspace_bytes(*bad) == 0, bad
+
+    def qw(N=2048, K=2048, scheme=rq.MOE_Q_INT4, codes=FAKE, scales=FAKE):
+        v = lambda p: None if p is None else p.value
+        return rq._QWeight(N, K, scheme, v(codes), v(scales))
+
+    def call(x=FAKE, xt=rq.MOE_F16, T=1, w="default", a=FAKE, b=FAKE, r=16, y=FAKE, ws=FAKE, nws=1 << 20):
+        w = qw() if w == "default" else w
+        return L.moe_qlinear_lora_forward(x, xt, T, ctypes.byref(w) if w is not None else None, a, b, r, 0.5, y, ws,
+                                          nws, None)
+
+    assert call(x=None) == rq.MOE_ERR_INVALID_ARG
+    assert call(xt=9) == rq.MOE_ERR_UNSUPPORTED
+    assert call(w=None) == rq.MOE_ERR_INVALID_ARG
+    assert call(w=qw(scheme=4)) == rq.MOE_ERR_UNSUPPORTED
+    assert call(w=qw(K=100)) == rq.MOE_ERR_INVALID_ARG
+    assert call(w=qw(K=8192)) == rq.MOE_ERR_INVALID_ARG
+    assert call(w=qw(N=0)) == rq.MOE_ERR_INVALID_ARG
+    assert call(w=qw(codes=None)) == rq.MOE_ERR_INVALID_ARG
+    assert call(w=qw(codes=ctypes.c_void_p(0x10004))) == rq.MOE_ERR_INVALID_ARG
+    assert call(w=qw(scales=ctypes.c_void_p(0x10001))) == rq.MOE_ERR_INVALID_ARG
+    assert call(T=0) == rq.MOE_ERR_INVALID_ARG
+    assert call(r=65) == rq.MOE_ERR_INVALID_ARG
+    assert call(a=None) == rq.MOE_ERR_INVALID_ARG
+    assert call(a=ctypes.c_void_p(0x10008)) == rq.MOE_ERR_INVALID_ARG
+    assert call(y=None) == rq.MOE_ERR_INVALID_ARG
+    assert call(ws=None) == rq.MOE_ERR_WORKSPACE
+    assert call(T=4096, nws=1024) == rq.MOE_ERR_WORKSPACE
