@@ -147,9 +147,9 @@ def prerouted_step(w, xs, nl, pools, routers, ws, seed, K, W, path_flag, rq, syn
     its head (moe_prerouter_forward, logits only) on the layer input and its own
     routing at this token and the previous one. No other router runs. Heads are
     seeded random weights (F = synth.PREROUTER_F). Timed twice, each as HIP
-    graphs (one per parity of the step, for the double-buffered routing): heads
-    in line on the layer stream, then on a second graph branch that waits only
-    for its own layer's expert call."""
+    graphs (one per parity of the step, for the double-buffered routing): with
+    separate expert and head calls, then with moe_prerouted_layer_forward, which
+    runs the head's rows inside the expert launches for one token."""
     import numpy as np
     F, T, k = synth.PREROUTER_F, w.T, w.k
     heads = []
@@ -178,39 +178,39 @@ def prerouted_step(w, xs, nl, pools, routers, ws, seed, K, W, path_flag, rq, syn
             rq.moe_prerouter_forward(xs[0], warm, None, None, k, ws=hws, logits_out=lgs[l][g], topk=False)
     torch.cuda.synchronize()
     ys = [torch.empty((T, w.H), dtype=torch.float32, device="cuda") for _ in range(nl)]
-    side = torch.cuda.Stream()
-
-    def run(gen, overlap):
+    def run(gen, fused):
         cur, other = gen % 2, 1 - gen % 2
-        main = torch.cuda.current_stream()
         for l in range(nl):
             if l == 0:
                 rq.moe_layer_forward(xbuf, routers[0], pools[0], k, rq.MOE_FLAG_RENORM | path_flag, ws=ws,
                                      out=ys[0], routing_out=(idxs[0][cur], gates[0]))
+            elif fused:
+                # experts on the predicted logits and the next layer's head, together
+                head = heads[l] if l + 1 < nl else None
+                rq.moe_prerouted_layer_forward(xbuf, lgs[l][cur], pools[l], k, head, idxs[l][other], idxs[l][cur],
+                                               lgs[l + 1][other] if head is not None else None,
+                                               flags=rq.MOE_FLAG_RENORM | path_flag, gate_out=gates[l], ws=ws,
+                                               out=ys[l])
+                continue
             else:
                 rq.moe_experts_from_logits(xbuf, lgs[l][cur], pools[l], k, rq.MOE_FLAG_RENORM | path_flag, ws=ws,
                                            out=ys[l], routing_out=(idxs[l][cur], gates[l]))
             if l + 1 < nl:
-                hs = side if overlap else main
-                if overlap:
-                    side.wait_stream(main)
-                with torch.cuda.stream(hs):
-                    rq.moe_prerouter_forward(xbuf, heads[l], idxs[l][cur], idxs[l][other], k, ws=hws,
-                                             logits_out=lgs[l + 1][other], topk=False, stream=hs)
-        if overlap:
-            main.wait_stream(side)
+                rq.moe_prerouter_forward(xbuf, heads[l], idxs[l][cur], idxs[l][other], k, ws=hws,
+                                         logits_out=lgs[l + 1][other], topk=False)
 
     for gen in range(2):
         run(gen, False)
+        run(gen, True)
     torch.cuda.synchronize()
     nx = xs.shape[0]
     out = {}
-    for overlap in (False, True):
+    for fused in (False, True):
         graphs = []
         for gen in range(2):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                run(gen, overlap)
+                run(gen, fused)
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -228,8 +228,8 @@ def prerouted_step(w, xs, nl, pools, routers, ws, seed, K, W, path_flag, rq, syn
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
-        out["overlapped" if overlap else "serial"] = {"us_per_layer": round(ms * 1e3 / (K * nl), 3),
-                                                      "step_tokens_per_s": round(T / (ms * 1e-3 / K), 1)}
+        out["fused" if fused else "separate_calls"] = {"us_per_layer": round(ms * 1e3 / (K * nl), 3),
+                                                       "step_tokens_per_s": round(T / (ms * 1e-3 / K), 1)}
         del graphs
     # head kernels alone, per launch (eager): stage 1 (fc1 + GELU, residual
     # path), stage 2 (fc2); the top-k runs inside the next layer's expert call

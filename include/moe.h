@@ -305,6 +305,31 @@ moe_status moe_prerouter_forward(const void* x, int32_t xtype, int32_t T, const 
                                  int32_t* topk_idx, float* topk_gate, float* logits, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* One layer of prerouted decode (prediction as routing, "The Other Half of the
+ * Memory Wall: Serving 35B MoEs from SSD with Trained Routing Prediction"
+ * (xyznot.com), section 主なアイデア): moe_experts_from_logits on the logits
+ * predicted for this layer, then, when head is not NULL, the next layer's head
+ * (moe_prerouter_forward, logits only) on this layer's input, with this layer's
+ * routing as the current-token k-hot input and prev_idx as the previous one.
+ * For one token on the matvec path (I <= 1024, F <= 1024) both run together in
+ * two launches: the head's rows are extra workgroups of the gate/up and down
+ * launches. Otherwise the calls run one after the other.
+ *   logits:        [T][E] fp32 predicted for this layer (16-byte aligned).
+ *   topk_idx_out:  out [T][k], this layer's routing; required with a head (it
+ *                  is the next token's prev_idx).
+ *   prev_idx:      [T][k] this layer's routing at the previous token, or NULL.
+ *   logits_next:   out [T][E] fp32, the next layer's predicted logits (16-byte
+ *                  aligned); required with a head. It must not alias `logits`.
+ *   ws:            moe_workspace_bytes(T, E, H, I, k, scheme) rounded up to 256,
+ *                  plus moe_prerouter_workspace_bytes(T, E, F) with a head.
+ * Errors as moe_experts_from_logits and moe_prerouter_forward, and
+ * MOE_ERR_INVALID_ARG for a head whose H or E differ from the experts'. */
+moe_status moe_prerouted_layer_forward(const void* x, int32_t xtype, int32_t T, const float* logits,
+                                       const moe_experts* ex, int32_t k, uint32_t flags, float* y,
+                                       int32_t* topk_idx_out, float* topk_gate_out, const moe_prerouter* head,
+                                       const int32_t* prev_idx, float* logits_next, void* ws, size_t ws_bytes,
+                                       void* stream);
+
 /* Block-quantized linear with an unmerged LoRA delta. "The Other Half of the
  * Memory Wall: Serving 35B MoEs from SSD with Trained Routing Prediction"
  * (xyznot.com), section 手法 (method), "非マージアダプターの実行" (running the

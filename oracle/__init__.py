@@ -79,6 +79,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "oref_logits": ([P, I32, I32, I32, P, I32, P], ctypes.c_int),
         "oref_route": ([P, I32, I32, I32, P, I32, I32, U32, P, P], ctypes.c_int),
         "oref_group": ([P, I32, I32, I32, P, P, P, P, P], ctypes.c_int),
+        "oref_topk_logits": ([P, I32, I32, I32, U32, P, P], ctypes.c_int),
         "oref_qlinear_lora": ([P, I32, I32, I32, I32, I32, P, P, P, P, I32, ctypes.c_double, P], ctypes.c_int),
         "oref_prerouter": ([P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, I32, U32, P, P, P], ctypes.c_int),
         "oref_gather_forward": ([P, I32, I32, ctypes.POINTER(_Experts), I32, P, P, P], ctypes.c_int),
@@ -260,6 +261,16 @@ def qlinear_lora(x: np.ndarray, codes: np.ndarray, scales: np.ndarray, scheme: i
                                    _ptr(np.ascontiguousarray(scales)), _ptr(A if r else None),
                                    _ptr(B if r else None), r, float(scale), _ptr(y)), "oref_qlinear_lora")
     return y
+
+
+def topk_logits(logits: np.ndarray, k: int, flags: int = RENORM):
+    """The router's softmax/top-k on given fp32 logits [T][E]: (idx [T][k], gate [T][k])."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    idx = np.empty((T, k), dtype=np.int32)
+    gate = np.empty((T, k), dtype=np.float32)
+    _check(lib().oref_topk_logits(_ptr(lg), T, E, k, flags, _ptr(idx), _ptr(gate)), "oref_topk_logits")
+    return idx, gate
 
 
 def group(idx: np.ndarray, E: int):

@@ -239,6 +239,23 @@ int oref_route(const void* x, int32_t xtype, int32_t T, int32_t H,
   return fail ? -3 : 0;
 }
 
+/* The router's softmax and top-k on given fp32 logits [T][E] (as oref_route
+ * after its gate linear). */
+int oref_topk_logits(const float* logits, int32_t T, int32_t E, int32_t k, uint32_t flags, int32_t* idx,
+                     float* gate) {
+  if (!logits || !idx || !gate || T < 0 || E <= 0 || k < 1 || k > E) return -1;
+  int fail = 0;
+  #pragma omp parallel for schedule(static)
+  for (int32_t t = 0; t < T; ++t) {
+    double* l = (double*)malloc(sizeof(double) * (size_t)E);
+    if (!l) { fail = 1; continue; }
+    for (int32_t e = 0; e < E; ++e) l[e] = (double)logits[(int64_t)t * E + e];
+    if (softmax_topk_row(l, E, k, flags, idx + (int64_t)t * k, gate + (int64_t)t * k)) fail = 1;
+    free(l);
+  }
+  return fail ? -3 : 0;
+}
+
 /* ---------------- prerouter head ---------------- */
 
 /* erf-form GELU: z * Phi(z), Phi the standard normal CDF, written with erf

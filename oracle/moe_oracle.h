@@ -78,6 +78,10 @@ int oref_route(const void* x, int32_t xtype, int32_t T, int32_t H,
                const float* R, int32_t E, int32_t k, uint32_t flags,
                int32_t* idx, float* gate);
 
+/* oref_route's softmax and top-k on given fp32 logits [T][E]. */
+int oref_topk_logits(const float* logits, int32_t T, int32_t E, int32_t k, uint32_t flags, int32_t* idx,
+                     float* gate);
+
 /* Prerouter head [MW "prerouter head architecture"], per token t:
  *   f = [x_t ; khot(cur_t) ; khot(prev_t)]   (H + 2E values; khot(ids) has a 1
  *       at each of the k ids and 0 elsewhere, all 0 when the array is NULL)

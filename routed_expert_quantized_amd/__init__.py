@@ -29,7 +29,8 @@ MOE_FLAG_RENORM, MOE_FLAG_PATH_GATHER, MOE_FLAG_PATH_GEMM = 1, 2, 4
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_group", "moe_gather_qmm_forward", "moe_layer_forward",
            "moe_quantize", "moe_timer_start", "moe_timer_read", "moe_stream_read", "moe_miss_replay",
            "moe_stage_experts", "moe_remap_ids", "moe_prerouter_workspace_bytes", "moe_prerouter_forward",
-           "moe_experts_from_logits", "moe_qlinear_lora_workspace_bytes", "moe_qlinear_lora_forward",
+           "moe_experts_from_logits", "moe_prerouted_layer_forward", "moe_qlinear_lora_workspace_bytes",
+           "moe_qlinear_lora_forward",
            "moe_status_str", "moe_last_error")
 
 (MOE_KERNEL_ROUTE_LOGITS, MOE_KERNEL_TOPK, MOE_KERNEL_GROUP, MOE_KERNEL_GATE_UP, MOE_KERNEL_DOWN, MOE_KERNEL_COMBINE,
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
             "moe_prerouter_forward": ([P, I32, I32, ctypes.POINTER(_Prerouter), P, P, I32, U32, P, P, P, P, SZ, P],
                                       ctypes.c_int),
             "moe_experts_from_logits": ([P, I32, I32, P, E, I32, U32, P, P, P, P, SZ, P], ctypes.c_int),
+            "moe_prerouted_layer_forward": ([P, I32, I32, P, E, I32, U32, P, P, P, ctypes.POINTER(_Prerouter), P, P, P,
+                                             SZ, P], ctypes.c_int),
             "moe_qlinear_lora_workspace_bytes": ([I32, I32], SZ),
             "moe_qlinear_lora_forward": ([P, I32, I32, ctypes.POINTER(_QWeight), P, P, I32, ctypes.c_float, P, P, SZ,
                                           P], ctypes.c_int),
@@ -395,6 +398,31 @@ def moe_qlinear_lora_forward(x: torch.Tensor, w: QWeight, lora_a: torch.Tensor |
     _check("moe_qlinear_lora_forward",
            lib().moe_qlinear_lora_forward(_p(x), _xtype(x), T, ctypes.byref(c), _p(lora_a), _p(lora_b), r, scale,
                                           _p(y), _p(buf), buf.numel(), _stream(stream)))
+    return y
+
+
+def moe_prerouted_layer_forward(x: torch.Tensor, logits: torch.Tensor, ex: "Experts", k: int,
+                                head: Prerouter | None, prev_idx: torch.Tensor | None, idx_out: torch.Tensor,
+                                logits_next: torch.Tensor | None, flags: int = MOE_FLAG_RENORM,
+                                gate_out: torch.Tensor | None = None, ws: Workspace | None = None, stream=None,
+                                out: torch.Tensor | None = None) -> torch.Tensor:
+    """One prerouted decode layer: experts on the predicted `logits` (routing into
+    idx_out), then the next layer's head writing logits_next. Returns y [T][H]."""
+    _device_tensor(x, "x")
+    _device_tensor(logits, "logits")
+    T = x.shape[0]
+    y = out if out is not None else torch.empty((T, ex.H), dtype=torch.float32, device=x.device)
+    nb = -(-moe_workspace_bytes(T, ex.E, ex.H, ex.I, k, ex.scheme) // 256) * 256
+    hc = None
+    if head is not None:
+        nb += moe_prerouter_workspace_bytes(T, head.E, head.F)
+        hc = head.c()
+    w = _ws(ws, nb, x.device)
+    c = ex.c()
+    _check("moe_prerouted_layer_forward",
+           lib().moe_prerouted_layer_forward(_p(x), _xtype(x), T, _p(logits), ctypes.byref(c), k, flags, _p(y),
+                                             _p(idx_out), _p(gate_out), ctypes.byref(hc) if hc is not None else None,
+                                             _p(prev_idx), _p(logits_next), _p(w), w.numel(), _stream(stream)))
     return y
 
 

@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "head_rows.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -50,14 +51,14 @@ constexpr int kGateUpWaves = 4;
 // With H16 the activation is stored as fp16 (round to nearest even) for the
 // slot-parallel down kernel, else as fp32.
 template <int SCHEME, int XT, int NBJ, int RP, bool FROM_LOGITS, int VPL, bool H16>
-__global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1(const void* __restrict__ x, ExpertsDev ex, int k, int renorm,
-                                                    const float* __restrict__ logits,
-                                                    const int32_t* __restrict__ idx_in,
-                                                    int32_t* __restrict__ idx_ws, float* __restrict__ gate_ws,
-                                                    int32_t* __restrict__ idx_user, float* __restrict__ gate_user,
-                                                    float* __restrict__ h, int blocks_per_slot) {
+__device__ __forceinline__ void gate_up_t1_body(const void* __restrict__ x, const ExpertsDev& ex, int k, int renorm,
+                                                const float* __restrict__ logits,
+                                                const int32_t* __restrict__ idx_in,
+                                                int32_t* __restrict__ idx_ws, float* __restrict__ gate_ws,
+                                                int32_t* __restrict__ idx_user, float* __restrict__ gate_user,
+                                                float* __restrict__ h, int blocks_per_slot, int bid) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int slot = blockIdx.x / blocks_per_slot, blk = blockIdx.x % blocks_per_slot;
+  const int slot = bid / blocks_per_slot, blk = bid % blocks_per_slot;
   const int H = ex.H, I = ex.I, NB = H / 32;
   // Every load below is unconditional (block and row indices are clamped in
   // bounds, surplus lanes get a zero scale) so the scheduler can issue them all
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1(const void* __
     // the routing for the down kernel and the caller.
     int my_idx;
     float my_gate;
-    const bool publisher = blockIdx.x == (k - 1) * blocks_per_slot;
+    const bool publisher = bid == (k - 1) * blocks_per_slot;
     // wave 0 picks the routing; the other waves wait for it at the barrier
     __shared__ int e_sh;
     if (wave == 0) {
@@ -156,6 +157,17 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1(const void* __
   }
 }
 
+template <int SCHEME, int XT, int NBJ, int RP, bool FROM_LOGITS, int VPL, bool H16>
+__global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1(const void* __restrict__ x, ExpertsDev ex, int k, int renorm,
+                                                    const float* __restrict__ logits,
+                                                    const int32_t* __restrict__ idx_in,
+                                                    int32_t* __restrict__ idx_ws, float* __restrict__ gate_ws,
+                                                    int32_t* __restrict__ idx_user, float* __restrict__ gate_user,
+                                                    float* __restrict__ h, int blocks_per_slot) {
+  gate_up_t1_body<SCHEME, XT, NBJ, RP, FROM_LOGITS, VPL, H16>(x, ex, k, renorm, logits, idx_in, idx_ws, gate_ws,
+                                                             idx_user, gate_user, h, blocks_per_slot, blockIdx.x);
+}
+
 // Single-token down, one wave per slot. Grid: ceil(H / (4 RW)) workgroups of
 // k waves. Wave q takes slot q; its four 16-lane row groups take RW rows each,
 // and lane ll of a group owns blocks ll + 16 j of the I inputs for those rows,
@@ -165,14 +177,14 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1(const void* __
 // own slot's rows, y[q][m]). Many small waves per CU let the dot products of
 // the rows that have arrived overlap the loads still in flight.
 template <int SCHEME, int NBJ, int RW>
-__global__ __launch_bounds__(1024) void k_down_t1_slots(ExpertsDev ex, int k, const int32_t* __restrict__ idx,
-                                                       const float* __restrict__ gate,
-                                                       const uint16_t* __restrict__ h16, float* __restrict__ y) {
+__device__ __forceinline__ void down_t1_slots_body(const ExpertsDev& ex, int k, const int32_t* __restrict__ idx,
+                                                   const float* __restrict__ gate,
+                                                   const uint16_t* __restrict__ h16, float* __restrict__ y, int bid) {
   __shared__ float part[kMaxK][4 * RW];
   const int tid = (int)threadIdx.x;
   const int q = tid >> 6, lane = tid & 63, lg = lane >> 4, ll = lane & 15;
   const int H = ex.H, I = ex.I, NBI = I / 32;
-  const int mb = (int)blockIdx.x * 4 * RW, m0 = mb + lg * RW;
+  const int mb = (int)bid * 4 * RW, m0 = mb + lg * RW;
   const int64_t rb = row_bytes<SCHEME>(I);
   XBlockH<SCHEME> hb[NBJ];
 #pragma unroll
@@ -209,6 +221,13 @@ __global__ __launch_bounds__(1024) void k_down_t1_slots(ExpertsDev ex, int k, co
     for (int s = 0; s < k; ++s) acc = fmaf(gate[s], part[s][tid], acc);
     y[mb + tid] = acc;
   }
+}
+
+template <int SCHEME, int NBJ, int RW>
+__global__ __launch_bounds__(1024) void k_down_t1_slots(ExpertsDev ex, int k, const int32_t* __restrict__ idx,
+                                                       const float* __restrict__ gate,
+                                                       const uint16_t* __restrict__ h16, float* __restrict__ y) {
+  down_t1_slots_body<SCHEME, NBJ, RW>(ex, k, idx, gate, h16, y, blockIdx.x);
 }
 
 // General single-token down (any k, any I): KC slots' rows in flight at a
@@ -556,6 +575,119 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
     };
     if (nbi <= 4) go(IC<4>{});
     else go(IC<8>{});
+  });
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ prerouted decode, T = 1
+// Prediction as routing ("The Other Half of the Memory Wall: Serving 35B MoEs
+// from SSD with Trained Routing Prediction", xyznot.com, section 主なアイデア):
+// a layer runs its experts on the logits its predecessor's head predicted, and
+// its own head predicts the next layer's. The head's stage 1 needs only the
+// layer input and the layer's routing, and its stage 2 only stage 1's output,
+// so each joins an expert launch as extra workgroups: blocks past the expert
+// grid run the head. Two launches per layer, against the router path's three.
+
+// Gate/up grid, then F + E head rows (fc1 + GELU, residual path). A head
+// workgroup first picks the layer's routing from the same logits, as the
+// gate/up workgroups do, for the current-token k-hot input.
+template <int SCHEME, int XT, int NBJ, int VPL, int HNCH>
+__global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1_head(
+    const void* __restrict__ x, ExpertsDev ex, int k, int renorm, const float* __restrict__ logits,
+    int32_t* __restrict__ idx_ws, float* __restrict__ gate_ws, int32_t* __restrict__ idx_user,
+    float* __restrict__ gate_user, float* __restrict__ h, int blocks_per_slot, HeadDev hd,
+    const int32_t* __restrict__ prev, float* __restrict__ act, float* __restrict__ part) {
+  static_assert(kGateUpWaves == kHeadWaves, "head rows run on gate/up-sized workgroups");
+  const int nmain = k * blocks_per_slot;
+  if ((int)blockIdx.x < nmain) {
+    gate_up_t1_body<SCHEME, XT, NBJ, 1, true, VPL, true>(x, ex, k, renorm, logits, nullptr, idx_ws, gate_ws, idx_user,
+                                                         gate_user, h, blocks_per_slot, blockIdx.x);
+    return;
+  }
+  __shared__ int32_t cur_sh[kMaxK];
+  if (threadIdx.x < 64) {
+    int my_idx;
+    float my_gate;
+    wave_topk<VPL>(logits, ex.E, k, renorm != 0, my_idx, my_gate);
+    if ((int)threadIdx.x < k) cur_sh[threadIdx.x] = my_idx;
+  }
+  __syncthreads();
+  head_stage1_body<XT, HNCH, 1, 1>((int)blockIdx.x - nmain, 0, x, 1, hd.H, hd.E, hd.F, hd.w1, hd.b1, hd.wl, hd.b2,
+                                   cur_sh, prev, k, act, part);
+}
+
+// Down grid, then ceil(E / k) workgroups of head stage 2 (one fc2 row per wave).
+template <int SCHEME, int NBJ, int RW, int HNCHF>
+__global__ __launch_bounds__(1024) void k_down_t1_slots_head(ExpertsDev ex, int k, const int32_t* __restrict__ idx,
+                                                            const float* __restrict__ gate,
+                                                            const uint16_t* __restrict__ h16, float* __restrict__ y,
+                                                            int nmain, const float* __restrict__ act,
+                                                            const float* __restrict__ part,
+                                                            const float* __restrict__ w2, int E, int F,
+                                                            float* __restrict__ logits_next) {
+  if ((int)blockIdx.x < nmain) {
+    down_t1_slots_body<SCHEME, NBJ, RW>(ex, k, idx, gate, h16, y, blockIdx.x);
+    return;
+  }
+  head_stage2_body<HNCHF, 1>((int)blockIdx.x - nmain, 0, (int)(blockDim.x >> 6), act, part, w2, 1, E, F,
+                             logits_next);
+}
+
+bool prerouted_t1_fusable(const ExpertsDev& ex, int xtype, const HeadDev& hd) {
+  const int nbi = (ex.I / 32 + 15) / 16;
+  return nbi <= 2 && hd.E == ex.E && hd.H == ex.H && hd.F <= 1024 && (xtype == MOE_F16 || xtype == MOE_BF16 ||
+                                                                       xtype == MOE_F32);
+}
+
+hipError_t launch_prerouted_t1(const void* x, int xtype, const ExpertsDev& ex, int k, int renorm,
+                               const float* logits, int32_t* idx_ws, float* gate_ws, int32_t* idx_user,
+                               float* gate_user, float* h, float* y, const HeadDev& hd, const int32_t* prev,
+                               float* act, float* part, float* logits_next, hipStream_t s) {
+  const int nbi = (ex.I / 32 + 15) / 16;
+  const int nbj = (ex.H / 32 + 63) / 64;
+  const int hnch = ((hd.H + 255) / 256 + kHeadWaves - 1) / kHeadWaves;
+  with_scheme(ex.scheme, [&](auto S) {
+    with_xtype(xtype, [&](auto X) {
+      constexpr int SC = decltype(S)::value, XT = decltype(X)::value;
+      auto go = [&](auto NBJc, auto VPLc, auto HNc) {
+        constexpr int NBJ = decltype(NBJc)::value, VPL = decltype(VPLc)::value, HN = decltype(HNc)::value;
+        const int bps = (ex.I + kGateUpWaves - 1) / kGateUpWaves;
+        dim3 grid(k * bps + hd.F + hd.E);
+        MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_t1_head<SC, XT, NBJ, VPL, HN>), grid, dim3(64 * kGateUpWaves), 0, s,
+                   x, ex, k, renorm, logits, idx_ws, gate_ws, idx_user, gate_user, h, bps, hd, prev, act, part);
+      };
+      auto with_hn = [&](auto NBJc, auto VPLc) {
+        if (hnch <= 1) go(NBJc, VPLc, IC<1>{});
+        else if (hnch <= 2) go(NBJc, VPLc, IC<2>{});
+        else go(NBJc, VPLc, IC<4>{});
+      };
+      auto with_v = [&](auto NBJc) {
+        if (ex.E <= 256) with_hn(NBJc, IC<4>{});
+        else if (ex.E <= 512) with_hn(NBJc, IC<8>{});
+        else with_hn(NBJc, IC<16>{});
+      };
+      if (nbj <= 1) with_v(IC<1>{});
+      else with_v(IC<2>{});
+    });
+  });
+  const int hnchf = (hd.F + 255) / 256;
+  with_scheme(ex.scheme, [&](auto S) {
+    constexpr int SC = decltype(S)::value;
+    const int nmain = (ex.H + 4 * kDownRows - 1) / (4 * kDownRows);
+    dim3 grid(nmain + (hd.E + k - 1) / k);
+    const uint16_t* h16 = reinterpret_cast<const uint16_t*>(h);
+    auto go = [&](auto NBIc, auto HFc) {
+      constexpr int NBI = decltype(NBIc)::value, HF = decltype(HFc)::value;
+      MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_t1_slots_head<SC, NBI, kDownRows, HF>), grid, dim3(64 * k), 0, s, ex, k,
+                 idx_ws, gate_ws, h16, y, nmain, act, part, hd.w2, hd.E, hd.F, logits_next);
+    };
+    auto with_hf = [&](auto NBIc) {
+      if (hnchf <= 1) go(NBIc, IC<1>{});
+      else if (hnchf <= 2) go(NBIc, IC<2>{});
+      else go(NBIc, IC<4>{});
+    };
+    if (nbi <= 1) with_hf(IC<1>{});
+    else with_hf(IC<2>{});
   });
   return hipGetLastError();
 }

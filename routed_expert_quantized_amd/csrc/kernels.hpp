@@ -126,6 +126,16 @@ hipError_t launch_prerouter(const void* x, int xtype, int T, const HeadDev& hd, 
 hipError_t launch_qlinear_lora(const void* x, int xtype, int T, int N, int K, int scheme, const uint8_t* codes,
                                const uint16_t* scales, const float* A, const float* B, int r, float c, float* u,
                                float* y, hipStream_t s);
+// Prerouted decode of one token: experts on the predicted `logits` (top-k in
+// the gate/up kernel, routing to idx_ws/gate_ws and the optional user copies),
+// with the next layer's head run beside them: its logits for the next token go
+// to logits_next. prev: this layer's routing at the previous token, or null.
+// Valid when prerouted_t1_fusable() holds.
+bool prerouted_t1_fusable(const ExpertsDev& ex, int xtype, const HeadDev& hd);
+hipError_t launch_prerouted_t1(const void* x, int xtype, const ExpertsDev& ex, int k, int renorm,
+                               const float* logits, int32_t* idx_ws, float* gate_ws, int32_t* idx_user,
+                               float* gate_user, float* h, float* y, const HeadDev& hd, const int32_t* prev,
+                               float* act, float* part, float* logits_next, hipStream_t s);
 hipError_t launch_quantize(const float* w, int64_t rows, int K, int scheme, uint8_t* codes, uint16_t* scales,
                            hipStream_t s);
 

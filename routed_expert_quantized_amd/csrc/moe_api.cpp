@@ -399,6 +399,21 @@ static bool head_shape_ok(int64_t T, int64_t E, int64_t F) {
   return T >= 1 && T <= 65536 && E >= 2 && E <= moe::kMaxE && E % 2 == 0 && F >= 32 && F <= 4096 && F % 32 == 0;
 }
 
+static moe_status check_head(const moe_prerouter* head, int64_t T, int64_t k) {
+  moe_status st;
+  if (!head) return fail(MOE_ERR_INVALID_ARG, "prerouter struct is NULL");
+  const int64_t H = head->H, E = head->E, F = head->F;
+  if ((st = check_shape(T, E, H, 32, k))) return st;
+  if (E < 2 || E % 2) return fail(MOE_ERR_INVALID_ARG, "E=%lld must be even and >= 2 for the prerouter", (long long)E);
+  if (F < 32 || F > 4096 || F % 32)
+    return fail(MOE_ERR_INVALID_ARG, "F=%lld must be a multiple of 32 in [32, 4096]", (long long)F);
+  if (!head->w1 || !head->w2 || !head->wl) return fail(MOE_ERR_INVALID_ARG, "w1, w2 or wl is NULL");
+  if (!aligned(head->w1, 16) || !aligned(head->w2, 16) || !aligned(head->wl, 16) ||
+      (head->b1 && !aligned(head->b1, 4)) || (head->b2 && !aligned(head->b2, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "head weights must be 16-byte aligned and biases 4-byte aligned");
+  return MOE_OK;
+}
+
 size_t moe_prerouter_workspace_bytes(int32_t T, int32_t E, int32_t F) {
   if (!head_shape_ok(T, E, F)) return 0;
   // fc1 activations [T][F], residual-path partials [T][E], logits [T][E]
@@ -411,16 +426,8 @@ moe_status moe_prerouter_forward(const void* x, int32_t xtype, int32_t T, const 
                                  void* stream) {
   moe_status st;
   if ((st = check_x(x, xtype))) return st;
-  if (!head) return fail(MOE_ERR_INVALID_ARG, "prerouter struct is NULL");
+  if ((st = check_head(head, T, k))) return st;
   const int64_t H = head->H, E = head->E, F = head->F;
-  if ((st = check_shape(T, E, H, 32, k))) return st;
-  if (E < 2 || E % 2) return fail(MOE_ERR_INVALID_ARG, "E=%lld must be even and >= 2 for the prerouter", (long long)E);
-  if (F < 32 || F > 4096 || F % 32)
-    return fail(MOE_ERR_INVALID_ARG, "F=%lld must be a multiple of 32 in [32, 4096]", (long long)F);
-  if (!head->w1 || !head->w2 || !head->wl) return fail(MOE_ERR_INVALID_ARG, "w1, w2 or wl is NULL");
-  if (!aligned(head->w1, 16) || !aligned(head->w2, 16) || !aligned(head->wl, 16) ||
-      (head->b1 && !aligned(head->b1, 4)) || (head->b2 && !aligned(head->b2, 4)))
-    return fail(MOE_ERR_INVALID_ARG, "head weights must be 16-byte aligned and biases 4-byte aligned");
   if ((cur && !aligned(cur, 4)) || (prev && !aligned(prev, 4)))
     return fail(MOE_ERR_INVALID_ARG, "cur or prev is not 4-byte aligned");
   if (!topk_idx != !topk_gate) return fail(MOE_ERR_INVALID_ARG, "only one of topk_idx and topk_gate is NULL");
@@ -473,6 +480,46 @@ moe_status moe_qlinear_lora_forward(const void* x, int32_t xtype, int32_t T, con
                                              w->scales, lora_a, lora_b, r, scale, at<float>(ws, 0), y,
                                              static_cast<hipStream_t>(stream)),
                     "quantized linear with LoRA");
+}
+
+moe_status moe_prerouted_layer_forward(const void* x, int32_t xtype, int32_t T, const float* logits,
+                                       const moe_experts* ex, int32_t k, uint32_t flags, float* y,
+                                       int32_t* topk_idx_out, float* topk_gate_out, const moe_prerouter* head,
+                                       const int32_t* prev_idx, float* logits_next, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  moe_status st;
+  moe::ExpertsDev d;
+  Layout L;
+  if ((st = check_layer_args(x, xtype, T, ex, k, flags, y, ws, ws_bytes, &d, &L))) return st;
+  if (!logits) return fail(MOE_ERR_INVALID_ARG, "logits is NULL");
+  if (!aligned(logits, 16)) return fail(MOE_ERR_INVALID_ARG, "logits is not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!head) return layer_from_logits(x, xtype, T, d, k, flags, logits, 1, y, topk_idx_out, topk_gate_out, ws, L, s);
+  if ((st = check_head(head, T, k))) return st;
+  if (head->H != d.H || head->E != d.E)
+    return fail(MOE_ERR_INVALID_ARG, "head (H=%d, E=%d) does not match the experts (H=%d, E=%d)", head->H, head->E,
+                d.H, d.E);
+  if (!topk_idx_out) return fail(MOE_ERR_INVALID_ARG, "topk_idx_out is NULL (the head reads this layer's routing)");
+  if (!logits_next || !aligned(logits_next, 16))
+    return fail(MOE_ERR_INVALID_ARG, "logits_next is NULL or not 16-byte aligned");
+  if (prev_idx && !aligned(prev_idx, 4)) return fail(MOE_ERR_INVALID_ARG, "prev_idx is not 4-byte aligned");
+  const size_t base = align256(L.total);
+  const size_t need = base + moe_prerouter_workspace_bytes(T, head->E, head->F);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  const moe::HeadDev hd{head->H, head->E, head->F, head->w1, head->b1, head->w2, head->b2, head->wl};
+  float* act = at<float>(ws, base);
+  float* part = at<float>(ws, base + align256((size_t)T * head->F * 4));
+  const int renorm = (flags & MOE_FLAG_RENORM) ? 1 : 0;
+  if (T == 1 && !(flags & MOE_FLAG_PATH_GEMM) && moe::prerouted_t1_fusable(d, xtype, hd))
+    return hip_status(moe::launch_prerouted_t1(x, xtype, d, k, renorm, logits, at<int32_t>(ws, L.idx),
+                                               at<float>(ws, L.gate), topk_idx_out, topk_gate_out,
+                                               at<float>(ws, L.h), y, hd, prev_idx, act, part, logits_next, s),
+                      "prerouted decode (one token)");
+  if ((st = layer_from_logits(x, xtype, T, d, k, flags, logits, 1, y, topk_idx_out, topk_gate_out, ws, L, s)))
+    return st;
+  return hip_status(moe::launch_prerouter(x, xtype, T, hd, topk_idx_out, prev_idx, k, renorm, act, part, logits_next,
+                                          nullptr, nullptr, s),
+                    "prerouter head");
 }
 
 moe_status moe_stream_read(const void* buf, int64_t bytes, void* stream) {

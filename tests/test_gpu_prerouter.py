@@ -186,3 +186,43 @@ def test_head_logits_drive_experts_from_logits(T, path):
     rex = oracle.quantize_experts(wgu, wd, rq.MOE_Q_INT4)
     yref = oracle.gather_forward(x, rex, ref[0], ref[1])
     assert rel_norm_err(y.cpu().numpy(), yref) <= Y_REL_NORM
+
+
+# T, codec, activations, I, F: the first four run fused (head rows inside the
+# expert launches); I = 2048, F = 2048 and T = 3 take the call-after-call path
+PREROUTED = [(1, synth.SYM8, synth.F16, 512, 256), (1, synth.INT4, synth.F16, 256, 96),
+             (1, synth.SYM8, synth.BF16, 128, 128), (1, synth.INT4, synth.F32, 1024, 1024),
+             (1, synth.SYM8, synth.F16, 2048, 128), (1, synth.INT4, synth.F16, 128, 2048),
+             (3, synth.SYM8, synth.F16, 128, 128)]
+
+
+@pytest.mark.parametrize("T,scheme,xtype,I,F", PREROUTED)
+def test_prerouted_layer(T, scheme, xtype, I, F):
+    """One prerouted decode layer: experts on the predicted logits, and the next
+    layer's head on this layer's input and routing."""
+    H, E, k = 512, 64, 6
+    say(f"prerouted layer T={T} scheme={scheme} xtype={xtype} I={I} F={F}")
+    head, x, _, prev, _ = _case(T, H, E, F, k, xtype, seed=50 + I + F + T)
+    g = np.random.default_rng(50 + I + F)
+    logits = (g.standard_normal((T, E)) * 2.0).astype(np.float32)   # predicted for this layer
+    wgu = (g.standard_normal((E, 2 * I, H)) * 0.02).astype(np.float32)
+    wd = (g.standard_normal((E, H, I)) * 0.02).astype(np.float32)
+    ex = rq.quantize_experts(torch.from_numpy(wgu).cuda(), torch.from_numpy(wd).cuda(), scheme)
+    xd = to_dev_x(x, xtype)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    nxt = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    y = rq.moe_prerouted_layer_forward(xd, torch.from_numpy(logits).cuda(), ex, k, _dev_head(head), _dev_ids(prev), idx,
+                                       nxt, gate_out=gate)
+    y_last = rq.moe_prerouted_layer_forward(xd, torch.from_numpy(logits).cuda(), ex, k, None, None, idx, None)
+    torch.cuda.synchronize()
+    bf16 = xtype == synth.BF16
+    ridx, rgate = oracle.topk_logits(logits, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
+    rex = oracle.quantize_experts(wgu, wd, scheme)
+    yref = oracle.gather_forward(x, rex, ridx, rgate, bf16=bf16)
+    assert rel_norm_err(y.cpu().numpy(), yref) <= Y_REL_NORM
+    assert rel_norm_err(y_last.cpu().numpy(), yref) <= Y_REL_NORM
+    nref = oracle.prerouter(x, head, ridx, prev, k, bf16=bf16)[2]
+    assert rel_inf_err(nxt.cpu().numpy(), nref) <= HEAD_LOGIT_TOL

@@ -126,3 +126,14 @@ def test_group_matches_sorted_by_expert_then_flat_id():
 def test_group_rejects_out_of_range_ids():
     with pytest.raises(ValueError):
         oracle.group(np.array([[0, 16]], dtype=np.int32), 16)
+
+
+def test_topk_on_given_logits_matches_the_router():
+    """Top-k on handed-in logits is the router's step after its gate linear."""
+    x, R = _case(6, 128, 40, 21)
+    lg = oracle.logits(x, R).astype(np.float32)
+    for flags in (0, oracle.RENORM):
+        idx, gate = oracle.topk_logits(lg, 5, flags)
+        ridx, rgate = oracle.route(x, R, 5, flags)
+        assert np.array_equal(idx, ridx)
+        assert np.allclose(gate, rgate, rtol=1e-6, atol=1e-7)
