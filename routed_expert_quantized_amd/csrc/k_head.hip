@@ -12,7 +12,10 @@
 // the sum of the 2k entries at the routed ids, gathered from the row itself.
 // fc1 and the residual path both read the whole input, so they share the first
 // launch (one workgroup per output row and group of tokens, the row's hidden
-// part in registers); fc2 needs all of fc1's outputs and is the second launch.
+// part in registers); from 16 tokens the hidden-part products run instead on
+// the fp32 matrix cores (the router's logits kernel) and a small epilogue adds
+// the routed columns, the biases and the GELU. fc2 needs all of fc1's outputs
+// and is the next launch.
 // The top-k follows as the router's one-wave kernel, or, for a few tokens of a
 // narrow head, inside the second launch. A caller that hands the logits to the
 // next layer's expert call skips it: that call takes the top-k inside its own
@@ -39,6 +42,42 @@ __global__ __launch_bounds__(64 * kHeadWaves) void k_head_stage2(
     const float* __restrict__ act, const float* __restrict__ part, const float* __restrict__ w2, int T, int E,
     int F, float* __restrict__ logits) {
   head_stage2_body<NCHF, TU>(blockIdx.x, blockIdx.y, kHeadWaves, act, part, w2, T, E, F, logits);
+}
+
+// Stage 1 of a batch from the matrix-core products: the partial planes of
+// W1 x (nsplit1 planes [T][F]) and Wl x (nsplit2 planes [T][E]) are added in
+// plane order, then the k-hot columns and the bias, and fc1's rows take the
+// GELU. One thread per (token, row).
+__global__ __launch_bounds__(256) void k_head_epilogue(const float* __restrict__ raw1, int nsplit1,
+                                                       const float* __restrict__ raw2, int nsplit2, int T, int H,
+                                                       int E, int F, const float* __restrict__ W1,
+                                                       const float* __restrict__ b1, const float* __restrict__ Wl,
+                                                       const float* __restrict__ b2, const int32_t* __restrict__ cur,
+                                                       const int32_t* __restrict__ prev, int k,
+                                                       float* __restrict__ act, float* __restrict__ part) {
+  const int nbx = (F + E + 255) / 256;
+  const int t = blockIdx.x / nbx;
+  const int i = (blockIdx.x % nbx) * 256 + threadIdx.x;
+  if (i >= F + E) return;
+  const bool fc1 = i < F;
+  const int r = fc1 ? i : i - F;
+  const int R = fc1 ? F : E;
+  const float* raw = fc1 ? raw1 : raw2;
+  const int ns = fc1 ? nsplit1 : nsplit2;
+  const int64_t plane = (int64_t)T * R;
+  float z = raw[(int64_t)t * R + r];
+  for (int q = 1; q < ns; ++q) z += raw[q * plane + (int64_t)t * R + r];
+  const float* row = (fc1 ? W1 : Wl) + (int64_t)r * (H + 2 * E);
+  float g = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    if (cur) g += row[H + cur[(int64_t)t * k + j]];
+    if (prev) g += row[H + E + prev[(int64_t)t * k + j]];
+  }
+  z += g;
+  const float* bias = fc1 ? b1 : b2;
+  if (bias) z += bias[r];
+  if (fc1) act[(int64_t)t * F + r] = gelu_erf(z);
+  else part[(int64_t)t * E + r] = z;
 }
 
 // Stage 2 with the top-k, for a few tokens of a narrow head (F <= 256, E <=
@@ -99,14 +138,27 @@ __global__ __launch_bounds__(64 * kFuseWaves) void k_head_stage2_topk(
 
 hipError_t launch_prerouter(const void* x, int xtype, int T, const HeadDev& hd, const int32_t* cur,
                             const int32_t* prev, int k, int renorm, float* act, float* part, float* logits,
-                            int32_t* idx, float* gate, hipStream_t s) {
+                            int32_t* idx, float* gate, float* raw, hipStream_t s) {
   const int H = hd.H, E = hd.E, F = hd.F;
-  // stage 1: a = gelu(fc1(f)) for F rows, part = l(f) + b2 for E rows
-  {
+  hipError_t e;
+  if (T >= kMfmaLogitsMinT) {
+    // a batch: the hidden-part products on the fp32 matrix cores (the router's
+    // logits kernel with the head's row stride), then the epilogue
+    const int64_t ldx = (int64_t)H + 2 * E;
+    float* raw1 = raw;
+    float* raw2 = raw + logits_max_splits(T, F) * (int64_t)T * F;
+    int ns1 = 1, ns2 = 1;
+    e = launch_logits(x, xtype, T, H, hd.w1, F, raw1, &ns1, nullptr, s, ldx);
+    if (e != hipSuccess) return e;
+    e = launch_logits(x, xtype, T, H, hd.wl, E, raw2, &ns2, nullptr, s, ldx);
+    if (e != hipSuccess) return e;
+    MOE_LAUNCH(MOE_KERNEL_HEAD, k_head_epilogue, dim3((unsigned)(((F + E + 255) / 256) * T)), dim3(256), 0, s, raw1, ns1,
+               raw2, ns2, T,
+               H, E, F, hd.w1, hd.b1, hd.wl, hd.b2, cur, prev, k, act, part);
+  } else {
+    // stage 1 of a few tokens: a = gelu(fc1(f)) for F rows, part = l(f) + b2 for
+    // E rows, one workgroup per row and group of 4 tokens
     const int nch = ((H + 255) / 256 + kHeadWaves - 1) / kHeadWaves;
-    // groups of 4 tokens per workgroup: enough workgroups to fill the GPU,
-    // few enough re-reads of each weight row
-    const int groups = T <= 16 ? 1 : T <= 64 ? 4 : 8;
     auto go = [&](auto NC, auto TUc, auto GC) {
       constexpr int N = decltype(NC)::value, U = decltype(TUc)::value, G = decltype(GC)::value;
       const dim3 grid(F + E, (T + U * G - 1) / (U * G)), block(64 * kHeadWaves);
@@ -120,15 +172,13 @@ hipError_t launch_prerouter(const void* x, int xtype, int T, const HeadDev& hd, 
       using I1 = std::integral_constant<int, 1>;
       using I4 = std::integral_constant<int, 4>;
       if (T == 1) go(NC, I1{}, I1{});
-      else if (groups == 1) go(NC, I4{}, I1{});
-      else if (groups == 4) go(NC, I4{}, I4{});
-      else go(NC, I4{}, std::integral_constant<int, 8>{});
+      else go(NC, I4{}, I1{});
     };
     if (nch <= 1) with_tu(std::integral_constant<int, 1>{});
     else if (nch <= 2) with_tu(std::integral_constant<int, 2>{});
     else with_tu(std::integral_constant<int, 4>{});
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   // stage 2: logits = part + fc2(a), then the top-k (in the same kernel for a few tokens)
   const int nchf = (F + 255) / 256;

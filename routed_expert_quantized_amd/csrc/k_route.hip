@@ -307,7 +307,7 @@ typedef float float4v_r __attribute__((ext_vector_type(4)));
 template <int XT, int MTT, int NTT>
 __global__ __launch_bounds__(1024) void k_logits_mfma(const void* __restrict__ x, int T, int H,
                                                       const float* __restrict__ R, int E, float* __restrict__ logits,
-                                                      int kw) {
+                                                      int kw, int64_t ldr) {
   extern __shared__ float red[];  // [waves][MTT*NTT*4][64]
   // split blockIdx.z takes K range [z*nw*kw, (z+1)*nw*kw) into plane z
   logits += (int64_t)blockIdx.z * T * E;
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(1024) void k_logits_mfma(const void* __restrict__ x
 #pragma unroll
   for (int mt = 0; mt < MTT; ++mt) xrow[mt] = (int64_t)min(t0 + 16 * mt + r, T - 1) * H;
 #pragma unroll
-  for (int nt = 0; nt < NTT; ++nt) rrow[nt] = R + (int64_t)min(e0 + 16 * nt + r, E - 1) * H;
+  for (int nt = 0; nt < NTT; ++nt) rrow[nt] = R + (int64_t)min(e0 + 16 * nt + r, E - 1) * ldr;
   float4v_r acc[MTT][NTT];
 #pragma unroll
   for (int mt = 0; mt < MTT; ++mt)
@@ -483,8 +483,9 @@ __global__ __launch_bounds__(1024) void k_logits_bf16x3(const uint16_t* __restri
 constexpr int kLogitsWaves = 4;
 
 hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R, int E, float* logits,
-                         int* nsplit, uint16_t* r3, hipStream_t s) {
+                         int* nsplit, uint16_t* r3, hipStream_t s, int64_t ldr) {
   *nsplit = 1;
+  if (ldr == 0) ldr = H;
   if (T >= kMfmaLogitsMinT) {
     // bf16 activations of a large batch: the split-weight bf16 kernel
     const bool split3 = xtype == MOE_BF16 && r3 != nullptr && T >= kSplitRouterMinT;
@@ -518,7 +519,7 @@ hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R,
                    static_cast<const uint16_t*>(x), T, H, static_cast<const uint16_t*>(r3), E, logits, kw);
       else
         MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_mfma<X_, M_, N_>), grid, dim3(64 * nw), lds, s, x, T, H, R, E,
-                   logits, kw);
+                   logits, kw, ldr);
     };
     auto with_tile = [&](auto XC) {
       if (mtt == 2 && ntt == 2) go(XC, std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});

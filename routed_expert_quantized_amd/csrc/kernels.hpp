@@ -60,8 +60,10 @@ inline int logits_max_splits(int64_t T, int64_t E) {
 // Writes *nsplit partial planes logits[s][T][E] (one for T < kMfmaLogitsMinT).
 // r3: scratch for the router split into three bf16 planes [3][E][H] (used for
 // bf16 activations from kSplitRouterMinT tokens; may be null below that).
+// ldr: row stride of R in elements (0: H); another stride is only for the
+// fp32 matrix-core path (T >= kMfmaLogitsMinT, r3 null).
 hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R, int E, float* logits,
-                         int* nsplit, uint16_t* r3, hipStream_t s);
+                         int* nsplit, uint16_t* r3, hipStream_t s, int64_t ldr = 0);
 hipError_t launch_topk(const float* logits, int nsplit, int T, int E, int k, int renorm, int32_t* idx, float* gate,
                        int32_t* idx2, float* gate2, hipStream_t s);
 hipError_t launch_group(const int32_t* idx, int T, int k, int E, const GroupBufs& g, hipStream_t s);
@@ -117,10 +119,16 @@ struct HeadDev {
 };
 // fc1 + GELU into act [T][F] and the residual path + fc2's bias into part
 // [T][E]; then part + fc2 into logits [T][E] and the router's top-k into
-// idx/gate [T][k]. cur/prev [T][k] or null.
+// idx/gate [T][k] (skipped when idx is null). cur/prev [T][k] or null. raw:
+// scratch of head_raw_floats(T, E, F) floats (the matrix-core partial planes
+// of a batch; unused below kMfmaLogitsMinT tokens).
+inline int64_t head_raw_floats(int64_t T, int64_t E, int64_t F) {
+  if (T < kMfmaLogitsMinT) return 0;
+  return logits_max_splits(T, F) * T * F + logits_max_splits(T, E) * T * E;
+}
 hipError_t launch_prerouter(const void* x, int xtype, int T, const HeadDev& hd, const int32_t* cur,
                             const int32_t* prev, int k, int renorm, float* act, float* part, float* logits,
-                            int32_t* idx, float* gate, hipStream_t s);
+                            int32_t* idx, float* gate, float* raw, hipStream_t s);
 // Quantized linear with an unmerged LoRA delta: u = A x into u [T][r] (when
 // r > 0), then y [T][N] = W_q x + c * B u.
 hipError_t launch_qlinear_lora(const void* x, int xtype, int T, int N, int K, int scheme, const uint8_t* codes,

@@ -416,8 +416,10 @@ static moe_status check_head(const moe_prerouter* head, int64_t T, int64_t k) {
 
 size_t moe_prerouter_workspace_bytes(int32_t T, int32_t E, int32_t F) {
   if (!head_shape_ok(T, E, F)) return 0;
-  // fc1 activations [T][F], residual-path partials [T][E], logits [T][E]
-  return align256((size_t)T * F * 4) + 2 * align256((size_t)T * E * 4);
+  // fc1 activations [T][F], residual-path partials [T][E], logits [T][E], and
+  // for a batch the matrix-core partial planes
+  return align256((size_t)T * F * 4) + 2 * align256((size_t)T * E * 4) +
+         align256((size_t)moe::head_raw_floats(T, E, F) * 4);
 }
 
 moe_status moe_prerouter_forward(const void* x, int32_t xtype, int32_t T, const moe_prerouter* head,
@@ -442,9 +444,10 @@ moe_status moe_prerouter_forward(const void* x, int32_t xtype, int32_t T, const 
   float* act = at<float>(ws, 0);
   float* part = at<float>(ws, o_part);
   float* lg = logits ? logits : at<float>(ws, o_lg);
+  float* raw = at<float>(ws, o_lg + align256((size_t)T * E * 4));
   const moe::HeadDev hd{(int)H, (int)E, (int)F, head->w1, head->b1, head->w2, head->b2, head->wl};
   return hip_status(moe::launch_prerouter(x, xtype, T, hd, cur, prev, k, (flags & MOE_FLAG_RENORM) ? 1 : 0, act, part,
-                                          lg, topk_idx, topk_gate, static_cast<hipStream_t>(stream)),
+                                          lg, topk_idx, topk_gate, raw, static_cast<hipStream_t>(stream)),
                     "prerouter head");
 }
 
@@ -509,6 +512,7 @@ moe_status moe_prerouted_layer_forward(const void* x, int32_t xtype, int32_t T, 
   const moe::HeadDev hd{head->H, head->E, head->F, head->w1, head->b1, head->w2, head->b2, head->wl};
   float* act = at<float>(ws, base);
   float* part = at<float>(ws, base + align256((size_t)T * head->F * 4));
+  float* raw = at<float>(ws, base + align256((size_t)T * head->F * 4) + 2 * align256((size_t)T * head->E * 4));
   const int renorm = (flags & MOE_FLAG_RENORM) ? 1 : 0;
   if (T == 1 && !(flags & MOE_FLAG_PATH_GEMM) && moe::prerouted_t1_fusable(d, xtype, hd))
     return hip_status(moe::launch_prerouted_t1(x, xtype, d, k, renorm, logits, at<int32_t>(ws, L.idx),
@@ -518,7 +522,7 @@ moe_status moe_prerouted_layer_forward(const void* x, int32_t xtype, int32_t T, 
   if ((st = layer_from_logits(x, xtype, T, d, k, flags, logits, 1, y, topk_idx_out, topk_gate_out, ws, L, s)))
     return st;
   return hip_status(moe::launch_prerouter(x, xtype, T, hd, topk_idx_out, prev_idx, k, renorm, act, part, logits_next,
-                                          nullptr, nullptr, s),
+                                          nullptr, nullptr, raw, s),
                     "prerouter head");
 }
 
