@@ -90,8 +90,10 @@ CASES = [
     ("unfused_edge", 5, 512, 64, 96, 6, synth.BF16, True, True),
     ("fused_e96", 2, 256, 96, 256, 5, synth.F32, True, True),     # 8 rows per wave, two logits per lane
     ("wide_few", 1, 512, 64, 512, 4, synth.F16, True, True),      # one token, F past the fused kernel's 256
-    ("many", 203, 256, 16, 64, 4, synth.BF16, True, True),        # 32 tokens per workgroup, ragged last group
-    ("mid", 37, 384, 32, 64, 2, synth.F16, True, True),           # 16 tokens per workgroup, ragged
+    ("many", 203, 256, 16, 64, 4, synth.BF16, True, True),        # matrix-core stage 1, ragged token tiles
+    ("mid", 37, 384, 32, 64, 2, synth.F16, True, True),           # matrix-core stage 1
+    ("ragged_batch", 20, 256, 10, 64, 3, synth.F16, True, True),  # matrix-core stage 1, E not a multiple of 16
+    ("batched_f32", 16, 512, 64, 128, 4, synth.F32, False, False),  # matrix cores from fp32 input, no history
 ]
 
 
