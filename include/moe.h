@@ -317,7 +317,8 @@ moe_status moe_prerouter_forward(const void* x, int32_t xtype, int32_t T, const 
  *   logits:        [T][E] fp32 predicted for this layer (16-byte aligned).
  *   topk_idx_out:  out [T][k], this layer's routing; required with a head (it
  *                  is the next token's prev_idx).
- *   prev_idx:      [T][k] this layer's routing at the previous token, or NULL.
+ *   prev_idx:      [T][k] this layer's routing at the previous token, or NULL;
+ *                  not the same array as topk_idx_out.
  *   logits_next:   out [T][E] fp32, the next layer's predicted logits (16-byte
  *                  aligned); required with a head. It must not alias `logits`.
  *   ws:            moe_workspace_bytes(T, E, H, I, k, scheme) rounded up to 256,

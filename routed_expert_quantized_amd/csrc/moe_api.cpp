@@ -506,6 +506,9 @@ moe_status moe_prerouted_layer_forward(const void* x, int32_t xtype, int32_t T, 
   if (!logits_next || !aligned(logits_next, 16))
     return fail(MOE_ERR_INVALID_ARG, "logits_next is NULL or not 16-byte aligned");
   if (prev_idx && !aligned(prev_idx, 4)) return fail(MOE_ERR_INVALID_ARG, "prev_idx is not 4-byte aligned");
+  // the fused launches read these while they write the others
+  if (prev_idx && prev_idx == topk_idx_out) return fail(MOE_ERR_INVALID_ARG, "prev_idx aliases topk_idx_out");
+  if (logits_next == logits) return fail(MOE_ERR_INVALID_ARG, "logits_next aliases logits");
   const size_t base = align256(L.total);
   const size_t need = base + moe_prerouter_workspace_bytes(T, head->E, head->F);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);

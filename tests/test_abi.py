@@ -236,3 +236,26 @@ def test_qlinear_lora_validation(L):
     assert call(y=None) == rq.MOE_ERR_INVALID_ARG
     assert call(ws=None) == rq.MOE_ERR_WORKSPACE
     assert call(T=4096, nws=1024) == rq.MOE_ERR_WORKSPACE
+
+
+def test_prerouted_layer_validation(L):
+    ex = _experts(E=256, H=2048, I=512)
+    hd = rq._Prerouter(2048, 256, 256, FAKE.value, None, FAKE.value, None, FAKE.value)
+    other = ctypes.c_void_p(0x20000)
+
+    def call(lg=FAKE, e=ex, h=hd, idx=FAKE, prev=None, nxt=other, y=FAKE, ws=FAKE, nws=1 << 30):
+        return L.moe_prerouted_layer_forward(FAKE, rq.MOE_F16, 1, lg, ctypes.byref(e), 8, 1, y, idx, None,
+                                             ctypes.byref(h) if h is not None else None, prev, nxt, ws, nws, None)
+
+    assert call(lg=None) == rq.MOE_ERR_INVALID_ARG
+    assert call(idx=None) == rq.MOE_ERR_INVALID_ARG
+    assert b"topk_idx_out" in L.moe_last_error()
+    assert call(nxt=None) == rq.MOE_ERR_INVALID_ARG
+    assert call(nxt=FAKE) == rq.MOE_ERR_INVALID_ARG        # the same array as logits
+    assert b"aliases" in L.moe_last_error()
+    assert call(prev=FAKE) == rq.MOE_ERR_INVALID_ARG       # the same array as topk_idx_out
+    assert call(h=rq._Prerouter(2048, 128, 256, FAKE.value, None, FAKE.value, None, FAKE.value)) == \
+        rq.MOE_ERR_INVALID_ARG                              # head E differs from the experts'
+    assert call(h=rq._Prerouter(2048, 256, 100, FAKE.value, None, FAKE.value, None, FAKE.value)) == \
+        rq.MOE_ERR_INVALID_ARG
+    assert call(nws=1 << 16) == rq.MOE_ERR_WORKSPACE
