@@ -15,11 +15,9 @@
 // part in registers); from 16 tokens the hidden-part products run instead on
 // the fp32 matrix cores (the router's logits kernel) and a small epilogue adds
 // the routed columns, the biases and the GELU. fc2 needs all of fc1's outputs
-// and is the next launch.
-// The top-k follows as the router's one-wave kernel, or, for a few tokens of a
-// narrow head, inside the second launch. A caller that hands the logits to the
-// next layer's expert call skips it: that call takes the top-k inside its own
-// first kernel.
+// and is the next launch. The top-k follows as the router's one-wave kernel; a
+// caller that hands the logits to the next layer's expert call skips it, since
+// that call takes the top-k inside its own first kernel.
 #include "common.hpp"
 #include "head_rows.hpp"
 #include "kernels.hpp"
@@ -80,60 +78,6 @@ __global__ __launch_bounds__(256) void k_head_epilogue(const float* __restrict__
   else part[(int64_t)t * E + r] = z;
 }
 
-// Stage 2 with the top-k, for a few tokens of a narrow head (F <= 256, E <=
-// kFuseWaves * kFuseRows): one 1024-thread workgroup per token. Wave w takes
-// rows w, w + 16, ...; every lane issues all its row loads before the first
-// sum, so the whole of fc2 is in flight at once. The E logits land in LDS and
-// wave 0 runs the router's top-k on them; they also go out to memory.
-constexpr int kFuseTopkMaxT = 4;
-constexpr int kFuseWaves = 16;
-constexpr int kFuseRows = 16;
-
-template <int RPW, int VPL>
-__global__ __launch_bounds__(64 * kFuseWaves) void k_head_stage2_topk(
-    const float* __restrict__ act, const float* __restrict__ part, const float* __restrict__ w2, int E, int F,
-    float* __restrict__ logits, int k, int renorm, int32_t* __restrict__ idx, float* __restrict__ gate) {
-  __shared__ float lg[64 * VPL];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int t = blockIdx.x;
-  const bool ok = lane * 4 < F;
-  const int col = min(lane * 4, F - 4);
-  const float4 v = *reinterpret_cast<const float4*>(act + (int64_t)t * F + col);
-  float4 r[RPW];
-#pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int e = min(w + kFuseWaves * i, E - 1);
-    r[i] = *reinterpret_cast<const float4*>(w2 + (int64_t)e * F + col);
-  }
-#pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int e = w + kFuseWaves * i;
-    float acc = 0.0f;
-    if (ok) {
-      acc = fmaf(r[i].x, v.x, acc);
-      acc = fmaf(r[i].y, v.y, acc);
-      acc = fmaf(r[i].z, v.z, acc);
-      acc = fmaf(r[i].w, v.w, acc);
-    }
-    acc = wave_sum(acc);
-    if (lane == 0 && e < E) {
-      const float z = part[(int64_t)t * E + e] + acc;
-      lg[e] = z;
-      logits[(int64_t)t * E + e] = z;
-    }
-  }
-  __syncthreads();
-  if (w == 0) {
-    int my_idx;
-    float my_gate;
-    wave_topk<VPL>(lg, E, k, renorm != 0, my_idx, my_gate);
-    if (lane < k) {
-      idx[(int64_t)t * k + lane] = my_idx;
-      gate[(int64_t)t * k + lane] = my_gate;
-    }
-  }
-}
-
 }  // namespace
 
 hipError_t launch_prerouter(const void* x, int xtype, int T, const HeadDev& hd, const int32_t* cur,
@@ -180,7 +124,7 @@ hipError_t launch_prerouter(const void* x, int xtype, int T, const HeadDev& hd, 
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // stage 2: logits = part + fc2(a), then the top-k (in the same kernel for a few tokens)
+  // stage 2: logits = part + fc2(a), then the router's top-k
   const int nchf = (F + 255) / 256;
   auto with_nchf = [&](auto fn) {
     if (nchf <= 1) fn(std::integral_constant<int, 1>{});
@@ -189,20 +133,6 @@ hipError_t launch_prerouter(const void* x, int xtype, int T, const HeadDev& hd, 
     else if (nchf <= 8) fn(std::integral_constant<int, 8>{});
     else fn(std::integral_constant<int, 16>{});
   };
-  if (idx && T <= kFuseTopkMaxT && F <= 256 && E <= kFuseWaves * kFuseRows) {
-    const int rpw = (E + kFuseWaves - 1) / kFuseWaves;
-    const int vpl = (E + 63) / 64;
-    auto go = [&](auto RC, auto VC) {
-      constexpr int R = decltype(RC)::value, V = decltype(VC)::value;
-      MOE_LAUNCH(MOE_KERNEL_HEAD, (k_head_stage2_topk<R, V>), dim3(T), dim3(64 * kFuseWaves), 0, s, act, part, hd.w2,
-                 E, F, logits, k, renorm, idx, gate);
-    };
-    if (rpw <= 1) go(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
-    else if (rpw <= 4) go(std::integral_constant<int, 4>{}, std::integral_constant<int, 1>{});
-    else if (vpl <= 2) go(std::integral_constant<int, 8>{}, std::integral_constant<int, 2>{});
-    else go(std::integral_constant<int, kFuseRows>{}, std::integral_constant<int, 4>{});
-    return hipGetLastError();
-  }
   with_nchf([&](auto NC) {
     constexpr int N = decltype(NC)::value;
     constexpr int U = N >= 8 ? 1 : N >= 4 ? 2 : 4;  // tokens per workgroup, within the register budget

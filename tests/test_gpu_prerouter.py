@@ -86,10 +86,10 @@ CASES = [
     ("first_token", 5, 256, 16, 64, 4, synth.F16, False, True),  # no routing history yet
     ("max", 3, 4096, 1024, 4096, 16, synth.BF16, True, True),  # largest H, E, F and k
     ("min", 2, 32, 2, 32, 1, synth.F32, True, True),
-    ("fused_topk_edge", 4, 512, 64, 96, 6, synth.F16, True, True),  # most tokens whose top-k is fused
-    ("unfused_edge", 5, 512, 64, 96, 6, synth.BF16, True, True),
-    ("fused_e96", 2, 256, 96, 256, 5, synth.F32, True, True),     # 8 rows per wave, two logits per lane
-    ("wide_few", 1, 512, 64, 512, 4, synth.F16, True, True),      # one token, F past the fused kernel's 256
+    ("four_tokens", 4, 512, 64, 96, 6, synth.F16, True, True),
+    ("five_tokens", 5, 512, 64, 96, 6, synth.BF16, True, True),
+    ("e96", 2, 256, 96, 256, 5, synth.F32, True, True),           # two logits per lane in the top-k
+    ("wide_few", 1, 512, 64, 512, 4, synth.F16, True, True),      # one token, F over two 256 chunks
     ("many", 203, 256, 16, 64, 4, synth.BF16, True, True),        # matrix-core stage 1, ragged token tiles
     ("mid", 37, 384, 32, 64, 2, synth.F16, True, True),           # matrix-core stage 1
     ("ragged_batch", 20, 256, 10, 64, 3, synth.F16, True, True),  # matrix-core stage 1, E not a multiple of 16
