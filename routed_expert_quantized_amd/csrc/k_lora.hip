@@ -7,7 +7,8 @@
 //
 // Two launches. The first makes u = A x (r values per token; A is small and
 // read once). The second is the quantized matvec (one row per wave for a single
-// token, several for a batch), with the delta folded into the same wave-wide sum:
+// token, several for a batch; from 16 fp16 tokens a matrix-core tile), with the
+// delta folded into the same wave-wide sum:
 // lanes 0..r-1 each add scale * B[n][j] * u[j] to their partial before the
 // reduction, so the delta costs r floats of B per row and no extra pass over y.
 #include "common.hpp"
@@ -124,6 +125,87 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_qlinear_lora(
   }
 }
 
+// Batched form for fp16 activations, on the matrix cores. Codes are exact in
+// fp16 and the MFMA's K of 32 is one quantisation block, so each block's fp32
+// partial is multiplied by its row's scale before it joins the sum: the same
+// products and per-block scaling as the matvec, summed in another order. A
+// workgroup owns a 16-token x 16-row tile; its four waves split K and add their
+// partial tiles in LDS. Operand layout of
+// v_mfma_f32_16x16x32_f16: lane l holds A[l%16][8(l/16)+j] and B[8(l/16)+j][l%16]
+// for j < 8, and D[4(l/16)+i][l%16] for i < 4; here A = x (token rows), B =
+// codes (weight rows as columns), D[token][row].
+typedef _Float16 half8_l __attribute__((ext_vector_type(8)));
+typedef float float4_l __attribute__((ext_vector_type(4)));
+
+template <int SCHEME>
+__device__ __forceinline__ half8_l codes8(const uint8_t* __restrict__ row, int k0) {
+  half8_l h;
+  if constexpr (SCHEME == MOE_Q_SYM8) {
+    const uint2 v = *reinterpret_cast<const uint2*>(row + k0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h[j] = (_Float16)(int)(int8_t)(v.x >> (8 * j));
+      h[4 + j] = (_Float16)(int)(int8_t)(v.y >> (8 * j));
+    }
+  } else {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(row + k0 / 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = (_Float16)(((int)(v << (28 - 4 * j))) >> 28);
+  }
+  return h;
+}
+
+template <int SCHEME>
+__global__ __launch_bounds__(64 * kLoraWaves) void k_qlinear_lora_mfma(
+    const uint16_t* __restrict__ x, int T, int N, int K, const uint8_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const float* __restrict__ u, const float* __restrict__ B, int r, float c,
+    float* __restrict__ y) {
+  static_assert(kLoraWaves == 4, "wave w adds the delta of the lane's w-th output row");
+  __shared__ float red[kLoraWaves][4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+  const int nb = K >> 5;
+  const int n = min(n0 + r16, N - 1);   // rows past N are read in bounds and not stored
+  const int ta = min(t0 + r16, T - 1);  // token row of this lane's A operand
+  const uint8_t* crow = codes + (int64_t)n * row_bytes<SCHEME>(K);
+  const uint16_t* srow = scales + (int64_t)n * nb;
+  const uint16_t* xrow = x + (int64_t)ta * K;
+  // the delta of token t0 + 4g + w for this lane's row, before the products so
+  // its loads overlap them; wave w adds it to output i == w
+  const int td = min(t0 + 4 * g + w, T - 1);
+  float d = 0.0f;
+#pragma unroll 8
+  for (int j = 0; j < r; ++j) d = fmaf(B[(int64_t)n * r + j], u[(int64_t)td * r + j], d);
+  // wave w takes blocks [b0, b1) of K
+  const int per = (nb + kLoraWaves - 1) / kLoraWaves;
+  const int b0 = w * per, b1 = min(nb, b0 + per);
+  float4_l acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int b = b0; b < b1; ++b) {
+    const int k0 = 32 * b + 8 * g;
+    const half8_l a = __builtin_bit_cast(half8_l, *reinterpret_cast<const uint4*>(xrow + k0));
+    const half8_l bq = codes8<SCHEME>(crow, k0);
+    const float4_l p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, float4_l{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    const float s = f16_bits_to_f32(srow[b]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(s, p[i], acc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[w][i][lane] = i == w ? fmaf(c, d, acc[i]) : acc[i];
+  __syncthreads();
+  if (w != 0) return;
+  const bool store = n0 + r16 < N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = red[0][i][lane];
+#pragma unroll
+    for (int q = 1; q < kLoraWaves; ++q) v += red[q][i][lane];
+    const int t = t0 + 4 * g + i;
+    if (store && t < T) y[(int64_t)t * N + n] = v;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_qlinear_lora(const void* x, int xtype, int T, int N, int K, int scheme, const uint8_t* codes,
@@ -149,6 +231,15 @@ hipError_t launch_qlinear_lora(const void* x, int xtype, int T, int N, int K, in
     else with_tu(std::integral_constant<int, 4>{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (xtype == MOE_F16 && T >= 16) {
+    const dim3 grid((N + 15) / 16, (T + 15) / 16), block(64 * kLoraWaves);
+    const uint16_t* xh = static_cast<const uint16_t*>(x);
+    if (scheme == MOE_Q_SYM8)
+      MOE_LAUNCH(MOE_KERNEL_LORA, k_qlinear_lora_mfma<MOE_Q_SYM8>, grid, block, 0, s, xh, T, N, K, codes, scales, u, B, r, c, y);
+    else
+      MOE_LAUNCH(MOE_KERNEL_LORA, k_qlinear_lora_mfma<MOE_Q_INT4>, grid, block, 0, s, xh, T, N, K, codes, scales, u, B, r, c, y);
+    return hipGetLastError();
   }
   const int bpl = (K / 32 + 63) / 64;
   // one row per wave for a single token (most workgroups); for a batch, 4 rows

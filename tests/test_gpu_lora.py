@@ -48,7 +48,11 @@ CASES = [
     (1, 1024, 2048, 16, synth.INT4, synth.F16),
     (7, 301, 96, 3, synth.INT4, synth.F32),        # rows not a multiple of 4, K below one 256 chunk
     (5, 130, 4096, 64, synth.SYM8, synth.BF16),    # largest K (two blocks per lane) and r
-    (64, 512, 2048, 16, synth.INT4, synth.F16),    # a batch: token groups of 4
+    (64, 512, 2048, 16, synth.INT4, synth.F16),    # a batch of fp16 tokens: matrix-core tiles
+    (20, 77, 96, 5, synth.SYM8, synth.F16),        # matrix cores, ragged token and row tiles
+    (16, 130, 4096, 64, synth.INT4, synth.F16),    # matrix cores, largest K and r
+    (33, 64, 544, 0, synth.SYM8, synth.F16),       # matrix cores without the delta
+    (40, 96, 256, 8, synth.INT4, synth.BF16),      # a bf16 batch: the matvec form
     (3, 77, 32, 1, synth.SYM8, synth.F32),         # one block per row, rank 1
     (2, 64, 544, 0, synth.INT4, synth.F16),        # r = 0: the plain quantized linear
 ]
