@@ -585,12 +585,14 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
 // a layer runs its experts on the logits its predecessor's head predicted, and
 // its own head predicts the next layer's. The head's stage 1 needs only the
 // layer input and the layer's routing, and its stage 2 only stage 1's output,
-// so each joins an expert launch as extra workgroups: blocks past the expert
-// grid run the head. Two launches per layer, against the router path's three.
+// so each joins an expert launch as extra workgroups ahead of the expert grid.
+// Two launches per layer, against the router path's three.
 
-// Gate/up grid, then F + E head rows (fc1 + GELU, residual path). A head
-// workgroup first picks the layer's routing from the same logits, as the
-// gate/up workgroups do, for the current-token k-hot input.
+// F + E head rows (fc1 + GELU, residual path), then the gate/up grid; the head
+// rows come first so their weight reads, which do not wait for the routing,
+// start with the launch. A head workgroup first picks the layer's routing from
+// the same logits, as the gate/up workgroups do, for the current-token k-hot
+// input.
 template <int SCHEME, int XT, int NBJ, int VPL, int HNCH>
 __global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1_head(
     const void* __restrict__ x, ExpertsDev ex, int k, int renorm, const float* __restrict__ logits,
@@ -598,10 +600,10 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1_head(
     float* __restrict__ gate_user, float* __restrict__ h, int blocks_per_slot, HeadDev hd,
     const int32_t* __restrict__ prev, float* __restrict__ act, float* __restrict__ part) {
   static_assert(kGateUpWaves == kHeadWaves, "head rows run on gate/up-sized workgroups");
-  const int nmain = k * blocks_per_slot;
-  if ((int)blockIdx.x < nmain) {
+  const int nhead = hd.F + hd.E;
+  if ((int)blockIdx.x >= nhead) {
     gate_up_t1_body<SCHEME, XT, NBJ, 1, true, VPL, true>(x, ex, k, renorm, logits, nullptr, idx_ws, gate_ws, idx_user,
-                                                         gate_user, h, blocks_per_slot, blockIdx.x);
+                                                         gate_user, h, blocks_per_slot, (int)blockIdx.x - nhead);
     return;
   }
   __shared__ int32_t cur_sh[kMaxK];
@@ -612,11 +614,12 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1_head(
     if ((int)threadIdx.x < k) cur_sh[threadIdx.x] = my_idx;
   }
   __syncthreads();
-  head_stage1_body<XT, HNCH, 1, 1>((int)blockIdx.x - nmain, 0, x, 1, hd.H, hd.E, hd.F, hd.w1, hd.b1, hd.wl, hd.b2,
-                                   cur_sh, prev, k, act, part);
+  head_stage1_body<XT, HNCH, 1, 1>((int)blockIdx.x, 0, x, 1, hd.H, hd.E, hd.F, hd.w1, hd.b1, hd.wl, hd.b2, cur_sh,
+                                   prev, k, act, part);
 }
 
-// Down grid, then ceil(E / k) workgroups of head stage 2 (one fc2 row per wave).
+// ceil(E / k) workgroups of head stage 2 (one fc2 row per wave), then the down
+// grid.
 template <int SCHEME, int NBJ, int RW, int HNCHF>
 __global__ __launch_bounds__(1024) void k_down_t1_slots_head(ExpertsDev ex, int k, const int32_t* __restrict__ idx,
                                                             const float* __restrict__ gate,
@@ -625,12 +628,12 @@ __global__ __launch_bounds__(1024) void k_down_t1_slots_head(ExpertsDev ex, int 
                                                             const float* __restrict__ part,
                                                             const float* __restrict__ w2, int E, int F,
                                                             float* __restrict__ logits_next) {
-  if ((int)blockIdx.x < nmain) {
-    down_t1_slots_body<SCHEME, NBJ, RW>(ex, k, idx, gate, h16, y, blockIdx.x);
+  const int nhead = (int)gridDim.x - nmain;
+  if ((int)blockIdx.x >= nhead) {
+    down_t1_slots_body<SCHEME, NBJ, RW>(ex, k, idx, gate, h16, y, (int)blockIdx.x - nhead);
     return;
   }
-  head_stage2_body<HNCHF, 1>((int)blockIdx.x - nmain, 0, (int)(blockDim.x >> 6), act, part, w2, 1, E, F,
-                             logits_next);
+  head_stage2_body<HNCHF, 1>((int)blockIdx.x, 0, (int)(blockDim.x >> 6), act, part, w2, 1, E, F, logits_next);
 }
 
 bool prerouted_t1_fusable(const ExpertsDev& ex, int xtype, const HeadDev& hd) {
