@@ -63,14 +63,27 @@ __global__ __launch_bounds__(256) void k_head_epilogue(const float* __restrict__
   const float* raw = fc1 ? raw1 : raw2;
   const int ns = fc1 ? nsplit1 : nsplit2;
   const int64_t plane = (int64_t)T * R;
-  float z = raw[(int64_t)t * R + r];
-  for (int q = 1; q < ns; ++q) z += raw[q * plane + (int64_t)t * R + r];
+  // every load is issued before the first add: the planes, the routed ids,
+  // then the routed columns
+  float pz[kMaxLogitSplits];
+#pragma unroll
+  for (int q = 0; q < kMaxLogitSplits; ++q) pz[q] = q < ns ? raw[q * plane + (int64_t)t * R + r] : 0.0f;
   const float* row = (fc1 ? W1 : Wl) + (int64_t)r * (H + 2 * E);
-  float g = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    if (cur) g += row[H + cur[(int64_t)t * k + j]];
-    if (prev) g += row[H + E + prev[(int64_t)t * k + j]];
+  int id[2 * kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    id[j] = (cur && j < k) ? cur[(int64_t)t * k + j] : -1;
+    id[kMaxK + j] = (prev && j < k) ? E + prev[(int64_t)t * k + j] : -1;
   }
+  float gv[2 * kMaxK];
+#pragma unroll
+  for (int j = 0; j < 2 * kMaxK; ++j) gv[j] = id[j] >= 0 ? row[H + id[j]] : 0.0f;
+  float z = pz[0];
+#pragma unroll
+  for (int q = 1; q < kMaxLogitSplits; ++q) z += pz[q];
+  float g = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 2 * kMaxK; ++j) g += gv[j];
   z += g;
   const float* bias = fc1 ? b1 : b2;
   if (bias) z += bias[r];
