@@ -46,6 +46,8 @@ def _draw(T, N, K, r, xtype, seed):
 CASES = [
     (1, 2048, 2048, 16, synth.SYM8, synth.F16),    # a d_model-wide projection at decode
     (1, 1024, 2048, 16, synth.INT4, synth.F16),
+    (1, 301, 96, 3, synth.INT4, synth.F32),        # one token: ragged rows per workgroup, K below 256
+    (1, 130, 4096, 64, synth.SYM8, synth.BF16),    # one token: largest K and r
     (7, 301, 96, 3, synth.INT4, synth.F32),        # rows not a multiple of 4, K below one 256 chunk
     (5, 130, 4096, 64, synth.SYM8, synth.BF16),    # largest K (two blocks per lane) and r
     (64, 512, 2048, 16, synth.INT4, synth.F16),    # a batch of fp16 tokens: matrix-core tiles
