@@ -516,9 +516,16 @@ def main():
     tokens_per_s_layer = w.T / t_layer_s
 
     # per-kernel durations: eager pass with HIP events around every launch
+    # Each timing step is queued behind a long streaming read (about 1 ms), so
+    # its launches reach the GPU back to back, as in the graph, rather than one
+    # by one with the host's launch gaps in between.
+    spacer = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
+
     def timed_kernel(kid, n_steps):
+        torch.cuda.synchronize()
         with rq.KernelTimer(kid, n_steps * layers_per_step + 8) as t:
             for s in range(n_steps):
+                rq.moe_stream_read(spacer)
                 xbuf.copy_(xs[s % nx])
                 run_layers(s)
         torch.cuda.synchronize()
@@ -534,6 +541,7 @@ def main():
         kids.update(gate_up=rq.MOE_KERNEL_GATE_UP, down=rq.MOE_KERNEL_DOWN)
         dom = "gate_up"
     kern_us = {name: timed_kernel(kid, args.timer_steps) for name, kid in kids.items()}
+    del spacer
     gu_us = kern_us[dom]
     # algorithmic bytes of one launch of the dominant kernel (gate/up stage):
     # routed gate/up codes + scales, the activations, and the SwiGLU output
