@@ -385,6 +385,8 @@ def moe_qlinear_lora_forward(x: torch.Tensor, w: QWeight, lora_a: torch.Tensor |
     _device_tensor(x, "x")
     T = x.shape[0]
     r = 0
+    if (lora_a is None) != (lora_b is None):
+        raise ValueError("lora_a and lora_b must be given together")
     if lora_a is not None:
         _device_tensor(lora_a, "lora_a")
         _device_tensor(lora_b, "lora_b")

@@ -259,3 +259,11 @@ def test_prerouted_layer_validation(L):
     assert call(h=rq._Prerouter(2048, 256, 100, FAKE.value, None, FAKE.value, None, FAKE.value)) == \
         rq.MOE_ERR_INVALID_ARG
     assert call(nws=1 << 16) == rq.MOE_ERR_WORKSPACE
+
+
+def test_binding_rejects_half_an_adapter():
+    import torch
+    qw = rq.QWeight(32, 32, rq.MOE_Q_SYM8, torch.zeros((32, 32), dtype=torch.uint8),
+                    torch.zeros((32, 1), dtype=torch.int16))
+    with pytest.raises(ValueError):
+        rq.moe_qlinear_lora_forward(torch.zeros((1, 32)), qw, torch.zeros((4, 32)), None, 1.0)
