@@ -155,7 +155,13 @@ def prerouted_step(w, xs, nl, pools, routers, ws, seed, K, W, path_flag, rq, syn
     heads = []
     for l in range(nl - 1):
         d = synth.draw_prerouter(seed, w.wid, l, w.H, w.E, F, w.router_std)
-        heads.append(rq.Prerouter(*(torch.from_numpy(d[n]).cuda() for n in ("w1", "b1", "w2", "b2", "wl"))))
+        # fc1 and the residual path in one allocation, the residual rows right
+        # after fc1's, so a batch runs their products as one launch
+        D = w.H + 2 * w.E
+        w1l = torch.from_numpy(np.concatenate([d["w1"].ravel(), d["wl"].ravel()])).cuda()
+        heads.append(rq.Prerouter(w1l[:F * D].view(F, D), torch.from_numpy(d["b1"]).cuda(),
+                                  torch.from_numpy(d["w2"]).cuda(), torch.from_numpy(d["b2"]).cuda(),
+                                  w1l[F * D:].view(w.E, D)))
     # per layer, two generations of the predicted logits and of the routing taken
     lgs = [[torch.empty((T, w.E), dtype=torch.float32, device="cuda") for _ in range(2)] for _ in range(nl)]
     idxs = [[torch.empty((T, k), dtype=torch.int32, device="cuda") for _ in range(2)] for _ in range(nl)]
@@ -231,6 +237,10 @@ def prerouted_step(w, xs, nl, pools, routers, ws, seed, K, W, path_flag, rq, syn
         out["fused" if fused else "separate_calls"] = {"us_per_layer": round(ms * 1e3 / (K * nl), 3),
                                                        "step_tokens_per_s": round(T / (ms * 1e-3 / K), 1)}
         del graphs
+    # experts the predicted routing touches per layer (the head is random, so it
+    # lacks the workload's popularity and reuse structure)
+    uniq = [len(torch.unique(idxs[l][0])) for l in range(1, nl)]
+    out["unique_experts_per_layer"] = round(float(np.mean(uniq)), 2)
     # head kernels alone, per launch (eager): stage 1 (fc1 + GELU, residual
     # path), stage 2 (fc2); the top-k runs inside the next layer's expert call
     with rq.KernelTimer(rq.MOE_KERNEL_HEAD, 2 * (nl - 1) * 4 + 8) as t:

@@ -43,12 +43,13 @@ __global__ __launch_bounds__(64 * kHeadWaves) void k_head_stage2(
 }
 
 // Stage 1 of a batch from the matrix-core products: the partial planes of
-// W1 x (nsplit1 planes [T][F]) and Wl x (nsplit2 planes [T][E]) are added in
-// plane order, then the k-hot columns and the bias, and fc1's rows take the
-// GELU. One thread per (token, row).
-__global__ __launch_bounds__(256) void k_head_epilogue(const float* __restrict__ raw1, int nsplit1,
-                                                       const float* __restrict__ raw2, int nsplit2, int T, int H,
-                                                       int E, int F, const float* __restrict__ W1,
+// W1 x (nsplit1 planes [T][ld1]) and Wl x (nsplit2 planes [T][ld2], from column
+// off2) are added in plane order, then the k-hot columns and the bias, and
+// fc1's rows take the GELU. One thread per (token, row). When the two matrices
+// were one launch, both point at the same planes of F + E columns.
+__global__ __launch_bounds__(256) void k_head_epilogue(const float* __restrict__ raw1, int nsplit1, int ld1,
+                                                       const float* __restrict__ raw2, int nsplit2, int ld2, int off2,
+                                                       int T, int H, int E, int F, const float* __restrict__ W1,
                                                        const float* __restrict__ b1, const float* __restrict__ Wl,
                                                        const float* __restrict__ b2, const int32_t* __restrict__ cur,
                                                        const int32_t* __restrict__ prev, int k,
@@ -59,8 +60,8 @@ __global__ __launch_bounds__(256) void k_head_epilogue(const float* __restrict__
   if (i >= F + E) return;
   const bool fc1 = i < F;
   const int r = fc1 ? i : i - F;
-  const int R = fc1 ? F : E;
-  const float* raw = fc1 ? raw1 : raw2;
+  const int R = fc1 ? ld1 : ld2;            // row length of the planes
+  const float* raw = fc1 ? raw1 : raw2 + off2;
   const int ns = fc1 ? nsplit1 : nsplit2;
   const int64_t plane = (int64_t)T * R;
   // every load is issued before the first add: the planes, the routed ids,
@@ -104,13 +105,23 @@ hipError_t launch_prerouter(const void* x, int xtype, int T, const HeadDev& hd, 
     const int64_t ldx = (int64_t)H + 2 * E;
     float* raw1 = raw;
     float* raw2 = raw + logits_max_splits(T, F) * (int64_t)T * F;
-    int ns1 = 1, ns2 = 1;
-    e = launch_logits(x, xtype, T, H, hd.w1, F, raw1, &ns1, nullptr, s, ldx);
-    if (e != hipSuccess) return e;
-    e = launch_logits(x, xtype, T, H, hd.wl, E, raw2, &ns2, nullptr, s, ldx);
-    if (e != hipSuccess) return e;
+    int ns1 = 1, ns2 = 1, ld1 = F, ld2 = E, off2 = 0;
+    if (hd.wl == hd.w1 + (int64_t)F * ldx) {
+      // the residual path's rows follow fc1's in memory: one launch over F + E rows
+      e = launch_logits(x, xtype, T, H, hd.w1, F + E, raw1, &ns1, nullptr, s, ldx);
+      if (e != hipSuccess) return e;
+      raw2 = raw1;
+      ns2 = ns1;
+      ld1 = ld2 = F + E;
+      off2 = F;
+    } else {
+      e = launch_logits(x, xtype, T, H, hd.w1, F, raw1, &ns1, nullptr, s, ldx);
+      if (e != hipSuccess) return e;
+      e = launch_logits(x, xtype, T, H, hd.wl, E, raw2, &ns2, nullptr, s, ldx);
+      if (e != hipSuccess) return e;
+    }
     MOE_LAUNCH(MOE_KERNEL_HEAD, k_head_epilogue, dim3((unsigned)(((F + E + 255) / 256) * T)), dim3(256), 0, s, raw1, ns1,
-               raw2, ns2, T,
+               ld1, raw2, ns2, ld2, off2, T,
                H, E, F, hd.w1, hd.b1, hd.wl, hd.b2, cur, prev, k, act, part);
   } else {
     // stage 1 of a few tokens: a = gelu(fc1(f)) for F rows, part = l(f) + b2 for

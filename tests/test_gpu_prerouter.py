@@ -228,3 +228,19 @@ def test_prerouted_layer(T, scheme, xtype, I, F):
     assert rel_norm_err(y_last.cpu().numpy(), yref) <= Y_REL_NORM
     nref = oracle.prerouter(x, head, ridx, prev, k, bf16=bf16)[2]
     assert rel_inf_err(nxt.cpu().numpy(), nref) <= HEAD_LOGIT_TOL
+
+
+@pytest.mark.parametrize("T", [3, 16, 64])
+def test_prerouter_with_contiguous_fc1_and_residual(T):
+    """fc1's and the residual path's rows in one allocation (one matrix-core
+    launch for a batch)."""
+    H, E, F, k = 512, 64, 96, 6
+    say(f"prerouter contiguous weights T={T}")
+    head, x, cur, prev, ref = _case(T, H, E, F, k, synth.F16, seed=60 + T)
+    D = H + 2 * E
+    w1l = torch.from_numpy(np.concatenate([head.w1.ravel(), head.wl.ravel()])).cuda()
+    dh = rq.Prerouter(w1l[:F * D].view(F, D), torch.from_numpy(head.b1).cuda(), torch.from_numpy(head.w2).cuda(),
+                      torch.from_numpy(head.b2).cuda(), w1l[F * D:].view(E, D))
+    out = rq.moe_prerouter_forward(to_dev_x(x, synth.F16), dh, _dev_ids(cur), _dev_ids(prev), k, want_logits=True)
+    torch.cuda.synchronize()
+    _check(out, ref, k)
