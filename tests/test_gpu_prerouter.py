@@ -244,3 +244,32 @@ def test_prerouter_with_contiguous_fc1_and_residual(T):
     out = rq.moe_prerouter_forward(to_dev_x(x, synth.F16), dh, _dev_ids(cur), _dev_ids(prev), k, want_logits=True)
     torch.cuda.synchronize()
     _check(out, ref, k)
+
+
+def test_prerouted_layer_at_the_large_shape():
+    """The fused prerouted layer at H = 4096, E = 512, top-10, I = 1024 (two
+    code blocks per lane, eight logits per lane in the top-k, four hidden chunks
+    per head wave). Only the routed experts hold weights; the rest have NaN
+    scales, so a read of any other expert would show in y."""
+    from tests.gpu_cases import device_pool, oracle_compact, remap
+    w = synth.Workload("prerouted_large", T=1, H=4096, E=512, k=10, I=1024, scheme=synth.INT4, xtype=synth.F16)
+    F = synth.PREROUTER_F
+    say("prerouted layer at H=4096 E=512 k=10 I=1024")
+    head, x, _, prev, _ = _case(1, w.H, w.E, F, w.k, w.xtype, seed=71)
+    g = np.random.default_rng(71)
+    logits = (g.standard_normal((1, w.E)) * 2.0).astype(np.float32)
+    ridx, rgate = oracle.topk_logits(logits, w.k)
+    used = np.unique(ridx)
+    ex = device_pool(w, 71, 0, used)
+    rex, m = oracle_compact(w, 71, 0, used)
+    xd = to_dev_x(x, w.xtype)
+    idx = torch.empty((1, w.k), dtype=torch.int32, device="cuda")
+    nxt = torch.empty((1, w.E), dtype=torch.float32, device="cuda")
+    y = rq.moe_prerouted_layer_forward(xd, torch.from_numpy(logits).cuda(), ex, w.k, _dev_head(head), _dev_ids(prev),
+                                       idx, nxt)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    yref = oracle.gather_forward(x, rex, remap(ridx, m), rgate)
+    assert rel_norm_err(y.cpu().numpy(), yref) <= Y_REL_NORM
+    nref = oracle.prerouter(x, head, ridx, prev, w.k)[2]
+    assert rel_inf_err(nxt.cpu().numpy(), nref) <= HEAD_LOGIT_TOL
