@@ -149,6 +149,28 @@ moe_status moe_layer_forward(const void* x, int32_t xtype, int32_t T, const floa
                              int32_t* topk_idx_out, float* topk_gate_out,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * scratch comes from a static device array of MOE_NOALLOC_SCRATCH_BYTES inside
+ * the library instead of a caller workspace; every GPU the library runs on holds
+ * its own copy until the process ends. The call itself allocates nothing: its
+ * first call on a device, with that device current, looks the array's address
+ * up once (hipGetSymbolAddress).
+ *   Arguments, results and kernels are moe_layer_forward's. `stream` must belong
+ *   to the current device (NULL: its default stream).
+ *   Every call on one GPU shares that GPU's array and it keeps the last call's
+ *   contents; nothing in it needs to start at zero. Calls that overlap on one
+ *   GPU (two streams, two threads) race on it: order them, e.g. on one stream.
+ * Errors: as moe_layer_forward's, and MOE_ERR_WORKSPACE when the sizes need more
+ * than MOE_NOALLOC_SCRATCH_BYTES (moe_workspace_bytes(T, E, H, I, k, scheme)
+ * must not exceed it: any single-token shape, and batches such as T = 64, E =
+ * 512, H = 2048, I = 512, k = 10 fit), MOE_ERR_INVALID_ARG when `stream` is on
+ * another device, MOE_ERR_HIP when the address lookup fails. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+moe_status moe_layer_forward_noalloc(const void* x, int32_t xtype, int32_t T, const float* router_w,
+                                     const moe_experts* ex, int32_t k, uint32_t flags, float* y,
+                                     int32_t* topk_idx_out, float* topk_gate_out, void* stream);
+
 /* The expert layer from given router logits: moe_layer_forward after its gate
  * linear, for logits that come from elsewhere, such as moe_prerouter_forward
  * predicting this layer's routing (prediction as routing: "The Other Half of the

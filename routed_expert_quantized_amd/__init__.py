@@ -27,7 +27,7 @@ MOE_FLAG_RENORM, MOE_FLAG_PATH_GATHER, MOE_FLAG_PATH_GEMM = 1, 2, 4
 
 # Every function the header declares; the library must export all of them.
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_group", "moe_gather_qmm_forward", "moe_layer_forward",
-           "moe_quantize", "moe_timer_start", "moe_timer_read", "moe_stream_read", "moe_miss_replay",
+           "moe_layer_forward_noalloc", "moe_quantize", "moe_timer_start", "moe_timer_read", "moe_stream_read", "moe_miss_replay",
            "moe_stage_experts", "moe_remap_ids", "moe_prerouter_workspace_bytes", "moe_prerouter_forward",
            "moe_experts_from_logits", "moe_prerouted_layer_forward", "moe_qlinear_lora_workspace_bytes",
            "moe_qlinear_lora_forward",
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
             "moe_group": ([P, I32, I32, I32, P, P, P, P, P, P, SZ, P], ctypes.c_int),
             "moe_gather_qmm_forward": ([P, I32, I32, E, I32, P, P, P, U32, P, SZ, P], ctypes.c_int),
             "moe_layer_forward": ([P, I32, I32, P, E, I32, U32, P, P, P, P, SZ, P], ctypes.c_int),
+            "moe_layer_forward_noalloc": ([P, I32, I32, P, E, I32, U32, P, P, P, P], ctypes.c_int),
             "moe_quantize": ([P, I64, I32, I32, P, P, P], ctypes.c_int),
             "moe_timer_start": ([I32, I32], ctypes.c_int),
             "moe_timer_read": ([P, I32, P], ctypes.c_int),
@@ -500,6 +501,29 @@ def moe_layer_forward(x: torch.Tensor, router_w: torch.Tensor, ex: Experts, k: i
            lib().moe_layer_forward(_p(x), _xtype(x), T, _p(router_w), ctypes.byref(c), k, flags, _p(y), _p(idx),
                                    _p(gate), _p(w), w.numel(), _stream(stream)))
     return (y, idx, gate) if return_routing else y
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def moe_layer_forward_noalloc(x: torch.Tensor, router_w: torch.Tensor, ex: Experts, k: int,
+                              flags: int = MOE_FLAG_RENORM, stream=None, out: torch.Tensor | None = None,
+                              routing_out=None):
+    """moe_layer_forward with the library's static device scratch instead of a
+    workspace (for callers that cannot allocate). `out` and `routing_out`
+    ((idx, gate) tensors) let the caller pass every output, so the call itself
+    allocates nothing; without them y (and no routing) is allocated here.
+    Returns y [T][H]."""
+    _device_tensor(x, "x")
+    _device_tensor(router_w, "router_w")
+    T = x.shape[0]
+    y = out if out is not None else torch.empty((T, ex.H), dtype=torch.float32, device=x.device)
+    idx, gate = routing_out if routing_out is not None else (None, None)
+    c = ex.c()
+    _check("moe_layer_forward_noalloc",
+           lib().moe_layer_forward_noalloc(_p(x), _xtype(x), T, _p(router_w), ctypes.byref(c), k, flags, _p(y),
+                                           _p(idx), _p(gate), _stream(stream)))
+    return y
 
 
 class KernelTimer:

@@ -3,13 +3,21 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "kernels.hpp"
 #include "moe.h"
+
+// Scratch of moe_layer_forward_noalloc: a file-scope device array, one copy per
+// GPU. In host code its name stands for the host-side shadow, not a device
+// address, so kernels and copies only ever get the address looked up by
+// scratch_address() below.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -149,6 +157,39 @@ moe_status run_experts(const void* x, int32_t xtype, int32_t T, const moe::Exper
                     "decode (grouped)");
 }
 
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_dev[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch array: hipGetSymbolAddress once per
+// device, with that device current, then the cached pointer.
+moe_status scratch_address(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  if (s) {
+    hipDevice_t sd = -1;
+    e = hipStreamGetDevice(s, &sd);
+    if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+    if (sd != dev) return fail(MOE_ERR_INVALID_ARG, "stream belongs to device %d, the current device is %d", sd, dev);
+  }
+  void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+      if (!p || !aligned(p, 256)) return fail(MOE_ERR_HIP, "scratch address %p is not 256-byte aligned", p);
+      g_scratch_dev[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
 // Benchmark timer state (see moe_timer_start).
 struct KernelTimer {
   int kid = -1;
@@ -188,8 +229,10 @@ moe_status layer_from_logits(const void* x, int32_t xtype, int32_t T, const moe:
   return run_experts(x, xtype, T, d, k, idx, gate, y, flags, ws, L, s);
 }
 
-moe_status check_layer_args(const void* x, int32_t xtype, int32_t T, const moe_experts* ex, int32_t k, uint32_t flags,
-                            const float* y, void* ws, size_t ws_bytes, moe::ExpertsDev* d, Layout* L) {
+// Checks of a layer call other than its workspace; fills the decoded experts
+// and the workspace layout.
+moe_status check_layer_shapes(const void* x, int32_t xtype, int32_t T, const moe_experts* ex, int32_t k,
+                              uint32_t flags, const float* y, moe::ExpertsDev* d, Layout* L) {
   moe_status st;
   if ((st = check_x(x, xtype))) return st;
   if ((st = check_experts(ex, d))) return st;
@@ -201,7 +244,20 @@ moe_status check_layer_args(const void* x, int32_t xtype, int32_t T, const moe_e
   if (flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_PATH_GATHER | MOE_FLAG_PATH_GEMM))
     return fail(MOE_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
   *L = layout(T, d->E, d->H, d->I, k);
+  return MOE_OK;
+}
+
+moe_status check_layer_args(const void* x, int32_t xtype, int32_t T, const moe_experts* ex, int32_t k, uint32_t flags,
+                            const float* y, void* ws, size_t ws_bytes, moe::ExpertsDev* d, Layout* L) {
+  moe_status st;
+  if ((st = check_layer_shapes(x, xtype, T, ex, k, flags, y, d, L))) return st;
   return check_ws(ws, ws_bytes, *L);
+}
+
+moe_status check_router(const float* router_w) {
+  if (!router_w) return fail(MOE_ERR_INVALID_ARG, "router_w is NULL");
+  if (!aligned(router_w, 16)) return fail(MOE_ERR_INVALID_ARG, "router_w is not 16-byte aligned");
+  return MOE_OK;
 }
 }  // namespace
 
@@ -309,8 +365,7 @@ moe_status moe_layer_forward(const void* x, int32_t xtype, int32_t T, const floa
   moe::ExpertsDev d;
   Layout L;
   if ((st = check_layer_args(x, xtype, T, ex, k, flags, y, ws, ws_bytes, &d, &L))) return st;
-  if (!router_w) return fail(MOE_ERR_INVALID_ARG, "router_w is NULL");
-  if (!aligned(router_w, 16)) return fail(MOE_ERR_INVALID_ARG, "router_w is not 16-byte aligned");
+  if ((st = check_router(router_w))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* logits = at<float>(ws, L.logits);
   int nsplit = 1;
@@ -318,6 +373,26 @@ moe_status moe_layer_forward(const void* x, int32_t xtype, int32_t T, const floa
                                     T >= moe::kSplitRouterMinT ? at<uint16_t>(ws, L.r3) : nullptr, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
   return layer_from_logits(x, xtype, T, d, k, flags, logits, nsplit, y, topk_idx_out, topk_gate_out, ws, L, s);
+}
+
+moe_status moe_layer_forward_noalloc(const void* x, int32_t xtype, int32_t T, const float* router_w,
+                                     const moe_experts* ex, int32_t k, uint32_t flags, float* y,
+                                     int32_t* topk_idx_out, float* topk_gate_out, void* stream) {
+  moe_status st;
+  moe::ExpertsDev d;
+  Layout L;
+  // every check of moe_layer_forward, with the scratch size in place of the
+  // workspace's, before anything touches the device
+  if ((st = check_layer_shapes(x, xtype, T, ex, k, flags, y, &d, &L))) return st;
+  if ((st = check_router(router_w))) return st;
+  if (L.total > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE, "these sizes need %zu bytes of scratch; the static scratch holds %zu", L.total,
+                (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if ((st = scratch_address(s, &ws))) return st;
+  return moe_layer_forward(x, xtype, T, router_w, ex, k, flags, y, topk_idx_out, topk_gate_out, ws,
+                           MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 moe_status moe_experts_from_logits(const void* x, int32_t xtype, int32_t T, const float* logits,

@@ -117,6 +117,32 @@ def test_gather_and_layer_validation(L):
     assert layer(flags=0x40) == rq.MOE_ERR_UNSUPPORTED
 
 
+def test_layer_noalloc_validation(L):
+    """The static-scratch entry point checks everything on the host, scratch size
+    included, before it looks anything up on the device."""
+    ex = _experts()
+
+    def layer(x=FAKE, xt=rq.MOE_F16, T=1, R=FAKE, e=ex, k=8, flags=1, y=FAKE):
+        return L.moe_layer_forward_noalloc(x, xt, T, R, ctypes.byref(e) if e is not None else None, k, flags, y,
+                                           None, None, None)
+
+    assert layer(x=None) == rq.MOE_ERR_INVALID_ARG
+    assert layer(R=None) == rq.MOE_ERR_INVALID_ARG
+    assert layer(y=None) == rq.MOE_ERR_INVALID_ARG
+    assert layer(e=None) == rq.MOE_ERR_INVALID_ARG
+    assert layer(k=300) == rq.MOE_ERR_INVALID_ARG
+    assert layer(flags=0x40) == rq.MOE_ERR_UNSUPPORTED
+    assert layer(xt=9) == rq.MOE_ERR_UNSUPPORTED
+    # prefill: 2048 tokens need about 175 MiB of scratch, beyond the static 16 MiB
+    big = _experts(E=256, H=2048, I=512)
+    assert layer(T=2048, e=big, xt=rq.MOE_BF16) == rq.MOE_ERR_WORKSPACE
+    assert b"static scratch" in L.moe_last_error()
+    assert L.moe_workspace_bytes(2048, 256, 2048, 512, 8, 0) > rq.MOE_NOALLOC_SCRATCH_BYTES
+    # the shapes the scratch is sized for
+    for T, E, H, I, k, s in [(1, 1024, 4096, 4096, 16, 0), (64, 512, 2048, 512, 10, 1), (16, 512, 4096, 1024, 10, 1)]:
+        assert 0 < L.moe_workspace_bytes(T, E, H, I, k, s) <= rq.MOE_NOALLOC_SCRATCH_BYTES
+
+
 def test_group_and_quantize_validation(L):
     assert L.moe_group(None, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == rq.MOE_ERR_INVALID_ARG
     assert L.moe_group(FAKE, 4, 9, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == rq.MOE_ERR_INVALID_ARG
