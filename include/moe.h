@@ -69,10 +69,15 @@ enum {
   /* Renormalise the k gates of each token so they sum to one. */
   MOE_FLAG_RENORM = 1u,
   /* Expert-path selection; with neither bit set the library uses the gathered
-   * matvec kernels for T == 1 and the grouped MFMA GEMM for T > 1.
-   * GATHER: gathered matvec kernels (fp32 arithmetic on dequantised codes).
-   * GEMM: grouped fp16 MFMA GEMM, fp32 accumulation (weights rounded once to
-   *       fp16 as code * scale, activations staged as fp16, h stored as fp16). */
+   * matvec kernels for T == 1 and for fp32 activations, and the grouped MFMA
+   * GEMM for T > 1 with fp16 or bf16 activations.
+   * GATHER: gathered matvec kernels (exact code * scale products, fp32 sums).
+   * GEMM: grouped MFMA GEMM on the raw codes, one 32-element block per MFMA
+   *       step, each block's fp32 partial times its scale (weights exact); the
+   *       activations are the other operand as given (fp16 or bf16; fp32 x is
+   *       MOE_ERR_UNSUPPORTED with this bit); h is held in fp16 with a
+   *       power-of-two exponent per tile, so no intermediate overflows; the
+   *       per-slot outputs ahead of the combine are fp32. */
   MOE_FLAG_PATH_GATHER = 2u,
   MOE_FLAG_PATH_GEMM = 4u
 };

@@ -101,11 +101,12 @@ hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsD
 hipError_t launch_combine(int T, int H, int k, const float* gate, const float* ys, const uint16_t* ys16, float* y,
                           hipStream_t s);
 
-// Grouped MFMA GEMM path (after launch_group): gate/up + SwiGLU into fp16 h,
-// down into ys (or y itself in per-slot mode), then the combine.
-// x16: [T][H] fp16 scratch for the activations when x is not fp16 already.
+// Grouped MFMA GEMM path (after launch_group), for fp16 or bf16 activations:
+// gate/up + SwiGLU into fp16 h [T*k][I] with one power-of-two exponent per tile
+// in sig [T*k][ceil(I/64)], down into fp32 ys [T*k][H] (or y itself in
+// per-slot mode), then the combine.
 hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev& ex, int k, const GroupBufs& g,
-                               const float* gate, uint16_t* h16, uint16_t* x16, float* ys, float* y, hipStream_t s);
+                               const float* gate, uint16_t* h16, int32_t* sig, float* ys, float* y, hipStream_t s);
 
 // Prerouter head weights as the kernels see them (fp32, the page's layout:
 // w1 [F][H+2E], b1 [F] or null, w2 [E][F], b2 [E] or null, wl [E][H+2E]).

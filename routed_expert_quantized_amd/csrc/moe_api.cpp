@@ -47,7 +47,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 // Scratch regions inside the caller's workspace, each 256-byte aligned.
 struct Layout {
-  size_t logits, idx, gate, mask, base, counts, offsets, perm, uniq, n_uniq, h, ys, x16, r3, total;
+  size_t logits, idx, gate, mask, base, counts, offsets, perm, uniq, n_uniq, h, hsig, ys, r3, total;
 };
 
 Layout layout(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
@@ -70,8 +70,8 @@ Layout layout(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
   L.uniq = take(E * 4);
   L.n_uniq = take(4);
   L.h = take(T * k * I * 4);
+  L.hsig = take(T * k * ((I + 63) / 64) * 4);  // the grouped GEMM's tile exponents of h
   L.ys = take(T * k * H * 4);
-  L.x16 = take(T * H * 2);
   L.r3 = take(T >= moe::kSplitRouterMinT ? 3 * E * H * 2 : 0);  // router split into bf16 planes
   L.total = off;
   return L;
@@ -102,6 +102,18 @@ moe_status check_shape(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
     return fail(MOE_ERR_INVALID_ARG, "I=%lld must be a multiple of 32 in [32, 4096]", (long long)I);
   if (k < 1 || k > std::min<int64_t>(E, moe::kMaxK))
     return fail(MOE_ERR_INVALID_ARG, "k=%lld outside [1, min(E, %d)]", (long long)k, moe::kMaxK);
+  return MOE_OK;
+}
+
+// The expert-path flags: at most one path, and the grouped GEMM only for
+// 16-bit activations (its MFMA operands are the activations as given).
+moe_status check_path_flags(uint32_t flags, int32_t xtype) {
+  if ((flags & MOE_FLAG_PATH_GATHER) && (flags & MOE_FLAG_PATH_GEMM))
+    return fail(MOE_ERR_INVALID_ARG, "both path flags are set");
+  if (flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_PATH_GATHER | MOE_FLAG_PATH_GEMM))
+    return fail(MOE_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  if ((flags & MOE_FLAG_PATH_GEMM) && xtype == MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "the grouped GEMM path takes fp16 or bf16 activations, not fp32");
   return MOE_OK;
 }
 
@@ -139,9 +151,10 @@ moe_status run_experts(const void* x, int32_t xtype, int32_t T, const moe::Exper
                        const int32_t* idx, const float* gate, float* y, uint32_t flags, void* ws,
                        const Layout& L, hipStream_t s) {
   float* h = at<float>(ws, L.h);
-  // Path choice: the grouped MFMA GEMM when asked, and by default for T > 1;
-  // the gathered matvec for a single token or when asked.
-  const bool gemm = (flags & MOE_FLAG_PATH_GEMM) || (!(flags & MOE_FLAG_PATH_GATHER) && T > 1);
+  // Path choice: the grouped MFMA GEMM when asked, and by default for T > 1
+  // with 16-bit activations; the gathered matvec for a single token, for fp32
+  // activations or when asked (validation has rejected the GEMM with fp32).
+  const bool gemm = (flags & MOE_FLAG_PATH_GEMM) || (!(flags & MOE_FLAG_PATH_GATHER) && T > 1 && xtype != MOE_F32);
   if (T == 1 && !gemm)
     return hip_status(moe::launch_decode_t1(x, xtype, d, k, 0, nullptr, idx, gate, nullptr, nullptr, nullptr,
                                             nullptr, h, y, s),
@@ -151,7 +164,7 @@ moe_status run_experts(const void* x, int32_t xtype, int32_t T, const moe::Exper
   if (e != hipSuccess) return hip_status(e, "grouping");
   if (gemm)
     return hip_status(moe::launch_gemm_grouped(x, xtype, T, d, k, g, gate, reinterpret_cast<uint16_t*>(h),
-                                               at<uint16_t>(ws, L.x16), at<float>(ws, L.ys), y, s),
+                                               at<int32_t>(ws, L.hsig), at<float>(ws, L.ys), y, s),
                       "grouped GEMM");
   return hip_status(moe::launch_decode_grouped(x, xtype, T, d, k, g, gate, h, at<float>(ws, L.ys), y, s),
                     "decode (grouped)");
@@ -239,10 +252,7 @@ moe_status check_layer_shapes(const void* x, int32_t xtype, int32_t T, const moe
   if ((st = check_shape(T, d->E, d->H, d->I, k))) return st;
   if (!y) return fail(MOE_ERR_INVALID_ARG, "y is NULL");
   if (!aligned(y, 16)) return fail(MOE_ERR_INVALID_ARG, "y is not 16-byte aligned");
-  if ((flags & MOE_FLAG_PATH_GATHER) && (flags & MOE_FLAG_PATH_GEMM))
-    return fail(MOE_ERR_INVALID_ARG, "both path flags are set");
-  if (flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_PATH_GATHER | MOE_FLAG_PATH_GEMM))
-    return fail(MOE_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  if ((st = check_path_flags(flags, xtype))) return st;
   *L = layout(T, d->E, d->H, d->I, k);
   return MOE_OK;
 }
@@ -349,10 +359,7 @@ moe_status moe_gather_qmm_forward(const void* x, int32_t xtype, int32_t T, const
   if ((st = check_shape(T, d.E, d.H, d.I, k))) return st;
   if (!topk_idx || !y) return fail(MOE_ERR_INVALID_ARG, "topk_idx or y is NULL");
   if (!aligned(y, 16)) return fail(MOE_ERR_INVALID_ARG, "y is not 16-byte aligned");
-  if ((flags & MOE_FLAG_PATH_GATHER) && (flags & MOE_FLAG_PATH_GEMM))
-    return fail(MOE_ERR_INVALID_ARG, "both path flags are set");
-  if (flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_PATH_GATHER | MOE_FLAG_PATH_GEMM))
-    return fail(MOE_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  if ((st = check_path_flags(flags, xtype))) return st;
   const Layout L = layout(T, d.E, d.H, d.I, k);
   if ((st = check_ws(ws, ws_bytes, L))) return st;
   return run_experts(x, xtype, T, d, k, topk_idx, topk_gate, y, flags, ws, L, static_cast<hipStream_t>(stream));

@@ -103,6 +103,9 @@ def test_gather_and_layer_validation(L):
     assert gather(y=None) == rq.MOE_ERR_INVALID_ARG
     assert gather(flags=rq.MOE_FLAG_PATH_GATHER | rq.MOE_FLAG_PATH_GEMM) == rq.MOE_ERR_INVALID_ARG
     assert gather(flags=0x100) == rq.MOE_ERR_UNSUPPORTED
+    # the grouped GEMM takes 16-bit activations only; fp32 goes to the gathered path
+    assert gather(flags=rq.MOE_FLAG_PATH_GEMM, xt=rq.MOE_F32, T=4) == rq.MOE_ERR_UNSUPPORTED
+    assert b"fp16 or bf16" in L.moe_last_error()
     assert gather(nws=4096) == rq.MOE_ERR_WORKSPACE
     need = L.moe_workspace_bytes(64, 256, 2048, 512, 8, 0)
     assert gather(T=64, nws=need - 1) == rq.MOE_ERR_WORKSPACE

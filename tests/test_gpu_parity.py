@@ -145,6 +145,12 @@ def test_gather_parity_small(T, E, H, I, k, scheme, xtype, path):
     xd = to_dev_x(x, xtype)
     bf16 = xtype == synth.BF16
     fl = PATHS[path]
+    if path == "gemm" and xtype == synth.F32:
+        # the grouped GEMM's operands are the activations as given: 16-bit only
+        with pytest.raises(rq.MoeError) as err:
+            rq.moe_gather_qmm_forward(xd, ex, torch.from_numpy(idx).cuda(), torch.from_numpy(gate).cuda(), flags=fl)
+        assert err.value.status == rq.MOE_ERR_UNSUPPORTED
+        return
     y = rq.moe_gather_qmm_forward(xd, ex, torch.from_numpy(idx).cuda(), torch.from_numpy(gate).cuda(), flags=fl)
     ref = oracle.gather_forward(x, rex, idx, gate, bf16=bf16)
     assert rel_norm_err(y.cpu().numpy(), ref) <= Y_REL_NORM
@@ -154,15 +160,36 @@ def test_gather_parity_small(T, E, H, I, k, scheme, xtype, path):
 
 
 # ---------------------------------------------------------------- whole layer at the workloads' sizes
-LAYER_CASES = [("tiny", None, None, "auto"), ("decode40", None, None, "auto"), ("batched_int4", None, 16, "auto"),
-               ("large_int4", None, 6, "auto"), ("prefill", None, 12, "auto"), ("batched_int4", 7, None, "auto"),
-               ("batched_int4", None, 16, "gemm"), ("large_int4", None, 6, "gemm"), ("prefill", None, 12, "gather"),
-               ("decode40", None, None, "gemm"), ("prefill", 300, 8, "gemm"),
+# Every token is compared with the oracle, except at prefill8k (8192 tokens),
+# where the tokens are a stratified sample ("passes"): for every routed expert,
+# the assignments at the first and last row of each 96-row pass of its grouped
+# list (the six-tile passes the GEMM takes at this load) and its last
+# assignment, plus a random spread.
+LAYER_CASES = [("tiny", None, "all", "auto"), ("decode40", None, "all", "auto"), ("batched_int4", None, "all", "auto"),
+               ("large_int4", None, "all", "auto"), ("prefill", None, "all", "auto"), ("batched_int4", 7, "all", "auto"),
+               ("batched_int4", None, "all", "gemm"), ("large_int4", None, "all", "gemm"),
+               ("prefill", None, "all", "gather"), ("decode40", None, "all", "gemm"), ("prefill", 300, "all", "gemm"),
                # one token at the E=512, top-10 shapes: scan top-k, two blocks per lane (H=4096),
                # the general down kernel (k*I > 4096)
-               ("large_int4", 1, None, "auto"), ("batched_int4", 1, None, "auto"),
-               # ~256 assignments per expert: 18-tile GEMM passes
-               ("prefill8k", None, 8, "auto")]
+               ("large_int4", 1, "all", "auto"), ("batched_int4", 1, "all", "auto"),
+               # ~256 assignments per expert: six-tile GEMM passes
+               ("prefill8k", None, "passes", "auto")]
+
+
+def pass_boundary_tokens(ridx: np.ndarray, E: int, rows: int, extra: int, seed: int) -> np.ndarray:
+    """Tokens of every expert's first and last assignment in each `rows`-row pass
+    of its grouped list (stable by flat id), its last assignment, and `extra`
+    random tokens."""
+    k = ridx.shape[1]
+    counts, offsets, perm = oracle.group(ridx, E)[:3]
+    pos = []
+    for e in np.nonzero(counts)[0]:
+        n, o = int(counts[e]), int(offsets[e])
+        for p0 in range(0, n, rows):
+            pos += [o + p0, o + min(p0 + rows, n) - 1]
+    toks = set(int(perm[p]) // k for p in pos)
+    toks |= set(np.random.default_rng(seed).choice(ridx.shape[0], extra, replace=False).tolist())
+    return np.array(sorted(toks))
 
 
 @pytest.mark.parametrize("name,T,sample,path", LAYER_CASES)
@@ -182,7 +209,8 @@ def test_layer_parity(name, T, sample, path):
     yn = y.cpu().numpy()
     assert np.isfinite(yn).all()   # unrouted experts carry NaN scales
     Tn = li.x.shape[0]
-    toks = np.arange(Tn) if sample is None or sample >= Tn else np.random.default_rng(1).choice(Tn, sample, replace=False)
+    toks = np.arange(Tn) if sample == "all" else pass_boundary_tokens(ridx, w.E, 96, 64, seed=1)
+    say(f"  comparing {len(toks)} of {Tn} tokens")
     rex, m = oracle_compact(w, 0, 0, np.unique(ridx[toks]))
     ref = oracle.gather_forward(np.ascontiguousarray(li.x[toks]), rex, remap(ridx[toks], m), rgate[toks], bf16=bf16)
     err, inf = rel_norm_err(yn[toks], ref), rel_inf_err(yn[toks], ref)
@@ -199,6 +227,38 @@ def test_layer_is_deterministic():
     a = rq.moe_layer_forward(xd, Rd, ex, w.k)[0].clone()
     b = rq.moe_layer_forward(xd, Rd, ex, w.k)[0]
     assert torch.equal(a, b)
+
+
+# The grouped GEMM multiplies raw codes and applies each block's scale to the
+# fp32 partial, and takes bf16 activations as they are: activations beyond the
+# fp16 range, scales beyond 65504 / 127 and weights in the fp16 subnormal range
+# stay exact. (xtype, activation scale, weight std) per case.
+GEMM_RANGE = [(synth.BF16, 1e5, 0.02),      # activations above 65504
+              (synth.BF16, 1e-3, 600.0),    # block scales above 516 (code * scale above 65504)
+              (synth.F16, 1.0, 1e-5),       # weights below the fp16 normal range
+              (synth.BF16, 1.0, 1e-5),
+              (synth.F16, 8.0, 40.0)]       # large weights with h and outputs inside the fp16 range
+
+
+@pytest.mark.parametrize("xtype,xs,wstd", GEMM_RANGE)
+@pytest.mark.parametrize("scheme", [rq.MOE_Q_SYM8, rq.MOE_Q_INT4])
+def test_gemm_path_range(xtype, xs, wstd, scheme):
+    T, E, H, I, k = 48, 8, 256, 128, 3
+    say(f"gemm range xtype={xtype} x*{xs} wstd={wstd} scheme={scheme}")
+    g = np.random.default_rng(int(xs * 7 + wstd * 11) + scheme + 5 * xtype)
+    wgu = (g.standard_normal((E, 2 * I, H)) * wstd).astype(np.float32)
+    wd = (g.standard_normal((E, H, I)) * wstd).astype(np.float32)
+    x = synth.encode_x((g.standard_normal((T, H)) * xs).astype(np.float32), xtype)
+    idx = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    gate = g.random((T, k)).astype(np.float32)
+    ex = rq.quantize_experts(torch.from_numpy(wgu).cuda(), torch.from_numpy(wd).cuda(), scheme)
+    rex = oracle.quantize_experts(wgu, wd, scheme)
+    y = rq.moe_gather_qmm_forward(to_dev_x(x, xtype), ex, torch.from_numpy(idx).cuda(), torch.from_numpy(gate).cuda(),
+                                  flags=rq.MOE_FLAG_PATH_GEMM)
+    ref = oracle.gather_forward(x, rex, idx, gate, bf16=xtype == synth.BF16)
+    yn = y.cpu().numpy()
+    assert np.isfinite(yn).all()
+    assert rel_norm_err(yn, ref) <= Y_REL_NORM
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode40"])
