@@ -270,16 +270,31 @@ moe_status moe_miss_replay(const int32_t* topk_idx, const float* topk_gate, int3
  * and [0, stack->E), with distinct slots. All eight weight and scale pointers must
  * be 16-byte aligned. Asynchronous on `stream`.
  *
- * moe_remap_ids writes out[i] = slot_of[idx[i]] for i < n (DEVICE arrays; idx
- * trusted to lie in [0, E), slot_of [E] holding each resident expert's slot), so a
- * routing can be run on the stack with moe_gather_qmm_forward.
+ * moe_remap_ids writes out[i] = slot_of[idx[i]] for i < n, and -1 for an id
+ * outside [0, E) (DEVICE arrays; slot_of [E] holding each resident expert's slot),
+ * so a routing can be run on the stack with moe_gather_qmm_forward.
+ *
+ * moe_layer_forward_staged is moe_layer_forward with the slot table in the
+ * kernels' weight addressing: the router ranges over E experts (router_w [E][H]),
+ * and the weights of routed expert e are read from slot slot_of[e] of `stack`
+ * (DEVICE int32 [E], 4-byte aligned; stack->E is the slot count). Routing
+ * outputs are expert ids. A routed expert whose entry lies outside [0, stack->E)
+ * is not resident: it contributes nothing (its gate stays as routed; the pages
+ * leave the substitute of a missed expert open). For one token the entries are
+ * read beside the logits in the gate/up kernel, so the lookup adds no dependent
+ * memory read. `ws` holds moe_workspace_bytes(T, E, H, I, k, scheme) bytes.
  *
  * Errors: MOE_ERR_INVALID_ARG for null or misaligned pointers, n < 0, stacks whose
- * H, I or codec differ from the pool's; MOE_ERR_HIP for a failed launch. */
+ * H, I or codec differ from the pool's; the layer's errors for the staged layer;
+ * MOE_ERR_HIP for a failed launch. */
 moe_status moe_stage_experts(const moe_experts* pool, const moe_experts* stack, const int32_t* experts,
                              const int32_t* slots, int32_t n, void* stream);
 moe_status moe_remap_ids(const int32_t* idx, int64_t n, const int32_t* slot_of, int32_t E, int32_t* out,
                          void* stream);
+moe_status moe_layer_forward_staged(const void* x, int32_t xtype, int32_t T, const float* router_w, int32_t E,
+                                    const moe_experts* stack, const int32_t* slot_of, int32_t k, uint32_t flags,
+                                    float* y, int32_t* topk_idx_out, float* topk_gate_out, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /* Prerouter head, run at one layer to give the next layer's routing for the
  * next token. "The Other Half of the Memory Wall: Serving 35B MoEs from SSD with

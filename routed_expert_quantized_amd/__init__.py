@@ -27,7 +27,7 @@ MOE_FLAG_RENORM, MOE_FLAG_PATH_GATHER, MOE_FLAG_PATH_GEMM = 1, 2, 4
 
 # Every function the header declares; the library must export all of them.
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_group", "moe_gather_qmm_forward", "moe_layer_forward",
-           "moe_layer_forward_noalloc", "moe_quantize", "moe_timer_start", "moe_timer_read", "moe_stream_read", "moe_miss_replay",
+           "moe_layer_forward_noalloc", "moe_layer_forward_staged", "moe_quantize", "moe_timer_start", "moe_timer_read", "moe_stream_read", "moe_miss_replay",
            "moe_stage_experts", "moe_remap_ids", "moe_prerouter_workspace_bytes", "moe_prerouter_forward",
            "moe_experts_from_logits", "moe_prerouted_layer_forward", "moe_qlinear_lora_workspace_bytes",
            "moe_qlinear_lora_forward",
@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "moe_gather_qmm_forward": ([P, I32, I32, E, I32, P, P, P, U32, P, SZ, P], ctypes.c_int),
             "moe_layer_forward": ([P, I32, I32, P, E, I32, U32, P, P, P, P, SZ, P], ctypes.c_int),
             "moe_layer_forward_noalloc": ([P, I32, I32, P, E, I32, U32, P, P, P, P], ctypes.c_int),
+            "moe_layer_forward_staged": ([P, I32, I32, P, I32, E, P, I32, U32, P, P, P, P, SZ, P], ctypes.c_int),
             "moe_quantize": ([P, I64, I32, I32, P, P, P], ctypes.c_int),
             "moe_timer_start": ([I32, I32], ctypes.c_int),
             "moe_timer_read": ([P, I32, P], ctypes.c_int),
@@ -230,6 +231,35 @@ def moe_remap_ids(idx: torch.Tensor, slot_of: torch.Tensor, stream=None) -> torc
     _check("moe_remap_ids", lib().moe_remap_ids(_p(idx), idx.numel(), _p(slot_of), slot_of.numel(), _p(out),
                                                 _stream(stream)))
     return out
+
+
+def moe_layer_forward_staged(x: torch.Tensor, router_w: torch.Tensor, stack: "Experts", slot_of: torch.Tensor, k: int,
+                             flags: int = MOE_FLAG_RENORM, ws: "Workspace | None" = None, stream=None,
+                             out: torch.Tensor | None = None, return_routing: bool = True, routing_out=None):
+    """Router over E = router_w.shape[0] experts, then the routed experts read from
+    their slots slot_of[e] (device int32 [E]) of the resident stack. Returns y
+    [T][H] (and topk_idx, topk_gate: expert ids, with return_routing)."""
+    _device_tensor(x, "x")
+    _device_tensor(router_w, "router_w")
+    _device_tensor(slot_of, "slot_of")
+    if slot_of.dtype != torch.int32:
+        raise ValueError("slot_of must be int32")
+    T = x.shape[0]
+    E = router_w.shape[0]
+    y = out if out is not None else torch.empty((T, stack.H), dtype=torch.float32, device=x.device)
+    idx = gate = None
+    if routing_out is not None:
+        idx, gate = routing_out
+    elif return_routing:
+        idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        gate = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    nb = moe_workspace_bytes(T, E, stack.H, stack.I, k, stack.scheme)
+    w = _ws(ws, nb, x.device)
+    c = stack.c()
+    _check("moe_layer_forward_staged",
+           lib().moe_layer_forward_staged(_p(x), _xtype(x), T, _p(router_w), E, ctypes.byref(c), _p(slot_of), k,
+                                          flags, _p(y), _p(idx), _p(gate), _p(w), w.numel(), _stream(stream)))
+    return (y, idx, gate) if return_routing else y
 
 
 MOE_MISS_FETCH_ALL, MOE_MISS_RULE, MOE_MISS_FIRST_CHOICE = 0, 1, 2

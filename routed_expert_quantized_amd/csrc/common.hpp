@@ -109,6 +109,17 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
 }
 
+// fp16 scale at p, or +0 where keep is false (whatever p holds, NaN included).
+// The load is issued whatever keep says and the bits are masked: a select
+// between the loaded value and 0 is compiled into a branch around the load,
+// with a wait for it inside, which serialises a kernel's loads; the empty asm
+// hides from the optimiser that the mask is one of two constants.
+__device__ __forceinline__ float scale_or_zero(const uint16_t* p, bool keep) {
+  uint32_t m = keep ? 0xFFFFu : 0u;
+  asm("" : "+v"(m));
+  return f16_bits_to_f32((uint16_t)(*p & m));
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
@@ -363,17 +374,29 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
 // Same contract as wave_topk_scan.
 // Only the first `rounds` slots are produced (lanes s < rounds); gates are
 // computed when with_gates is set, and need rounds == k.
-template <int VPL>
+// With ROWS, a slot table slot_of [E] comes along: each lane loads its
+// experts' entries beside their logits and carries them through the sort, so
+// lane s also gets the entry of the expert of rank s in my_row (-1 when it is
+// outside [0, nslots)) without a dependent load after the selection.
+template <int VPL, bool ROWS = false>
 __device__ __forceinline__ void wave_topk_sorted(const float* logits, int E, int k, bool renorm,
-                                                 int& my_idx, float& my_gate, int rounds, bool with_gates) {
+                                                 int& my_idx, float& my_gate, int rounds, bool with_gates,
+                                                 const int32_t* slot_of = nullptr, int nslots = 0,
+                                                 int* my_row = nullptr) {
   const int lane = threadIdx.x & (kWave - 1);
   float v[VPL];
   uint32_t key[VPL];
-  int id[VPL];
+  int id[VPL], sl[VPL];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int e = lane + kWave * j;
-    v[j] = e < E ? logits[e] : 0.0f;
+    // read in bounds whatever e is (a load under a condition becomes a branch)
+    v[j] = logits[min(e, E - 1)];
+    if constexpr (ROWS) sl[j] = slot_of[min(e, E - 1)];
+  }
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int e = lane + kWave * j;
     key[j] = e < E ? logit_key(v[j]) : 0u;
     id[j] = e;
   }
@@ -389,6 +412,10 @@ __device__ __forceinline__ void wave_topk_sorted(const float* logits, int E, int
       const int i0 = id[b - 1], i1 = id[b];
       key[b - 1] = sw ? k1 : k0; key[b] = sw ? k0 : k1;
       id[b - 1] = sw ? i1 : i0; id[b] = sw ? i0 : i1;
+      if constexpr (ROWS) {
+        const int r0 = sl[b - 1], r1 = sl[b];
+        sl[b - 1] = sw ? r1 : r0; sl[b] = sw ? r0 : r1;
+      }
     }
   my_idx = -1;
   my_gate = 0.0f;
@@ -400,13 +427,26 @@ __device__ __forceinline__ void wave_topk_sorted(const float* logits, int E, int
   // offers key 0, below every logit.
   int head = 0;
   uint32_t hk = key[0];
-  int hid = id[0];
+  int hid = id[0], hsl = ROWS ? sl[0] : 0, row = -1;
   for (int s = 0; s < rounds; ++s) {
     const uint32_t m = wave_max_u32(hk);
     const uint64_t tie = __ballot(hk == m);
     int win;
-    if (__popcll(tie) == 1) win = __builtin_amdgcn_readlane(hid, (int)__builtin_ctzll(tie));
-    else win = wave_min_i(hk == m ? hid : 0x7FFFFFFF);
+    if constexpr (ROWS) {
+      // the winning lane: the only one holding the maximum, else the one
+      // among them with the lowest id
+      int wl = (int)__builtin_ctzll(tie);
+      if (__popcll(tie) != 1) {
+        const int lo = wave_min_i(hk == m ? hid : 0x7FFFFFFF);
+        wl = (int)__builtin_ctzll(__ballot(hk == m && hid == lo));
+      }
+      win = __builtin_amdgcn_readlane(hid, wl);
+      const int r = __builtin_amdgcn_readlane(hsl, wl);
+      if (lane == s) row = r;
+    } else {
+      if (__popcll(tie) == 1) win = __builtin_amdgcn_readlane(hid, (int)__builtin_ctzll(tie));
+      else win = wave_min_i(hk == m ? hid : 0x7FFFFFFF);
+    }
     if (s == 0) kmax = m;
     if (lane == s) { my_idx = win; my_key = m; }
     head += hid == win ? 1 : 0;
@@ -416,8 +456,10 @@ __device__ __forceinline__ void wave_topk_sorted(const float* logits, int E, int
     for (int j = 0; j < VPL; ++j) {
       hk = head == j ? key[j] : hk;
       hid = head == j ? id[j] : hid;
+      if constexpr (ROWS) hsl = head == j ? sl[j] : hsl;
     }
   }
+  if constexpr (ROWS) *my_row = row >= 0 && row < nslots ? row : -1;
   if (!with_gates) return;
   const float lmax = key_logit(kmax);
   const float my_logit = key_logit(my_key);
@@ -436,12 +478,24 @@ __device__ __forceinline__ void wave_topk_sorted(const float* logits, int E, int
 
 // Top k with gates (lanes s < k hold slot s). With rounds < k only the first
 // `rounds` slots are produced and no gates (the scan form produces all k).
-template <int VPL>
+// With ROWS, lane s also gets the slot-table entry of its expert (as in
+// wave_topk_sorted; the scan form looks it up after the selection).
+template <int VPL, bool ROWS = false>
 __device__ __forceinline__ void wave_topk(const float* logits, int E, int k, bool renorm, int& my_idx,
-                                          float& my_gate, int rounds = -1) {
+                                          float& my_gate, int rounds = -1, const int32_t* slot_of = nullptr,
+                                          int nslots = 0, int* my_row = nullptr) {
   if (rounds < 0) rounds = k;
-  if constexpr (VPL <= 8) wave_topk_sorted<VPL>(logits, E, k, renorm, my_idx, my_gate, rounds, rounds == k);
-  else wave_topk_scan<VPL>(logits, E, k, renorm, my_idx, my_gate);
+  if constexpr (VPL <= 8) {
+    wave_topk_sorted<VPL, ROWS>(logits, E, k, renorm, my_idx, my_gate, rounds, rounds == k, slot_of, nslots,
+                                my_row);
+  } else {
+    wave_topk_scan<VPL>(logits, E, k, renorm, my_idx, my_gate);
+    if constexpr (ROWS) {
+      const int lane = threadIdx.x & (kWave - 1);
+      const int r = lane < k ? slot_of[my_idx] : -1;
+      *my_row = r >= 0 && r < nslots ? r : -1;
+    }
+  }
 }
 
 template <int SCHEME>

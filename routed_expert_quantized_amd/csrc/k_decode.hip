@@ -44,13 +44,15 @@ constexpr int kGateUpWaves = 4;
 
 // Grid: k slots x blocks_per_slot. A wave computes RP (gate row n, up row I+n)
 // pairs of its slot's expert and writes h[slot][n] = silu(gate) * up.
-// With FROM_LOGITS wave 0 of each workgroup first picks the top k from the
-// router logits (every workgroup redoes this small step, so no cross-workgroup
-// sync is needed); one workgroup publishes the routing for the down kernel and
-// the caller.
+// ROUTE 0: the routing is given (idx_in, expert ids, mapped through the slot
+// table when there is one). ROUTE 1: wave 0 of each workgroup first picks the
+// top k from the router logits (every workgroup redoes this small step, so no
+// cross-workgroup sync is needed); one workgroup publishes the routing for the
+// down kernel and the caller. ROUTE 2: as 1, with each pick's slot-table entry
+// (the expert's slot in a resident stack) as the weights' index.
 // With H16 the activation is stored as fp16 (round to nearest even) for the
 // slot-parallel down kernel, else as fp32.
-template <int SCHEME, int XT, int NBJ, int RP, bool FROM_LOGITS, int VPL, bool H16>
+template <int SCHEME, int XT, int NBJ, int RP, int ROUTE, int VPL, bool H16>
 __device__ __forceinline__ void gate_up_t1_body(const void* __restrict__ x, const ExpertsDev& ex, int k, int renorm,
                                                 const float* __restrict__ logits,
                                                 const int32_t* __restrict__ idx_in,
@@ -63,49 +65,83 @@ __device__ __forceinline__ void gate_up_t1_body(const void* __restrict__ x, cons
   // Every load below is unconditional (block and row indices are clamped in
   // bounds, surplus lanes get a zero scale) so the scheduler can issue them all
   // before the arithmetic.
-  // Activations do not depend on the routing: they are requested first. fp16
-  // activations with the routing step come through LDS, one 16-byte piece per
-  // thread, behind the barrier that shares the routing (one read of x per
+  // Activations do not depend on the routing: they are requested first, into
+  // registers, and stay in flight while the routing's logits are read. fp16
+  // activations with the routing step then go through LDS, one 16-byte piece
+  // per thread, behind the barriers that share the routing (one read of x per
   // workgroup instead of one per wave); otherwise each wave loads its blocks.
+  constexpr bool FROM_LOGITS = ROUTE != 0;
   constexpr bool kStageX = XT == MOE_F16 && FROM_LOGITS;
   constexpr int kThreads = 64 * kGateUpWaves;
+  constexpr int kXPieces = kStageX ? (NBJ * 256 + kThreads - 1) / kThreads : 1;
   __shared__ uint4 xs[kStageX ? NBJ * 256 : 1];
   XReg<SCHEME, XT> xr[NBJ];
+  uint4 xv[kXPieces];
   if constexpr (kStageX) {
 #pragma unroll
-    for (int j = 0; j < (NBJ * 256 + kThreads - 1) / kThreads; ++j) {
-      const int i = (int)threadIdx.x + kThreads * j;
-      if (i < H / 8) xs[i] = reinterpret_cast<const uint4*>(x)[i];
-    }
+    for (int j = 0; j < kXPieces; ++j)
+      xv[j] = reinterpret_cast<const uint4*>(x)[min((int)threadIdx.x + kThreads * j, H / 8 - 1)];
   } else {
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) load_xreg<SCHEME, XT>(xr[j], x, 0, min(lane + 64 * j, NB - 1));
   }
-  __builtin_amdgcn_sched_barrier(0);
   int e;
+  // The first workgroup of the last slot publishes the routing for the down
+  // kernel and the caller (lane s < k of its wave 0 holds rank s), after its
+  // weight loads are issued (stores count in the same counter as loads, and a
+  // wait for them would hold the loads back).
+  bool publisher = false;
+  int pub_idx = 0, pub_row = 0;
+  float pub_gate = 0.0f;
   if constexpr (FROM_LOGITS) {
-    // A workgroup of slot s needs only the first s+1 rounds; the first
-    // workgroup of the last slot runs all k, computes the gates and publishes
-    // the routing for the down kernel and the caller.
-    int my_idx;
-    float my_gate;
-    const bool publisher = bid == (k - 1) * blocks_per_slot;
-    // wave 0 picks the routing; the other waves wait for it at the barrier
+    // A workgroup of slot s needs only the first s+1 rounds; the publisher
+    // runs all k and computes the gates. Wave 0 picks the routing (with a slot
+    // table, each rank's entry comes along); the other waves store the
+    // activations and wait for it at the barrier.
+    publisher = bid == (k - 1) * blocks_per_slot;
+    const int rounds = publisher ? k : slot + 1;
     __shared__ int e_sh;
     if (wave == 0) {
-      wave_topk<VPL>(logits, ex.E, k, renorm != 0, my_idx, my_gate, publisher ? k : slot + 1);
-      if (publisher && lane < k) {
-        idx_ws[lane] = my_idx;
-        gate_ws[lane] = my_gate;
-        if (idx_user) idx_user[lane] = my_idx;
-        if (gate_user) gate_user[lane] = my_gate;
+      int my_idx, my_row;
+      float my_gate;
+      if constexpr (ROUTE == 2) {
+        wave_topk<VPL, true>(logits, ex.E, k, renorm != 0, my_idx, my_gate, rounds, ex.slot_of, ex.slots, &my_row);
+      } else {
+        wave_topk<VPL>(logits, ex.E, k, renorm != 0, my_idx, my_gate, rounds);
+        my_row = my_idx;
       }
-      if (lane == slot) e_sh = my_idx;
+      pub_idx = my_idx;
+      pub_row = my_row;
+      pub_gate = my_gate;
+      if (lane == slot) e_sh = my_row;
+    }
+    if constexpr (kStageX) {
+#pragma unroll
+      for (int j = 0; j < kXPieces; ++j) {
+        const int i = (int)threadIdx.x + kThreads * j;
+        if (i < H / 8) xs[i] = xv[j];
+      }
     }
     __syncthreads();
     e = e_sh;
   } else {
-    e = idx_in[slot];
+    e = expert_index(ex, idx_in[slot]);
+  }
+  // an expert without a slot contributes nothing: index 0 is read with zero scales
+  const bool resident = e >= 0;  // a slot-less expert: zero scales, whatever slot 0 holds
+  e = max(e, 0);
+  if constexpr (kStageX) {
+#pragma unroll
+    for (int j = 0; j < NBJ; ++j) {
+      const int b = min(lane + 64 * j, NB - 1);
+      uint32_t nat[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = xs[4 * b + i];
+        nat[4 * i] = v.x; nat[4 * i + 1] = v.y; nat[4 * i + 2] = v.z; nat[4 * i + 3] = v.w;
+      }
+      xr[j].h = xblock_from_pairs<SCHEME>(nat);
+    }
   }
   const int n0 = (blk * kGateUpWaves + wave) * RP;
   const int64_t rb = row_bytes<SCHEME>(H);
@@ -120,22 +156,16 @@ __device__ __forceinline__ void gate_up_t1_body(const void* __restrict__ x, cons
       const int b = min(lane + 64 * j, NB - 1);
       cg[r][j] = load_block<SCHEME>(ex.wgu + grow * rb, b);
       cu[r][j] = load_block<SCHEME>(ex.wgu + urow * rb, b);
-      sg[r][j] = f16_bits_to_f32(ex.sgu[grow * NB + b]);
-      su[r][j] = f16_bits_to_f32(ex.sgu[urow * NB + b]);
+      sg[r][j] = scale_or_zero(ex.sgu + grow * NB + b, resident);
+      su[r][j] = scale_or_zero(ex.sgu + urow * NB + b, resident);
     }
   }
-  if constexpr (kStageX) {
-#pragma unroll
-    for (int j = 0; j < NBJ; ++j) {
-      const int b = min(lane + 64 * j, NB - 1);
-      uint32_t nat[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 v = xs[4 * b + i];
-        nat[4 * i] = v.x; nat[4 * i + 1] = v.y; nat[4 * i + 2] = v.z; nat[4 * i + 3] = v.w;
-      }
-      xr[j].h = xblock_from_pairs<SCHEME>(nat);
-    }
+  // the down kernel reads the weights' indices (slots when staged), the caller the expert ids
+  if (publisher && wave == 0 && lane < k) {
+    idx_ws[lane] = pub_row;
+    gate_ws[lane] = pub_gate;
+    if (idx_user) idx_user[lane] = pub_idx;
+    if (gate_user) gate_user[lane] = pub_gate;
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -157,14 +187,14 @@ __device__ __forceinline__ void gate_up_t1_body(const void* __restrict__ x, cons
   }
 }
 
-template <int SCHEME, int XT, int NBJ, int RP, bool FROM_LOGITS, int VPL, bool H16>
+template <int SCHEME, int XT, int NBJ, int RP, int ROUTE, int VPL, bool H16>
 __global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1(const void* __restrict__ x, ExpertsDev ex, int k, int renorm,
                                                     const float* __restrict__ logits,
                                                     const int32_t* __restrict__ idx_in,
                                                     int32_t* __restrict__ idx_ws, float* __restrict__ gate_ws,
                                                     int32_t* __restrict__ idx_user, float* __restrict__ gate_user,
                                                     float* __restrict__ h, int blocks_per_slot) {
-  gate_up_t1_body<SCHEME, XT, NBJ, RP, FROM_LOGITS, VPL, H16>(x, ex, k, renorm, logits, idx_in, idx_ws, gate_ws,
+  gate_up_t1_body<SCHEME, XT, NBJ, RP, ROUTE, VPL, H16>(x, ex, k, renorm, logits, idx_in, idx_ws, gate_ws,
                                                              idx_user, gate_user, h, blocks_per_slot, blockIdx.x);
 }
 
@@ -186,10 +216,16 @@ __device__ __forceinline__ void down_t1_slots_body(const ExpertsDev& ex, int k, 
   const int H = ex.H, I = ex.I, NBI = I / 32;
   const int mb = (int)bid * 4 * RW, m0 = mb + lg * RW;
   const int64_t rb = row_bytes<SCHEME>(I);
+  // idx holds weight indices, or expert ids mapped here through a slot table;
+  // an expert without a slot contributes nothing. The index is requested
+  // first, so that waiting for it does not wait for the h loads too.
+  const int iq = idx[q];
   XBlockH<SCHEME> hb[NBJ];
 #pragma unroll
   for (int j = 0; j < NBJ; ++j) hb[j] = load_xblock_h<SCHEME>(h16, (int64_t)q * I, min(ll + 16 * j, NBI - 1));
-  const int e = idx[q];
+  int e = expert_index(ex, iq);
+  const bool resident = e >= 0;  // a slot-less expert: zero scales, whatever slot 0 holds
+  e = max(e, 0);
   Block<SCHEME> c[RW][NBJ];
   float sc[RW][NBJ];
 #pragma unroll
@@ -199,7 +235,7 @@ __device__ __forceinline__ void down_t1_slots_body(const ExpertsDev& ex, int k, 
     for (int j = 0; j < NBJ; ++j) {
       const int b = min(ll + 16 * j, NBI - 1);
       c[r][j] = load_block<SCHEME>(ex.wd + row * rb, b);
-      sc[r][j] = f16_bits_to_f32(ex.sd[row * NBI + b]);
+      sc[r][j] = scale_or_zero(ex.sd + row * NBI + b, resident);
     }
   }
 #pragma unroll
@@ -249,12 +285,13 @@ __global__ __launch_bounds__(128) void k_down_t1(ExpertsDev ex, int k, const int
     float sc[KC][NBJ];
 #pragma unroll
     for (int q = 0; q < KC; ++q) {
-      const int64_t row = (int64_t)idx[min(s0 + q, k - 1)] * H + mm;
+      const int ei = expert_index(ex, idx[min(s0 + q, k - 1)]);  // -1: no slot, contributes nothing
+      const int64_t row = (int64_t)max(ei, 0) * H + mm;
 #pragma unroll
       for (int j = 0; j < NBJ; ++j) {
         const int b = min(ll + 16 * j, NBI - 1);
         c[q][j] = load_block<SCHEME>(ex.wd + row * rb, b);
-        sc[q][j] = f16_bits_to_f32(ex.sd[row * NBI + b]);
+        sc[q][j] = scale_or_zero(ex.sd + row * NBI + b, ei >= 0);
       }
     }
 #pragma unroll
@@ -365,6 +402,7 @@ __global__ __launch_bounds__(256) void k_gate_up_grouped(const void* __restrict_
   if (u >= *n_uniq) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = uniq[u], cnt = counts[e], beg = offsets[e];
+  const int ew = expert_index(ex, e);  // -1: no slot, contributes nothing
   const int H = ex.H, I = ex.I, NB = H / 32;
   const int n0 = (blockIdx.x * 4 + wave) * RP;
   const int64_t rb = row_bytes<SCHEME>(H);
@@ -373,15 +411,15 @@ __global__ __launch_bounds__(256) void k_gate_up_grouped(const void* __restrict_
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
     const int n = min(n0 + r, I - 1);
-    const int64_t grow = (int64_t)e * 2 * I + n, urow = grow + I;
+    const int64_t grow = (int64_t)max(ew, 0) * 2 * I + n, urow = grow + I;
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) {
       const int b = min(lane + 64 * j, NB - 1);
-      const float valid = lane + 64 * j < NB ? 1.0f : 0.0f;
+      const bool valid = lane + 64 * j < NB && ew >= 0;
       cg[r][j] = load_block<SCHEME>(ex.wgu + grow * rb, b);
       cu[r][j] = load_block<SCHEME>(ex.wgu + urow * rb, b);
-      sg[r][j] = valid * f16_bits_to_f32(ex.sgu[grow * NB + b]);
-      su[r][j] = valid * f16_bits_to_f32(ex.sgu[urow * NB + b]);
+      sg[r][j] = scale_or_zero(ex.sgu + grow * NB + b, valid);
+      su[r][j] = scale_or_zero(ex.sgu + urow * NB + b, valid);
     }
   }
   constexpr int xbytes = XT == MOE_F32 ? 4 : 2;
@@ -433,18 +471,19 @@ __global__ __launch_bounds__(256) void k_down_grouped(ExpertsDev ex, int k, cons
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lg = lane >> 4, ll = lane & 15;
   const int e = uniq[u], cnt = counts[e], beg = offsets[e];
+  const int ew = expert_index(ex, e);  // -1: no slot, contributes nothing
   const int H = ex.H, I = ex.I, NBI = I / 32;
   const int m = (blockIdx.x * 4 + wave) * 4 + lg;
   const int mm = min(m, H - 1);
   const int64_t rb = row_bytes<SCHEME>(I);
-  const int64_t row = (int64_t)e * H + mm;
+  const int64_t row = (int64_t)max(ew, 0) * H + mm;
   Block<SCHEME> c[NBJ];
   float sc[NBJ];
 #pragma unroll
   for (int j = 0; j < NBJ; ++j) {
     const int b = min(ll + 16 * j, NBI - 1);
     c[j] = load_block<SCHEME>(ex.wd + row * rb, b);
-    sc[j] = (ll + 16 * j < NBI ? 1.0f : 0.0f) * f16_bits_to_f32(ex.sd[row * NBI + b]);
+    sc[j] = scale_or_zero(ex.sd + row * NBI + b, ll + 16 * j < NBI && ew >= 0);
   }
   const int pblk = lds_block_stride(4), stride = NBI * pblk;
   const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
@@ -534,20 +573,26 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
         constexpr int NBJ = decltype(NBJc)::value, RP = decltype(RPc)::value;
         const int bps = (ex.I + kGateUpWaves * RP - 1) / (kGateUpWaves * RP);
         dim3 grid(k * bps);
-        auto launch = [&](auto FLc, auto VPLc, auto H16c) {
-          constexpr bool FL = decltype(FLc)::value != 0, H16 = decltype(H16c)::value != 0;
-          constexpr int VPL = decltype(VPLc)::value;
-          MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_t1<SC, XT, NBJ, RP, FL, VPL, H16>), grid, dim3(64 * kGateUpWaves), 0, s, x, ex,
+        auto launch = [&](auto RTc, auto VPLc, auto H16c) {
+          constexpr bool H16 = decltype(H16c)::value != 0;
+          constexpr int RT = decltype(RTc)::value, VPL = decltype(VPLc)::value;
+          MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_t1<SC, XT, NBJ, RP, RT, VPL, H16>), grid, dim3(64 * kGateUpWaves), 0, s, x, ex,
                      k, renorm, logits, idx_in, idx_ws, gate_ws, idx_user, gate_user, h, bps);
         };
-        auto with_h = [&](auto FLc, auto VPLc) {
-          if (slots) launch(FLc, VPLc, IC<1>{});
-          else launch(FLc, VPLc, IC<0>{});
+        auto with_h = [&](auto RTc, auto VPLc) {
+          if (slots) launch(RTc, VPLc, IC<1>{});
+          else launch(RTc, VPLc, IC<0>{});
+        };
+        // the top-k over a slot table is a kernel of its own, so that the
+        // plain one carries none of its code
+        auto with_vpl = [&](auto RTc) {
+          if (ex.E <= 256) with_h(RTc, IC<4>{});
+          else if (ex.E <= 512) with_h(RTc, IC<8>{});
+          else with_h(RTc, IC<16>{});
         };
         if (!from_logits) with_h(IC<0>{}, IC<1>{});
-        else if (ex.E <= 256) with_h(IC<1>{}, IC<4>{});
-        else if (ex.E <= 512) with_h(IC<1>{}, IC<8>{});
-        else with_h(IC<1>{}, IC<16>{});
+        else if (ex.slot_of) with_vpl(IC<2>{});
+        else with_vpl(IC<1>{});
       };
       if (nbj <= 1) go(IC<1>{}, IC<1>{});
       else go(IC<2>{}, IC<1>{});
@@ -555,23 +600,27 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
   });
   const int32_t* idx = from_logits ? idx_ws : idx_in;
   const float* gate = from_logits ? gate_ws : gate_in;
+  // from logits, gate/up publishes weight indices (slots when staged): the
+  // down kernel takes them as they are
+  ExpertsDev exd = ex;
+  if (from_logits) exd.slot_of = nullptr;
   with_scheme(ex.scheme, [&](auto S) {
     constexpr int SC = decltype(S)::value;
     if (slots) {
       dim3 grid((ex.H + 4 * kDownRows - 1) / (4 * kDownRows));
       const uint16_t* h16 = reinterpret_cast<const uint16_t*>(h);
       if (nbi <= 1)
-        MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_t1_slots<SC, 1, kDownRows>), grid, dim3(64 * k), 0, s, ex, k, idx, gate,
+        MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_t1_slots<SC, 1, kDownRows>), grid, dim3(64 * k), 0, s, exd, k, idx, gate,
                    h16, y);
       else
-        MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_t1_slots<SC, 2, kDownRows>), grid, dim3(64 * k), 0, s, ex, k, idx, gate,
+        MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_t1_slots<SC, 2, kDownRows>), grid, dim3(64 * k), 0, s, exd, k, idx, gate,
                    h16, y);
       return;
     }
     dim3 grid((ex.H + 7) / 8);
     auto go = [&](auto NBJc) {
       constexpr int NBJ = decltype(NBJc)::value;
-      MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_t1<SC, NBJ>), grid, dim3(128), 0, s, ex, k, idx, gate, h, y);
+      MOE_LAUNCH(MOE_KERNEL_DOWN, (k_down_t1<SC, NBJ>), grid, dim3(128), 0, s, exd, k, idx, gate, h, y);
     };
     if (nbi <= 4) go(IC<4>{});
     else go(IC<8>{});
@@ -602,7 +651,7 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1_head(
   static_assert(kGateUpWaves == kHeadWaves, "head rows run on gate/up-sized workgroups");
   const int nhead = hd.F + hd.E;
   if ((int)blockIdx.x >= nhead) {
-    gate_up_t1_body<SCHEME, XT, NBJ, 1, true, VPL, true>(x, ex, k, renorm, logits, nullptr, idx_ws, gate_ws, idx_user,
+    gate_up_t1_body<SCHEME, XT, NBJ, 1, 1, VPL, true>(x, ex, k, renorm, logits, nullptr, idx_ws, gate_ws, idx_user,
                                                          gate_user, h, blocks_per_slot, (int)blockIdx.x - nhead);
     return;
   }

@@ -200,6 +200,8 @@ __global__ __launch_bounds__(256) void k_gemm_grouped(const uint16_t* __restrict
   const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, r16 = lane & 15;
   const int e = uniq[u], cnt = counts[e], beg = offsets[e];
+  const int ew = expert_index(ex, e);       // -1: no slot, contributes nothing
+  const bool resident = ew >= 0;  // a slot-less expert: zero scales, whatever slot 0 holds
   const int H = ex.H, I = ex.I;
   const int K = MODE == 0 ? H : I;          // reduction length
   const int NB = K / 32;                    // quantisation blocks per weight row
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(256) void k_gemm_grouped(const uint16_t* __restrict
   }
   int64_t wrow[2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) wrow[c] = (int64_t)e * NROW + min(col[c] + r16, NROW - 1);
+  for (int c = 0; c < 2; ++c) wrow[c] = (int64_t)max(ew, 0) * NROW + min(col[c] + r16, NROW - 1);
   const int nchunks = (K + kRegChunk - 1) / kRegChunk;
   const int nsl = (I + 63) / 64;  // h slices per assignment row
   using M = BlockMfma<AT>;
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(256) void k_gemm_grouped(const uint16_t* __restrict
           const uint8_t* row = W + wrow[c] * rb;
           if constexpr (SCHEME == MOE_Q_SYM8) cw[c][b] = *reinterpret_cast<const u32x2*>(row + 32 * bc + 8 * g);
           else cw[c][b] = *reinterpret_cast<const uint32_t*>(row + 16 * bc + 4 * g);
-          sc[c][b] = blk < NB ? f16_bits_to_f32(S[wrow[c] * NB + bc]) : 0.0f;
+          sc[c][b] = scale_or_zero(S + wrow[c] * NB + bc, blk < NB && resident);
           // down: h of this block's 64-column slice was stored times 2^-sigma
           if (MODE == 1) sc[c][b] = ldexpf(sc[c][b], sg[blk >> 1]);
         }
@@ -508,14 +510,16 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
     const int u = (rest / ncb) * 8 + (tile & 7);
     if (u >= nu) continue;
     const int e = uniq[u], cnt = counts[e], beg = offsets[e];
+    const int ew = expert_index(ex, e);  // -1: no slot, contributes nothing (index 0, zero scales)
+    const bool resident = ew >= 0;  // a slot-less expert: zero scales, whatever slot 0 holds
     const int H = ex.H, I = ex.I;
     const int K = MODE == 0 ? H : I;
     const int NB = K / 32;
     const int NROW = MODE == 0 ? 2 * I : H;
     const int lim = MODE == 0 ? I : H;
     const int rb = (int)row_bytes<SCHEME>(K);
-    const uint8_t* Wexp = (MODE == 0 ? ex.wgu : ex.wd) + (int64_t)e * NROW * rb;
-    const uint16_t* Sexp = (MODE == 0 ? ex.sgu : ex.sd) + (int64_t)e * NROW * NB;
+    const uint8_t* Wexp = (MODE == 0 ? ex.wgu : ex.wd) + (int64_t)max(ew, 0) * NROW * rb;
+    const uint16_t* Sexp = (MODE == 0 ? ex.sgu : ex.sd) + (int64_t)max(ew, 0) * NROW * NB;
     const int n0 = MODE == 0 ? cb * 64 : cb * 128;
     // workgroup-local weight row lr (0..127) -> row of the expert (clamped in range)
     auto grow = [&](int lr) {
@@ -619,8 +623,8 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
 #pragma unroll
         for (int b = 0; b < D::BPS; ++b) {
           const bool valid = q * D::BPS + b < NB;  // K tail: blocks past the row end count 0
-          float s0 = valid ? f16_bits_to_f32((uint16_t)scale_bits(sw[0], b)) : 0.0f;
-          float s1 = valid ? f16_bits_to_f32((uint16_t)scale_bits(sw[1], b)) : 0.0f;
+          float s0 = valid && resident ? f16_bits_to_f32((uint16_t)scale_bits(sw[0], b)) : 0.0f;
+          float s1 = valid && resident ? f16_bits_to_f32((uint16_t)scale_bits(sw[1], b)) : 0.0f;
           if constexpr (MODE == 1) {
             // h of this block's 64-column slice was stored times 2^-sigma
             const int sgm = word_at(sgw[0], b >> 1);

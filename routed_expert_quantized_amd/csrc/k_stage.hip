@@ -39,9 +39,13 @@ __global__ __launch_bounds__(256) void k_stage_experts(ExpertsDev pool, ExpertsD
 }
 
 __global__ __launch_bounds__(256) void k_remap_ids(const int32_t* __restrict__ idx, int64_t n,
-                                                   const int32_t* __restrict__ slot_of, int32_t* __restrict__ out) {
+                                                   const int32_t* __restrict__ slot_of, int E,
+                                                   int32_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) out[i] = slot_of[idx[i]];
+  if (i < n) {
+    const int e = idx[i];
+    out[i] = e >= 0 && e < E ? slot_of[e] : -1;
+  }
 }
 
 hipError_t launch_stage_experts(const ExpertsDev& pool, const ExpertsDev& stack, const int32_t* experts,
@@ -53,9 +57,10 @@ hipError_t launch_stage_experts(const ExpertsDev& pool, const ExpertsDev& stack,
   return hipGetLastError();
 }
 
-hipError_t launch_remap_ids(const int32_t* idx, int64_t n, const int32_t* slot_of, int32_t* out, hipStream_t s) {
+hipError_t launch_remap_ids(const int32_t* idx, int64_t n, const int32_t* slot_of, int E, int32_t* out,
+                            hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_remap_ids, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, n, slot_of, out);
+  hipLaunchKernelGGL(k_remap_ids, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, n, slot_of, E, out);
   return hipGetLastError();
 }
 

@@ -41,14 +41,28 @@ struct GroupBufs {
   int32_t* n_uniq;   // [1]
 };
 
-// Experts as the kernels see them (byte pointers, decoded struct).
+// Experts as the kernels see them (byte pointers, decoded struct). E is the
+// number of experts the routing ranges over. With a slot table (staged
+// decode), expert e's weights sit at index slot_of[e] of a stack of `slots`
+// experts; without one (slot_of null) at index e.
 struct ExpertsDev {
   int E, H, I, scheme;
   const uint8_t* wgu;
   const uint16_t* sgu;
   const uint8_t* wd;
   const uint16_t* sd;
+  const int32_t* slot_of = nullptr;
+  int slots = 0;
 };
+
+// Index of expert e's weights: slot_of[e] when staged, else e. -1 for an
+// expert without a slot in [0, slots): such an expert contributes nothing
+// (kernels read index 0 with zero scales in its place).
+__device__ __forceinline__ int expert_index(const ExpertsDev& ex, int e) {
+  if (!ex.slot_of) return e;
+  const int s = ex.slot_of[e];
+  return s >= 0 && s < ex.slots ? s : -1;
+}
 
 // Split-K planes of the router logits the workspace holds room for: the batch
 // router may write up to this many partial [T][E] planes (summed by the top-k).
@@ -78,10 +92,12 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
                             int32_t* idx_ws, float* gate_ws, int32_t* idx_user, float* gate_user,
                             float* h, float* y, hipStream_t s);
 
-// Staged decode: copy experts[i] of pool into slot slots[i] of stack; out = slot_of[idx].
+// Staged decode: copy experts[i] of pool into slot slots[i] of stack;
+// out = slot_of[idx] for ids in [0, E), -1 for ids outside it.
 hipError_t launch_stage_experts(const ExpertsDev& pool, const ExpertsDev& stack, const int32_t* experts,
                                 const int32_t* slots, int n, hipStream_t s);
-hipError_t launch_remap_ids(const int32_t* idx, int64_t n, const int32_t* slot_of, int32_t* out, hipStream_t s);
+hipError_t launch_remap_ids(const int32_t* idx, int64_t n, const int32_t* slot_of, int E, int32_t* out,
+                            hipStream_t s);
 
 // Host replay of the expert-cache miss policies (arguments checked by the caller).
 void miss_replay(const int32_t* idx, const float* gate, int T, int k, int E, int capacity, int policy,

@@ -382,6 +382,33 @@ moe_status moe_layer_forward(const void* x, int32_t xtype, int32_t T, const floa
   return layer_from_logits(x, xtype, T, d, k, flags, logits, nsplit, y, topk_idx_out, topk_gate_out, ws, L, s);
 }
 
+moe_status moe_layer_forward_staged(const void* x, int32_t xtype, int32_t T, const float* router_w, int32_t E,
+                                    const moe_experts* stack, const int32_t* slot_of, int32_t k, uint32_t flags,
+                                    float* y, int32_t* topk_idx_out, float* topk_gate_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  moe_status st;
+  moe::ExpertsDev d;
+  Layout L;
+  if (!stack) return fail(MOE_ERR_INVALID_ARG, "stack struct is NULL");
+  if (stack->E < 1 || stack->E > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "stack slots %d outside [1, 2^20]", stack->E);
+  if (!slot_of) return fail(MOE_ERR_INVALID_ARG, "slot_of is NULL");
+  if (!aligned(slot_of, 4)) return fail(MOE_ERR_INVALID_ARG, "slot_of is not 4-byte aligned");
+  // the routing ranges over E experts; the weights sit in the stack's slots
+  moe_experts routed = *stack;
+  routed.E = E;
+  if ((st = check_layer_args(x, xtype, T, &routed, k, flags, y, ws, ws_bytes, &d, &L))) return st;
+  if ((st = check_router(router_w))) return st;
+  d.slot_of = slot_of;
+  d.slots = stack->E;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logits = at<float>(ws, L.logits);
+  int nsplit = 1;
+  hipError_t e = moe::launch_logits(x, xtype, T, d.H, router_w, d.E, logits, &nsplit,
+                                    T >= moe::kSplitRouterMinT ? at<uint16_t>(ws, L.r3) : nullptr, s);
+  if (e != hipSuccess) return hip_status(e, "router logits");
+  return layer_from_logits(x, xtype, T, d, k, flags, logits, nsplit, y, topk_idx_out, topk_gate_out, ws, L, s);
+}
+
 moe_status moe_layer_forward_noalloc(const void* x, int32_t xtype, int32_t T, const float* router_w,
                                      const moe_experts* ex, int32_t k, uint32_t flags, float* y,
                                      int32_t* topk_idx_out, float* topk_gate_out, void* stream) {
@@ -472,7 +499,7 @@ moe_status moe_remap_ids(const int32_t* idx, int64_t n, const int32_t* slot_of, 
                          void* stream) {
   if (n < 0 || E < 1) return fail(MOE_ERR_INVALID_ARG, "n=%lld E=%d", (long long)n, E);
   if (n > 0 && (!idx || !slot_of || !out)) return fail(MOE_ERR_INVALID_ARG, "idx, slot_of or out is NULL");
-  return hip_status(moe::launch_remap_ids(idx, n, slot_of, out, static_cast<hipStream_t>(stream)), "remap ids");
+  return hip_status(moe::launch_remap_ids(idx, n, slot_of, E, out, static_cast<hipStream_t>(stream)), "remap ids");
 }
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }

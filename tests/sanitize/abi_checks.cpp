@@ -38,7 +38,7 @@ hipError_t launch_decode_t1(const void*, int, const ExpertsDev&, int, int, const
 }
 hipError_t launch_stage_experts(const ExpertsDev&, const ExpertsDev&, const int32_t*, const int32_t*, int,
                                 hipStream_t) { launched("staging"); }
-hipError_t launch_remap_ids(const int32_t*, int64_t, const int32_t*, int32_t*, hipStream_t) { launched("remap"); }
+hipError_t launch_remap_ids(const int32_t*, int64_t, const int32_t*, int, int32_t*, hipStream_t) { launched("remap"); }
 hipError_t launch_stream_read(const void*, int64_t, hipStream_t) { launched("stream read"); }
 hipError_t launch_decode_grouped(const void*, int, int, const ExpertsDev&, int, const GroupBufs&, const float*, float*,
                                  float*, float*, hipStream_t) { launched("grouped decode"); }
@@ -119,6 +119,13 @@ int main() {
   rejected(moe_layer_forward(F, MOE_F16, 1, FF, &ex, 300, 1, FF, nullptr, nullptr, F, big, nullptr));
   rejected(moe_layer_forward(F, MOE_F16, 70000, FF, &ex, 8, 1, FF, nullptr, nullptr, F, big, nullptr));
   rejected(moe_layer_forward_noalloc(F, MOE_BF16, 2048, FF, &ex, 8, 1, FF, nullptr, nullptr, nullptr));
+  const moe_experts stack8 = experts(8, 2048, 512, MOE_Q_SYM8);
+  rejected(moe_layer_forward_staged(F, MOE_F16, 1, FF, 256, nullptr, FI, 8, 1, FF, nullptr, nullptr, F, big, nullptr));
+  rejected(moe_layer_forward_staged(F, MOE_F16, 1, FF, 256, &stack8, nullptr, 8, 1, FF, nullptr, nullptr, F, big,
+                                    nullptr));
+  rejected(moe_layer_forward_staged(F, MOE_F16, 1, FF, 2000, &stack8, FI, 8, 1, FF, nullptr, nullptr, F, big,
+                                    nullptr));
+  rejected(moe_layer_forward_staged(F, MOE_F16, 1, FF, 256, &stack8, FI, 8, 1, FF, nullptr, nullptr, F, 64, nullptr));
   rejected(moe_layer_forward_noalloc(F, MOE_F16, 1, FF, &ex, 8, 0x40, FF, nullptr, nullptr, nullptr));
   rejected(moe_experts_from_logits(F, MOE_F16, 1, nullptr, &ex, 8, 1, FF, nullptr, nullptr, F, big, nullptr));
   rejected(moe_experts_from_logits(F, MOE_F16, 1, reinterpret_cast<float*>(MIS), &ex, 8, 1, FF, nullptr, nullptr, F,

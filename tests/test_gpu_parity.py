@@ -14,7 +14,7 @@ import oracle
 import routed_expert_quantized_amd as rq
 import synth
 from tests.cases import GATE_ATOL, Y_REL_NORM, enforce_gap, rel_inf_err, rel_norm_err
-from tests.gpu_cases import device_pool, oracle_compact, remap, to_dev_x
+from tests.gpu_cases import NAN_F16, device_pool, oracle_compact, remap, to_dev_x
 
 pytestmark = pytest.mark.gpu
 
@@ -351,6 +351,84 @@ def test_single_token_layer_edge_shapes(E, H, I, k, scheme, xtype):
     assert rel_norm_err(y.cpu().numpy(), ref) <= Y_REL_NORM
 
 
+# staged layer: (workload, tokens, path); one token runs the slot lookup inside
+# the gate/up kernel's top-k, batches inside the grouped kernels
+STAGED = [("decode40", 1, "auto"), ("batched_int4", 1, "auto"), ("tiny", 1, "auto"), ("batched_int4", 64, "auto"),
+          ("large_int4", 16, "auto"), ("batched_int4", 7, "gather"), ("decode40", 3, "gemm")]
+
+
+@pytest.mark.parametrize("name,T,path", STAGED)
+def test_staged_layer_matches_oracle(name, T, path):
+    """The layer on a resident stack behind a slot table (moe_layer_forward_staged):
+    routing identical to the oracle's (expert ids), output within the contract
+    of the oracle layer on the experts themselves, and equal, bit for bit, to the
+    same kernels on the full pool."""
+    w = synth.WORKLOADS[name]
+    li = enforce_gap(w, synth.draw_layer(w, seed=9, layer=0, T=T, with_experts=False), seed=9, layer=0)
+    bf16 = w.xtype == synth.BF16
+    ridx, rgate = oracle.route(li.x, li.R, w.k, bf16=bf16)
+    routed = np.unique(ridx)
+    g = np.random.default_rng(len(routed) + T)
+    # resident: the routed experts and as many others, in shuffled slots
+    others = g.choice(np.setdiff1d(np.arange(w.E), routed), min(len(routed), w.E - len(routed)), replace=False)
+    resident = np.concatenate([routed, others]).astype(np.int32)
+    slots = g.permutation(len(resident)).astype(np.int32)
+    say(f"staged {name} T={T} path={path}: {len(routed)} routed experts, {len(resident)} slots")
+    pool = device_pool(w, 9, 0, resident)
+    stack = rq.empty_stack(pool, len(resident))
+    rq.moe_stage_experts(pool, stack, torch.from_numpy(resident).cuda(), torch.from_numpy(slots).cuda())
+    slot_of = np.full(w.E, -1, dtype=np.int32)
+    slot_of[resident] = slots
+    xd, Rd = to_dev_x(li.x, w.xtype), torch.from_numpy(li.R).cuda()
+    fl = rq.MOE_FLAG_RENORM | PATHS[path]
+    y, idx, gate = rq.moe_layer_forward_staged(xd, Rd, stack, torch.from_numpy(slot_of).cuda(), w.k, fl)
+    y_pool = rq.moe_layer_forward(xd, Rd, pool, w.k, fl)[0]
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
+    rex, m = oracle_compact(w, 9, 0, routed)
+    ref = oracle.gather_forward(li.x, rex, remap(ridx, m), rgate, bf16=bf16)
+    assert rel_norm_err(y.cpu().numpy(), ref) <= Y_REL_NORM
+    assert torch.equal(y, y_pool)
+
+
+@pytest.mark.parametrize("T,path", [(1, "auto"), (5, "auto"), (5, "gather")])
+def test_staged_layer_skips_experts_without_a_slot(T, path):
+    """A routed expert without a slot contributes nothing: the result equals the
+    oracle's with that expert's weights zero, and nothing outside the stack is
+    read (the stack holds only the resident experts)."""
+    w = synth.WORKLOADS["decode40"]
+    li = enforce_gap(w, synth.draw_layer(w, seed=13, layer=0, T=T, with_experts=False), seed=13, layer=0)
+    ridx, rgate = oracle.route(li.x, li.R, w.k)
+    routed = np.unique(ridx)
+    missing = ridx[0, 1]                      # slot 1 of the first token is not resident
+    resident = np.array([e for e in routed if e != missing], dtype=np.int32)
+    pool = device_pool(w, 13, 0, resident)
+    # slot 0 holds no expert: codes 0x5A and NaN scales, which a slot-less expert must not pick up
+    stack = rq.empty_stack(pool, len(resident) + 1)
+    stack.w_gate_up[0].fill_(0x5A)
+    stack.w_down[0].fill_(0x5A)
+    stack.s_gate_up[0].fill_(NAN_F16)
+    stack.s_down[0].fill_(NAN_F16)
+    rq.moe_stage_experts(pool, stack, torch.from_numpy(resident).cuda(),
+                         torch.arange(1, len(resident) + 1, dtype=torch.int32, device="cuda"))
+    slot_of = np.full(w.E, -1, dtype=np.int32)
+    slot_of[resident] = np.arange(1, len(resident) + 1, dtype=np.int32)
+    y, idx, gate = rq.moe_layer_forward_staged(to_dev_x(li.x, w.xtype), torch.from_numpy(li.R).cuda(), stack,
+                                               torch.from_numpy(slot_of).cuda(), w.k,
+                                               rq.MOE_FLAG_RENORM | PATHS[path])
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    rex, m = oracle_compact(w, 13, 0, routed)
+    j = m[int(missing)]
+    rex.s_gate_up[j] = 0
+    rex.s_down[j] = 0
+    ref = oracle.gather_forward(li.x, rex, remap(ridx, m), rgate)
+    yn = y.cpu().numpy()
+    assert np.isfinite(yn).all()
+    assert rel_norm_err(yn, ref) <= Y_REL_NORM
+
+
 @pytest.mark.parametrize("scheme", [rq.MOE_Q_SYM8, rq.MOE_Q_INT4])
 @pytest.mark.parametrize("T", [1, 5])
 def test_staged_stack_matches_pool(scheme, T):
@@ -388,3 +466,10 @@ def test_staged_stack_matches_pool(scheme, T):
     y_pool = rq.moe_gather_qmm_forward(x, pool, torch.from_numpy(idx).cuda(), gd)
     torch.cuda.synchronize()
     assert rel_norm_err(y_stack.cpu().numpy(), y_pool.cpu().numpy()) <= 1e-6
+    # against the oracle on the experts themselves (expert ids)
+    rex = oracle.quantize_experts(wgu.cpu().numpy(), wd.cpu().numpy(), scheme)
+    ref = oracle.gather_forward(x.cpu().numpy(), rex, idx, gate)
+    assert rel_norm_err(y_stack.cpu().numpy(), ref) <= Y_REL_NORM
+    # ids outside [0, E) map to -1
+    odd = torch.tensor([-1, E, 0], dtype=torch.int32, device="cuda")
+    assert rq.moe_remap_ids(odd, torch.from_numpy(slot_of).cuda()).cpu().tolist() == [-1, -1, int(slot_of[0])]
