@@ -162,6 +162,14 @@ __device__ __forceinline__ float workgroup_absmax(float v, float* red) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+// Instruction groups for the scheduler: the next `n` instructions of a kind
+// (in the order the calls are made within one scheduling region).
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008;
+template <int KIND, int N>
+__device__ __forceinline__ void sched_group() {
+  __builtin_amdgcn_sched_group_barrier(KIND, N, 0);
+}
+
 // acc += s * p for the four outputs a lane holds of one tile.
 __device__ __forceinline__ void scaled_add(float4v& acc, float s, float4v p) {
 #pragma unroll
@@ -468,7 +476,7 @@ __device__ __forceinline__ uint32_t scale_bits(const W& w, int b) {
 }
 
 template <int SCHEME, int AT, int MODE, int MT, int NS, int LB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 8)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 6 ? 2 : 1, 8)))
 void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const int32_t* __restrict__ uniq,
                 const int32_t* __restrict__ n_uniq, const int32_t* __restrict__ counts,
                 const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, uint16_t* __restrict__ h16,
@@ -573,7 +581,6 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int c = 0; c < 2; ++c) acc[mt][c] = float4v{0.f, 0.f, 0.f, 0.f};
-      const int mtiles = (nm + 15) / 16;
 
       auto issue = [&](int q, uint8_t* Bst) {
         uint8_t* Sst = Bst + D::B_BYTES;
@@ -619,30 +626,54 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
         lds_wait(cw1);
         lds_wait(sw);
         if constexpr (MODE == 1) lds_wait(sgw);
+        // a block's scales, zero past the row end (K tail) or for a slot-less
+        // expert; the mask keeps this free of branches, which would split the
+        // scheduling region of the MFMA chain
+        const uint32_t live = resident ? 0xFFFFu : 0u;
+        auto scale = [&](int c, int b) {
+          uint32_t m = q * D::BPS + b < NB ? live : 0u;
+          asm("" : "+v"(m));
+          float v = f16_bits_to_f32((uint16_t)(scale_bits(sw[c], b) & m));
+          // down: h of this block's 64-column slice was stored times 2^-sigma
+          if constexpr (MODE == 1) v = ldexpf(v, word_at(sgw[0], b >> 1));
+          // converted here, once per block: folded into each FMA instead
+          // (v_fma_mix_f32 on the fp16 bits) the FMAs run slower
+          asm("" : "+v"(v));
+          return v;
+        };
+        typename M::v8 bc0 = codes8<SCHEME, AT>(cw0[0]), bc1 = codes8<SCHEME, AT>(cw1[0]);
         lds_wait(fa[0]);
 #pragma unroll
         for (int b = 0; b < D::BPS; ++b) {
-          const bool valid = q * D::BPS + b < NB;  // K tail: blocks past the row end count 0
-          float s0 = valid && resident ? f16_bits_to_f32((uint16_t)scale_bits(sw[0], b)) : 0.0f;
-          float s1 = valid && resident ? f16_bits_to_f32((uint16_t)scale_bits(sw[1], b)) : 0.0f;
-          if constexpr (MODE == 1) {
-            // h of this block's 64-column slice was stored times 2^-sigma
-            const int sgm = word_at(sgw[0], b >> 1);
-            s0 = ldexpf(s0, sgm);
-            s1 = ldexpf(s1, sgm);
-          }
-          const typename M::v8 b0 = codes8<SCHEME, AT>(cw0[b]);
-          const typename M::v8 b1 = codes8<SCHEME, AT>(cw1[b]);
+          const float s0 = scale(0, b), s1 = scale(1, b);
           if (b + 1 < D::BPS) read_a(b + 1, fa[(b + 1) & 1]);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            if (mt < mtiles) {
-              const typename M::v8 a = a_operand<SCHEME, AT>(fa[b & 1][mt]);
-              scaled_add(acc[mt][0], s0, M::run(a, b0));
-              scaled_add(acc[mt][1], s1, M::run(a, b1));
+          // Every M tile runs, also past the pass's last assignment (those rows
+          // repeat a valid row and are discarded): no branches between the MFMAs.
+          // The 2 MT products go out in a chain where product j is issued before
+          // the four scale FMAs of product j-1, in two alternating registers, so
+          // the FMAs (and the conversion of the next block's codes) run while the
+          // next MFMA is in the matrix core instead of waiting for their own.
+          typename M::v8 bn0, bn1;
+          float4v pp[2];
+          static_for<2 * MT>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            pp[j & 1] = M::run(a_operand<SCHEME, AT>(fa[b & 1][j / 2]), (j & 1) ? bc1 : bc0);
+            if constexpr (j > 0) scaled_add(acc[(j - 1) / 2][(j - 1) & 1], ((j - 1) & 1) ? s1 : s0, pp[(j - 1) & 1]);
+            if constexpr (j == 0) {
+              if (b + 1 < D::BPS) {
+                bn0 = codes8<SCHEME, AT>(cw0[b + 1]);
+                bn1 = codes8<SCHEME, AT>(cw1[b + 1]);
+              }
             }
+            sched_group<kSchedMfma, 1>();
+            sched_group<kSchedValu, j == 0 ? 2 : 6>();
+          });
+          scaled_add(acc[MT - 1][1], s1, pp[(2 * MT - 1) & 1]);
+          if (b + 1 < D::BPS) {
+            bc0 = bn0;
+            bc1 = bn1;
+            lds_wait(fa[(b + 1) & 1]);
           }
-          if (b + 1 < D::BPS) lds_wait(fa[(b + 1) & 1]);
         }
       };
 
