@@ -476,7 +476,7 @@ __device__ __forceinline__ uint32_t scale_bits(const W& w, int b) {
 }
 
 template <int SCHEME, int AT, int MODE, int MT, int NS, int LB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 6 ? 2 : 1, 8)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 6 ? 2 : (MT == 1 ? (SCHEME == MOE_Q_SYM8 ? 3 : 2) : 1), 8)))
 void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const int32_t* __restrict__ uniq,
                 const int32_t* __restrict__ n_uniq, const int32_t* __restrict__ counts,
                 const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, uint16_t* __restrict__ h16,
@@ -591,9 +591,16 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
 #pragma unroll
         for (int i = 0; i < D::NSI; ++i)
           dma4(Sexp + so[i] + min(q * D::BPS + sp[i], NB - 2), Sst + (i * 4 + wave) * 256);
+        // Activation rows past the pass's last assignment are only ever
+        // multiplied into discarded output rows, so a wave whose rows all lie
+        // there skips its load (the rows keep whatever the stage held). With a
+        // two-stage ring every wait is for all loads in flight, so the skipped
+        // loads do not upset the wait counts; deeper rings load every row.
 #pragma unroll
-        for (int i = 0; i < D::NAI; ++i)
+        for (int i = 0; i < D::NAI; ++i) {
+          if (NS == 2 && (i * 4 + wave) * D::RPI >= nm) continue;
           dma16(act + aoff[i] + min(q * D::KC + apc[i], K - 8), Ast + (i * 4 + wave) * 1024);
+        }
       };
       // One stage: for each of its BPS blocks, the lane group's 8 codes of its
       // two rows become B fragments, each M tile's activation fragment of the
@@ -601,7 +608,12 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
       // block scale. The next block's activation fragments are read while the
       // current block's MFMAs run.
       auto compute = [&](int q, const uint8_t* Bst) {
-        const uint32_t bb = lds_addr(Bst);
+        uint32_t bb = lds_addr(Bst);
+        // One-tile passes are bound by bytes in flight, so by occupancy: the
+        // stage base is hidden from the optimiser, and each LDS address is
+        // formed where it is used instead of being hoisted, for every unrolled
+        // stage, into registers held across the loop.
+        if constexpr (MT == 1) asm("" : "+v"(bb));
         const uint32_t sb = bb + D::B_BYTES;
         const uint32_t ab = sb + D::S_BYTES;
         CodeWords<SCHEME> cw0[D::BPS], cw1[D::BPS];
@@ -761,11 +773,11 @@ static void launch_dma(int ncb, int maxu8, const uint16_t* act, const ExpertsDev
 // gate/up (activations of type AT) then down (fp16 h), with one tuning: M
 // tiles per pass, stages, line bytes per stage. Both take the same passes, so
 // the down GEMM finds the tile exponents of h where gate/up left them.
-template <int SCHEME, int AT, int MT, int NS, int LB>
+template <int SCHEME, int AT, int MT, int NS, int LB, int LBD = LB>
 static void launch_dma_pair(int maxu8, const uint16_t* x, const ExpertsDev& ex, int k, const GroupBufs& g,
                             uint16_t* h16, int32_t* sig, float* out, hipStream_t s) {
   launch_dma<SCHEME, AT, 0, MT, NS, LB>((ex.I + 63) / 64, maxu8, x, ex, k, g, h16, sig, nullptr, s);
-  launch_dma<SCHEME, MOE_F16, 1, MT, NS, LB>((ex.H + 127) / 128, maxu8, h16, ex, k, g, h16, sig, out, s);
+  launch_dma<SCHEME, MOE_F16, 1, MT, NS, LBD>((ex.H + 127) / 128, maxu8, h16, ex, k, g, h16, sig, out, s);
 }
 
 hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev& ex, int k, const GroupBufs& g,
@@ -791,7 +803,7 @@ hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev
         else launch_dma_pair<MOE_Q_SYM8, AT, 1, 2, 128>(maxu8, act, ex, k, g, h16, sig, out, s);
       } else {
         if (avg > 6) launch_dma_pair<MOE_Q_INT4, AT, 4, 2, 64>(maxu8, act, ex, k, g, h16, sig, out, s);
-        else launch_dma_pair<MOE_Q_INT4, AT, 1, 2, 128>(maxu8, act, ex, k, g, h16, sig, out, s);
+        else launch_dma_pair<MOE_Q_INT4, AT, 1, 2, 128, 64>(maxu8, act, ex, k, g, h16, sig, out, s);
       }
       return;
     }
