@@ -69,6 +69,16 @@ struct BlockMfma<MOE_BF16> {
 template <int SCHEME>
 using CodeWords = std::conditional_t<SCHEME == MOE_Q_SYM8, u32x2, uint32_t>;
 
+// (a & b) | c in one instruction: v_bitop3_b32 with truth table 0xEA (the
+// table's bit i is the result for a, b, c = bits 2, 1, 0 of i). Written out
+// because VOP3 takes no literal constants: the compiler splits the pair into
+// an and and an or around a constant it cannot place.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0xea" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // The lane group's 8 codes of one block as exact AT values: sym8 in natural
 // order; int4 as (c0, c4), (c1, c5), (c2, c6), (c3, c7).
 template <int SCHEME, int AT>
@@ -87,14 +97,23 @@ __device__ __forceinline__ typename BlockMfma<AT>::v8 codes8(CodeWords<SCHEME> w
         r[4 * t + 0] = lo[0]; r[4 * t + 1] = lo[1]; r[4 * t + 2] = hi[0]; r[4 * t + 3] = hi[1];
       }
     } else {
-      // nibble c: 1024 + (c + 8) as 0x640n, minus 1032
-      const half2v bias = as_h2(0xE408E408u);
-      const uint32_t u = w ^ 0x88888888u;
+      // n = c + 8 in [0, 15]. A nibble in bits 0-3 of a halfword ORed into
+      // 0x6400 is the fp16 number 1024 + n: minus 1032. A nibble in bits 4-7
+      // is 1024 + 16 n: times 1/16, minus 72 (one packed FMA, exact: every
+      // value is a small integer). One shift by 8 serves the other two pairs.
+      const half2v lo_bias = as_h2(0xE408E408u);  // -1032
+      const half2v hi_mul = as_h2(0x2C002C00u);   // 1/16
+      const half2v hi_bias = as_h2(0xD480D480u);  // -72
+      const uint32_t u = w ^ 0x88888888u, u8 = u >> 8;
+      half2v v[4];
+      v[0] = as_h2(and_or(u, 0x000F000Fu, 0x64006400u)) + lo_bias;
+      v[1] = __builtin_elementwise_fma(as_h2(and_or(u, 0x00F000F0u, 0x64006400u)), hi_mul, hi_bias);
+      v[2] = as_h2(and_or(u8, 0x000F000Fu, 0x64006400u)) + lo_bias;
+      v[3] = __builtin_elementwise_fma(as_h2(and_or(u8, 0x00F000F0u, 0x64006400u)), hi_mul, hi_bias);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const half2v v = as_h2(((u >> (4 * p)) & 0x000F000Fu) | 0x64006400u) + bias;
-        r[2 * p] = v[0];
-        r[2 * p + 1] = v[1];
+        r[2 * p] = v[p][0];
+        r[2 * p + 1] = v[p][1];
       }
     }
   } else {
