@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--no-lora", action="store_true", help="skip the quantized linear with a LoRA delta")
     ap.add_argument("--path", choices=["auto", "gather", "gemm"], default="auto",
                     help="expert path: the library's choice, the gathered matvec or the grouped MFMA GEMM")
+    ap.add_argument("--secondary", default=",".join(SECONDARY),
+                    help="after decode40, these workloads are measured too and reported under 'workloads' "
+                         "(comma-separated, or 'none')")
     return ap.parse_args()
 
 
@@ -85,7 +88,9 @@ def gate_up_bytes(w) -> int:
 def dtype_name(w, gemm: bool) -> str:
     """The arithmetic each stage of the timed path runs in."""
     if gemm:
-        return "f16xf16->f32 (grouped GEMM, mfma); f32 router, combine"
+        xt = "bf16" if w.xtype == 2 else "f16"
+        return (f"gate/up {xt} x raw codes on the matrix cores, f32 per-block scale; h f16 (tile exponent); "
+                f"down f16 x raw codes, f32; f32 router, combine")
     if w.T > 1:
         return "f32 (grouped matvec)"
     gu = "f16xf16->f32 (v_dot2)" if w.xtype == 1 else "f32"
@@ -138,6 +143,54 @@ def miss_policies(w, xs, router, pool, rq, torch) -> dict:
                               "gbps_copied": round(nbytes / (us * 1e-6) / 1e9, 1)}
     del stack
     return out
+
+
+def staged_step(w, xs, nl, pools, routers, ws, K, W, path_flag, rq, torch) -> dict:
+    """The layer on resident stacks behind slot tables (moe_layer_forward_staged):
+    every layer's E experts copied into a stack in a random slot order, so the
+    routing, the bytes and the outputs are the pool layer's and the difference
+    is the slot-table lookup. Timed as one HIP graph of the nl layers."""
+    stacks, tables = [], []
+    for l in range(nl):
+        st = rq.empty_stack(pools[l], w.E)
+        experts = torch.arange(w.E, dtype=torch.int32, device="cuda")
+        slots = torch.randperm(w.E, device="cuda").to(torch.int32)
+        rq.moe_stage_experts(pools[l], st, experts, slots)
+        slot_of = torch.empty(w.E, dtype=torch.int32, device="cuda")
+        slot_of[experts.long()] = slots
+        stacks.append(st)
+        tables.append(slot_of)
+    xbuf = torch.empty_like(xs[0])
+    ys = [torch.empty((w.T, w.H), dtype=torch.float32, device="cuda") for _ in range(nl)]
+    nx = xs.shape[0]
+
+    def run():
+        for l in range(nl):
+            rq.moe_layer_forward_staged(xbuf, routers[l], stacks[l], tables[l], w.k, rq.MOE_FLAG_RENORM | path_flag,
+                                        ws=ws, out=ys[l], return_routing=False)
+
+    xbuf.copy_(xs[0])
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for s in range(W):
+        xbuf.copy_(xs[s % nx])
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(K):
+        xbuf.copy_(xs[(W + s) % nx])
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (K * nl)
+    del g, stacks, tables
+    torch.cuda.empty_cache()
+    return {"us_per_layer": round(us, 3), "slots": w.E, "layers": nl, "steps": K}
 
 
 def prerouted_step(w, xs, nl, pools, routers, ws, seed, K, W, path_flag, rq, synth, torch) -> dict:
@@ -392,10 +445,11 @@ def to_dev(x, xtype, torch):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def cpu_baseline(w, seed, seconds):
+def cpu_baseline(w, seed, seconds, threads=None):
     """The oracle, timed on this host on a bounded sample: one token per layer
     for successive layers of the same workload (router + gathered experts).
-    Expert draws and quantisation happen before the clock starts."""
+    Expert draws and quantisation happen before the clock starts. `threads`
+    sets the oracle's OpenMP threads for this measurement (None: all)."""
     import numpy as np
     import oracle
     import synth
@@ -409,45 +463,138 @@ def cpu_baseline(w, seed, seconds):
         used = np.unique(idx)
         wgu, wd = synth.draw_experts(seed, w.wid, l, used, w.H, w.I, w.weight_std)
         samples.append((x, li.R, oracle.quantize_experts(wgu, wd, w.scheme), {int(e): i for i, e in enumerate(used)}))
-    t0 = time.perf_counter()
-    n_tok = 0
-    n_layers = 0
-    while True:
-        for x, R, ex, m in samples:
-            idx, gate = oracle.route(x, R, w.k, bf16=w.xtype == synth.BF16)
-            cidx = np.vectorize(lambda e: m[int(e)])(idx).astype(np.int32)
-            oracle.gather_forward(x, ex, cidx, gate, bf16=w.xtype == synth.BF16)
-            n_tok += x.shape[0]
-            n_layers += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": n_tok / dt, "unit": "tokens/s (per layer)", "cores": oracle.num_threads(), "kind": "oracle",
+    all_threads = oracle.num_threads()
+    if threads is not None:
+        oracle.set_num_threads(threads)
+    try:
+        used_threads = oracle.num_threads()
+        t0 = time.perf_counter()
+        n_tok = 0
+        n_layers = 0
+        while True:
+            for x, R, ex, m in samples:
+                idx, gate = oracle.route(x, R, w.k, bf16=w.xtype == synth.BF16)
+                cidx = np.vectorize(lambda e: m[int(e)])(idx).astype(np.int32)
+                oracle.gather_forward(x, ex, cidx, gate, bf16=w.xtype == synth.BF16)
+                n_tok += x.shape[0]
+                n_layers += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(all_threads)
+    return {"value": n_tok / dt, "unit": "tokens/s (per layer)", "cores": used_threads, "kind": "oracle",
             "sample": f"{len(samples)} layers x {t_sample} token(s) of {w.name}, {n_layers} layer calls in {dt:.1f} s "
                       f"(fp64 oracle: router + gathered experts; weight draws and quantisation untimed)"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the layer is built and measured on a single MI355X "
-              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
-        sys.exit(2)
+def host_info() -> dict:
+    """The host the CPU baseline ran on: logical CPUs, the ones this process may
+    use, and the CPU model."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
+def dense_over_read(w, seed, seconds) -> dict:
+    """The oracle's gathered forward (only the k routed experts) against its dense
+    form (all E experts evaluated, non-routed gates zero) on one token of one
+    layer: the host-side cost of reading every expert instead of the routed
+    ones. Codes are random bytes and scales a constant: the timing does not
+    depend on the values, and drawing and quantising every expert of a large
+    layer would take longer than the measurement."""
     import numpy as np
-    import torch
-
-    import routed_expert_quantized_amd as rq
+    import oracle
     import synth
+    g = np.random.default_rng(seed)
+    cb = 1 if w.scheme == synth.SYM8 else 2
+    E, H, I = w.E, w.H, w.I
+    ex = oracle.Experts(E, H, I, w.scheme, g.integers(0, 256, (E, 2 * I, H // cb), dtype=np.uint8),
+                        np.full((E, 2 * I, H // 32), 0x2000, dtype=np.uint16),
+                        g.integers(0, 256, (E, H, I // cb), dtype=np.uint8),
+                        np.full((E, H, I // 32), 0x2000, dtype=np.uint16))
+    li = synth.draw_layer(w, seed=seed, layer=0, T=1, with_experts=False)
+    x = np.ascontiguousarray(synth.draw_step_x(w, seed, 0)[:1])
+    bf16 = w.xtype == synth.BF16
+    idx, gate = oracle.route(x, li.R, w.k, bf16=bf16)
+    gfull = np.zeros((1, E), dtype=np.float32)
+    gfull[0, idx[0]] = gate[0]
 
-    w = synth.WORKLOADS[args.workload]
-    if args.k is not None:
-        w = dataclasses.replace(w, k=args.k)
-    K = args.steps if args.steps is not None else (512 if w.T == 1 else 64)
-    W = args.warmup if args.warmup is not None else 32
+    def rate(fn):
+        fn()
+        t0, n = time.perf_counter(), 0
+        while True:
+            fn()
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        return (time.perf_counter() - t0) / n
+
+    t_gather = rate(lambda: oracle.gather_forward(x, ex, idx, gate, bf16=bf16))
+    t_dense = rate(lambda: oracle.dense_forward(x, ex, gfull, bf16=bf16))
+    return {"E": E, "k": w.k, "gathered_ms_per_token": round(t_gather * 1e3, 3),
+            "dense_ms_per_token": round(t_dense * 1e3, 3), "dense_over_gathered": round(t_dense / t_gather, 2),
+            "E_over_k": round(E / w.k, 2)}
+
+
+def trace_kernel_us(wname: str, sha: str) -> dict | None:
+    """Average kernel durations from the committed rocprofv3 kernel trace of this
+    workload (profiles/kernel_trace_<workload>.md), when it was taken on the
+    current kernel sources (its "kernel source sha" line matches). The table
+    lists kernels by total time, so of several instantiations of one kernel
+    (the staged top-k, other tunings of the GEMM) the workload's main one comes
+    first and is the one taken."""
+    p = os.path.join(ROOT, "profiles", f"kernel_trace_{wname}.md")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        text = f.read()
+    if f"kernel source sha: {sha}" not in text:
+        return None
+    out = {}
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.split("|")]
+        if len(cells) < 6 or not cells[1].startswith("`"):
+            continue
+        name = cells[1].strip("`")
+        try:
+            avg = float(cells[3])
+        except ValueError:
+            continue
+        for key, pat in (("route_logits", "k_logits_"), ("topk", "k_topk<"), ("group", "k_group_"),
+                         ("combine", "k_combine<"), ("gate_up", "k_gate_up_t1<"), ("down", "k_down_t1_slots<"),
+                         ("down", "k_down_t1<")):
+            if pat in name:
+                out.setdefault(key, avg)
+        if "k_gemm_dma<" in name or "k_gemm_grouped<" in name:
+            targs = name[name.index("<") + 1:].split(",")
+            mode = targs[2].strip() if len(targs) > 2 else ""
+            out.setdefault("gemm_gate_up" if mode == "0" else "gemm_down", avg)
+    return out or None
+
+
+SECONDARY = ("batched_int4", "large_int4", "prefill", "prefill8k")
+
+
+def run_workload(w, args, K, W, rq, synth, torch, headline: bool) -> dict:
+    """Builds the workload's layers in HBM, times K steps (HIP graphs), then the
+    dominant kernel's launches with events, the streaming-read reference and, for
+    the headline, the rows beyond the layer. Frees its buffers before returning."""
+    import numpy as np
     multi = w.layers > 1
     nl = w.layers if multi else args.copies
     log(f"workload {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} scheme={w.scheme} layers={nl}")
-    rq.lib()
     t_setup = time.perf_counter()
     pools, routers = build_layers(w, nl, args.seed, rq, synth, torch)
     nx = w.steps if w.steps > 1 else 8
@@ -456,12 +603,14 @@ def main():
     ys = [torch.empty((w.T, w.H), dtype=torch.float32, device="cuda") for _ in range(nl)]
     ws = rq.Workspace()
     ws.get(rq.moe_workspace_bytes(w.T, w.E, w.H, w.I, w.k, w.scheme))
-    log(f"setup {time.perf_counter() - t_setup:.1f} s, pool {sum(p.w_gate_up.numel() + p.w_down.numel() for p in pools) / 1e9:.1f} GB codes")
+    log(f"setup {time.perf_counter() - t_setup:.1f} s, pool "
+        f"{sum(p.w_gate_up.numel() + p.w_down.numel() for p in pools) / 1e9:.1f} GB codes")
 
     layers_per_step = nl if multi else 1
     path_flag = {"auto": 0, "gather": rq.MOE_FLAG_PATH_GATHER, "gemm": rq.MOE_FLAG_PATH_GEMM}[args.path]
-    # the library's own choice (kept in step with moe_api.cpp): the GEMM path for T > 1
-    gemm = args.path == "gemm" or (args.path == "auto" and w.T > 1)
+    # the library's own choice (kept in step with moe_api.cpp): the GEMM path for
+    # T > 1 with 16-bit activations
+    gemm = args.path == "gemm" or (args.path == "auto" and w.T > 1 and w.xtype != synth.F32)
 
     def run_layers(step):
         ls = range(nl) if multi else [step % nl]
@@ -566,16 +715,22 @@ def main():
     mfma_tflops = gu_flops / (gu_us * 1e-6) / 1e12
 
     ceiling = stream_ceiling(int(round(routed_bytes)), rq, torch)
-    miss = miss_policies(w, [xs[i] for i in range(nx)], routers[0], pools[0], rq, torch) if w.T <= 64 else None
-    pre = None
-    if w.T <= 64 and not args.no_prerouter:
-        log("prerouted step ...")
-        pre = prerouted_step(w, xs, nl, pools, routers, ws, args.seed, K, W, path_flag, rq, synth, torch)
-        pre["routed_us_per_layer"] = round(t_layer_s * 1e6, 3)
-    lora = None
-    if w.T <= 64 and not args.no_lora:
-        log("quantized linear with LoRA ...")
-        lora = lora_linear(w, args.seed, rq, synth, torch)
+    extras = {}
+    if headline and w.T <= 64:
+        extras["miss_policies"] = miss_policies(w, [xs[i] for i in range(nx)], routers[0], pools[0], rq, torch)
+        if w.T == 1:
+            log("staged layer ...")
+            st = staged_step(w, xs, nl, pools, routers, ws, K, W, path_flag, rq, torch)
+            st["routed_us_per_layer"] = round(t_layer_s * 1e6, 3)
+            extras["staged"] = st
+        if not args.no_prerouter:
+            log("prerouted step ...")
+            pre = prerouted_step(w, xs, nl, pools, routers, ws, args.seed, K, W, path_flag, rq, synth, torch)
+            pre["routed_us_per_layer"] = round(t_layer_s * 1e6, 3)
+            extras["prerouted"] = pre
+        if not args.no_lora:
+            log("quantized linear with LoRA ...")
+            extras["lora_linear"] = lora_linear(w, args.seed, rq, synth, torch)
 
     traffic = None
     tf = os.path.join(ROOT, "profiles", f"traffic_{dom}_{w.name}.json")
@@ -585,25 +740,18 @@ def main():
             tj = json.load(f)
         if tj.get("kernel_source_sha") == sha:
             traffic = tj.get("bytes_per_launch")
+    trace = trace_kernel_us(w.name, sha)
 
-    result = {
-        "metric": METRIC,
-        "value": round(tokens_per_s_layer, 1),
-        "unit": "tokens/s per MoE layer",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(elapsed_ms / K, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dtype_name(w, gemm),
-        "data": "synthetic",
+    res = {
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k, "I": w.I,
                    "codec": "sym8" if w.scheme == 0 else "int4",
                    "x": {0: "f32", 1: "f16", 2: "bf16"}[w.xtype], "layers_per_step": layers_per_step,
                    "layer_copies": nl, "fresh_x": nx, "graph": not args.no_graph,
                    "path": "gemm" if gemm else "gather"},
+        "dtype": dtype_name(w, gemm),
+        "steps": K, "warmup": W,
+        "ms_per_step": round(elapsed_ms / K, 5),
+        "tokens_per_s_per_layer": round(tokens_per_s_layer, 1),
         "us_per_layer": round(t_layer_s * 1e6, 3),
         "step_tokens_per_s": round(w.T / (elapsed_ms * 1e-3 / K), 1),
         "routed_bytes_per_layer": int(routed_bytes),
@@ -611,18 +759,69 @@ def main():
         "routed_hbm_gbps": round(routed_gbps, 1),
         "routed_hbm_frac": round(routed_gbps / HBM_PEAK_GBPS, 4),
         "stream_read_ceiling": {**ceiling, "layer_vs_ceiling": round(routed_gbps / ceiling["gbps"], 4)},
-        **({"miss_policies": miss} if miss else {}),
-        **({"prerouted": pre} if pre else {}),
-        **({"lora_linear": lora} if lora else {}),
+        **extras,
         "kernel_us": {n: round(v, 3) for n, v in kern_us.items()},
+        "kernel_trace_us": trace,
         "roofline": {"kernel": kname, "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(gu_alg), "avg_launch_us": round(gu_us, 3),
-                     **({"mfma_tflops": round(mfma_tflops, 1), "mfma_peak_tflops_f16": 2500.0,
+                     **({"avg_launch_us_trace": round(trace[dom], 3)} if trace and dom in trace else {}),
+                     **({"mfma_tflops": round(mfma_tflops, 1), "mfma_peak_tflops": 2500.0,
                          "mfma_frac": round(mfma_tflops / 2500.0, 4)} if gemm else {})},
         "kernel_source_sha": sha,
     }
+    del graphs, pools, routers, xs, ys, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the layer is built and measured on a single MI355X "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import routed_expert_quantized_amd as rq
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if args.k is not None:
+        w = dataclasses.replace(w, k=args.k)
+    K = args.steps if args.steps is not None else (512 if w.T == 1 else 64)
+    W = args.warmup if args.warmup is not None else 32
+    rq.lib()
+    head = run_workload(w, args, K, W, rq, synth, torch, headline=True)
+    secondary = {}
+    names = [] if args.secondary == "none" or args.workload != "decode40" or args.k is not None else \
+        [n for n in args.secondary.split(",") if n]
+    for name in names:
+        sw = synth.WORKLOADS[name]
+        # the same step count as the headline, at most 64 (a step is one layer call
+        # for single-layer workloads, 60 layer calls at large_int4)
+        secondary[name] = run_workload(sw, args, min(K, 64), min(W, 16), rq, synth, torch, headline=False)
+
+    result = {
+        "metric": METRIC,
+        "value": head["tokens_per_s_per_layer"],
+        "unit": "tokens/s per MoE layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": head["config"],
+        **{k: v for k, v in head.items() if k not in ("config", "dtype", "steps", "warmup", "ms_per_step")},
+    }
+    if secondary:
+        result["workloads"] = secondary
     if args.calib_copy_mib:
         # a plain elementwise copy of known size (negation: a kernel nothing else
         # here launches): its FETCH_SIZE / WRITE_SIZE per dispatch give the factor
@@ -636,7 +835,16 @@ def main():
         result["calib_copy_bytes"] = n * 4
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds)
+        cb = cpu_baseline(w, args.seed, args.cpu_seconds)
+        cb["host"] = host_info()
+        one = cpu_baseline(w, args.seed, args.cpu_seconds / 3, threads=1)
+        cb["one_thread"] = {"value": one["value"], "cores": one["cores"], "sample": one["sample"]}
+        if args.workload == "decode40" and args.k is None:
+            cb["dense_all_experts"] = {n: dense_over_read(synth.WORKLOADS[n], args.seed, 1.0)
+                                       for n in ("tiny", "decode40")}
+        result["cpu_baseline"] = cb
+        for name, r in secondary.items():
+            r["cpu_baseline"] = cpu_baseline(synth.WORKLOADS[name], args.seed, args.cpu_seconds / 3)
     print(json.dumps(result), flush=True)
 
 

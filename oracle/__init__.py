@@ -87,6 +87,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "oref_dense_forward": ([P, I32, I32, ctypes.POINTER(_Experts), P, P], ctypes.c_int),
         "oref_set_plant": ([I32], None),
         "oref_num_threads": ([], I32),
+        "oref_set_num_threads": ([I32], None),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -344,3 +345,7 @@ class planted:
 
 def num_threads() -> int:
     return int(lib().oref_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().oref_set_num_threads(int(n))

@@ -40,6 +40,14 @@ int32_t oref_num_threads(void) {
 #endif
 }
 
+void oref_set_num_threads(int32_t n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ---------------- number formats (IEEE 754-2008 binary16, bfloat16) ---------------- */
 
 /* fp32 -> binary16, round to nearest, ties to even. Finite values at or above

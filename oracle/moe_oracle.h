@@ -155,6 +155,9 @@ void oref_set_plant(int32_t mistake);
 
 /* Number of OpenMP threads the oracle's loops use (1 when built without OpenMP). */
 int32_t oref_num_threads(void);
+/* Sets that number (n > 0; ignored without OpenMP). Results do not depend on
+ * it: the loops split independent outputs only. */
+void oref_set_num_threads(int32_t n);
 
 #ifdef __cplusplus
 }

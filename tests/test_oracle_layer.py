@@ -108,6 +108,26 @@ def test_dense_with_zeroed_gates_equals_gathered():
     assert rel_norm_err(yd, y) < 1e-6
 
 
+def test_result_does_not_depend_on_the_thread_count():
+    """The oracle's loops split independent outputs only, so one thread and all
+    threads give the same bits (the bench times it both ways)."""
+    E, H, I, T, k = 8, 128, 64, 16, 3
+    ex = _random_experts(E, H, I, oracle.INT4, 5)
+    g = np.random.default_rng(6)
+    x = g.standard_normal((T, H)).astype(np.float32)
+    R = (g.standard_normal((E, H)) * 0.3).astype(np.float32)
+    n = oracle.num_threads()
+    try:
+        oracle.set_num_threads(1)
+        assert oracle.num_threads() == 1
+        y1, i1, g1 = oracle.layer_forward(x, R, ex, k)
+    finally:
+        oracle.set_num_threads(n)
+    assert oracle.num_threads() == n
+    yn, i_n, gn = oracle.layer_forward(x, R, ex, k)
+    assert np.array_equal(i1, i_n) and np.array_equal(g1, gn) and np.array_equal(y1, yn)
+
+
 def test_identical_experts_give_the_single_expert_ffn():
     E, H, I, T = 6, 64, 32, 5
     one = _random_experts(1, H, I, oracle.INT4, 5)
