@@ -517,7 +517,9 @@ __global__ __launch_bounds__(256) void k_down_grouped(ExpertsDev ex, int k, cons
 // per-slot rows in fp32 (ys) or, with HALF, fp16 (ys16: the grouped GEMM's).
 // Four consecutive outputs of one token per thread; every slot's loads are
 // issued before the fused multiply-adds, which run in slot order (KMAX >= k).
-template <int KMAX, bool HALF>
+// With NT the fp32 rows are read non-temporally (rows larger than the cache
+// that would hold them).
+template <int KMAX, bool HALF, bool NT>
 __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const float* __restrict__ gate,
                                                  const float* __restrict__ ys, const uint16_t* __restrict__ ys16,
                                                  float* __restrict__ y) {
@@ -535,6 +537,10 @@ __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const floa
       const uint2 u = *reinterpret_cast<const uint2*>(ys16 + off);
       const half2v lo = as_h2(u.x), hi = as_h2(u.y);
       v[s] = make_float4((float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]);
+    } else if constexpr (NT) {
+      typedef float f4v __attribute__((ext_vector_type(4)));
+      const f4v q = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(ys + off));
+      v[s] = make_float4(q[0], q[1], q[2], q[3]);
     } else {
       v[s] = *reinterpret_cast<const float4*>(ys + off);
     }
@@ -793,17 +799,23 @@ hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsD
 hipError_t launch_combine(int T, int H, int k, const float* gate, const float* ys, const uint16_t* ys16, float* y,
                           hipStream_t s) {
   const dim3 cg((unsigned)((int64_t)T * ((H / 4 + 255) / 256)));
-  auto go = [&](auto KM, auto HF) {
+  auto go = [&](auto KM, auto HF, auto NTc) {
     constexpr int K_ = decltype(KM)::value;
-    constexpr bool H_ = decltype(HF)::value != 0;
-    MOE_LAUNCH(MOE_KERNEL_COMBINE, (k_combine<K_, H_>), cg, dim3(256), 0, s, T, H, k, gate, ys, ys16, y);
+    constexpr bool H_ = decltype(HF)::value != 0, N_ = decltype(NTc)::value != 0;
+    MOE_LAUNCH(MOE_KERNEL_COMBINE, (k_combine<K_, H_, N_>), cg, dim3(256), 0, s, T, H, k, gate, ys, ys16, y);
   };
+  // Per-slot rows beyond the 256 MB last-level cache are read non-temporally:
+  // measured faster there (8192 tokens, 537 MB) and slower below (2048, 134 MB).
+  const bool nt = (int64_t)T * k * H * 4 > ((int64_t)256 << 20);
   if (ys16) {
-    if (k <= 8) go(IC<8>{}, IC<1>{});
-    else go(IC<16>{}, IC<1>{});
+    if (k <= 8) go(IC<8>{}, IC<1>{}, IC<0>{});
+    else go(IC<16>{}, IC<1>{}, IC<0>{});
+  } else if (nt) {
+    if (k <= 8) go(IC<8>{}, IC<0>{}, IC<1>{});
+    else go(IC<16>{}, IC<0>{}, IC<1>{});
   } else {
-    if (k <= 8) go(IC<8>{}, IC<0>{});
-    else go(IC<16>{}, IC<0>{});
+    if (k <= 8) go(IC<8>{}, IC<0>{}, IC<0>{});
+    else go(IC<16>{}, IC<0>{}, IC<0>{});
   }
   return hipGetLastError();
 }

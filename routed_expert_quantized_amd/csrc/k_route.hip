@@ -3,6 +3,7 @@
 // [LR] "QwenのMoEルーターを観測してホットエキスパートを先読みしても速くならなかった" (lilting.ch),
 //      section "ルーターをフックする": the router is a gate linear, a softmax and a top-k.
 #include <type_traits>
+#include <utility>
 
 #include "kernels.hpp"
 
@@ -167,39 +168,66 @@ __device__ __forceinline__ int block_exclusive_scan_1024(int v, int* smem, int& 
   return excl;
 }
 
+// Per expert e: counts[e], offsets[e] (exclusive scan of the counts), and
+// base[c][e] = offsets[e] + the assignments of e in chunks before c. The
+// 1024 threads split each expert's C chunks into P = 1024 / E parts (one
+// thread per expert and part): each part counts its chunks, the parts' counts
+// give every part its starting position, and each part then writes its
+// chunks' bases, reading the masks again (batched) instead of updating the
+// bases in place.
 __global__ __launch_bounds__(1024) void k_group_scan(const uint64_t* __restrict__ mask, int C, int E,
                                                      int32_t* __restrict__ base, int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ uniq,
                                                      int32_t* __restrict__ n_uniq) {
   __shared__ int smem[64];
-  const int e = threadIdx.x;
-  int cnt = 0;
-  if (e < E) {
-    // masks of 8 chunks requested together, then counted in chunk order
-    for (int c0 = 0; c0 < C; c0 += 8) {
+  __shared__ int part_cnt[1024];
+  __shared__ int start[1024];
+  const int P = 1024 / E;  // E <= 1024
+  const int e = (int)threadIdx.x % E, p = (int)threadIdx.x / E;
+  const bool active = p < P;
+  const int c_lo = active ? (int)((int64_t)p * C / P) : 0, c_hi = active ? (int)((int64_t)(p + 1) * C / P) : 0;
+  // masks of 8 chunks requested together
+  auto for_chunks = [&](auto&& f) {
+    for (int c0 = c_lo; c0 < c_hi; c0 += 8) {
       uint64_t mk[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mk[j] = c0 + j < C ? mask[(int64_t)(c0 + j) * E + e] : 0ull;
+      for (int j = 0; j < 8; ++j) mk[j] = c0 + j < c_hi ? mask[(int64_t)(c0 + j) * E + e] : 0ull;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (c0 + j < C) {
-          base[(int64_t)(c0 + j) * E + e] = cnt;
-          cnt += __popcll(mk[j]);
-        }
+        if (c0 + j < c_hi) f(c0 + j, __popcll(mk[j]));
     }
-    counts[e] = cnt;
-  }
+  };
+  int mine = 0;
+  for_chunks([&](int, int n) { mine += n; });
+  part_cnt[threadIdx.x] = mine;
+  __syncthreads();
+  int cnt = 0;  // the expert's count, on its part-0 thread
+  if (p == 0)
+    for (int q = 0; q < P; ++q) cnt += part_cnt[q * E + e];
   int total;
-  const int off = block_exclusive_scan_1024(cnt, smem, total);
-  if (e < E) {
+  const int off = block_exclusive_scan_1024(p == 0 ? cnt : 0, smem, total);
+  if (p == 0) {
+    counts[e] = cnt;
     offsets[e] = off;
-    for (int c = 0; c < C; ++c) base[(int64_t)c * E + e] += off;
+    int run = off;  // each part's first position
+    for (int q = 0; q < P; ++q) {
+      start[q * E + e] = run;
+      run += part_cnt[q * E + e];
+    }
   }
-  if (e == 0) offsets[E] = total;
+  if (threadIdx.x == 0) offsets[E] = total;
+  __syncthreads();
+  if (active) {
+    int run = start[threadIdx.x];
+    for_chunks([&](int c, int n) {
+      base[(int64_t)c * E + e] = run;
+      run += n;
+    });
+  }
   int nu;
-  const int pos = block_exclusive_scan_1024(cnt > 0 ? 1 : 0, smem, nu);
-  if (e < E && cnt > 0) uniq[pos] = e;
-  if (e == 0) *n_uniq = nu;
+  const int pos = block_exclusive_scan_1024(p == 0 && cnt > 0 ? 1 : 0, smem, nu);
+  if (p == 0 && cnt > 0) uniq[pos] = e;
+  if (threadIdx.x == 0) *n_uniq = nu;
 }
 
 __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict__ idx, int T, int k, int E,
@@ -410,10 +438,27 @@ __global__ __launch_bounds__(256) void k_split_router(const float* __restrict__ 
 
 typedef __bf16 bf16x8_r __attribute__((ext_vector_type(8)));
 
+template <typename F, int... Is>
+__device__ __forceinline__ void router_static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+// f(0), ..., f(N-1) with compile-time indices
+template <int N, typename F>
+__device__ __forceinline__ void router_static_for(F&& f) {
+  router_static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Token tiles (of 16) of the split-weight router kernel for large batches.
+constexpr int kSplitTallM = 8;
+
+// K steps of operands in flight per wave in k_logits_bf16x3: step i's MFMAs
+// run while the loads of steps i+1 .. i+kRouterDepth-1 are outstanding.
+constexpr int kRouterDepth = 3;
+
 template <int MTT, int NTT>
-__global__ __launch_bounds__(1024) void k_logits_bf16x3(const uint16_t* __restrict__ x, int T, int H,
-                                                        const uint16_t* __restrict__ r3, int E,
-                                                        float* __restrict__ logits, int kw) {
+__global__ __launch_bounds__(256) void k_logits_bf16x3(const uint16_t* __restrict__ x, int T, int H,
+                                                       const uint16_t* __restrict__ r3, int E,
+                                                       float* __restrict__ logits, int kw) {
   extern __shared__ float red[];  // [waves][MTT*NTT*4][64]
   logits += (int64_t)blockIdx.z * T * E;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -431,23 +476,42 @@ __global__ __launch_bounds__(1024) void k_logits_bf16x3(const uint16_t* __restri
 #pragma unroll
     for (int nt = 0; nt < NTT; ++nt) acc[mt][nt] = float4v_r{0.f, 0.f, 0.f, 0.f};
   const int kb = (blockIdx.z * nw + w) * kw;
-#pragma unroll 2
-  for (int k = kb; k < kb + kw; k += 32) {
-    bf16x8_r a[MTT], b[3][NTT];
+  const int nsteps = kw / 32;
+  // A ring of kRouterDepth register buffers, each one K step's fragments: the
+  // loop is unrolled by the ring size so that every buffer index is a constant.
+  bf16x8_r a[kRouterDepth][MTT], b[kRouterDepth][3][NTT];
+  auto load = [&](auto S, int step) {
+    constexpr int sl = decltype(S)::value;
+    const int k = kb + 32 * step + 8 * g;
 #pragma unroll
-    for (int mt = 0; mt < MTT; ++mt) a[mt] = *reinterpret_cast<const bf16x8_r*>(x + xrow[mt] + k + 8 * g);
+    for (int mt = 0; mt < MTT; ++mt) a[sl][mt] = *reinterpret_cast<const bf16x8_r*>(x + xrow[mt] + k);
 #pragma unroll
     for (int p = 0; p < 3; ++p)
 #pragma unroll
       for (int nt = 0; nt < NTT; ++nt)
-        b[p][nt] = *reinterpret_cast<const bf16x8_r*>(r3 + p * plane + rrow[nt] + k + 8 * g);
+        b[sl][p][nt] = *reinterpret_cast<const bf16x8_r*>(r3 + p * plane + rrow[nt] + k);
+  };
+  auto mma = [&](auto S) {
+    constexpr int sl = decltype(S)::value;
 #pragma unroll
     for (int mt = 0; mt < MTT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NTT; ++nt)
 #pragma unroll
         for (int p = 0; p < 3; ++p)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b[p][nt], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sl][mt], b[sl][p][nt], acc[mt][nt], 0, 0, 0);
+  };
+  router_static_for<kRouterDepth>([&](auto S) {
+    if ((int)decltype(S)::value < nsteps) load(S, decltype(S)::value);
+  });
+  for (int i0 = 0; i0 < nsteps; i0 += kRouterDepth) {
+    router_static_for<kRouterDepth>([&](auto S) {
+      const int i = i0 + (int)decltype(S)::value;
+      if (i < nsteps) {
+        mma(S);
+        if (i + kRouterDepth < nsteps) load(S, i + kRouterDepth);
+      }
+    });
   }
   constexpr int NO = MTT * NTT * 4 * 64;
   auto store = [&](int o, float v) {
@@ -491,8 +555,14 @@ hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R,
     const bool split3 = xtype == MOE_BF16 && r3 != nullptr && T >= kSplitRouterMinT;
     const int kstep = split3 ? 32 : 16;
     // tile shape and split-K: aim for about two waves per SIMD (2048 waves)
-    const int mtt = T >= 32 && (int64_t)((T + 31) / 32) * ((E + 31) / 32) >= 128 ? 2 : 1;
-    const int ntt = E >= 32 && (int64_t)((T + 16 * mtt - 1) / (16 * mtt)) * ((E + 31) / 32) >= 128 ? 2 : 1;
+    int mtt = T >= 32 && (int64_t)((T + 31) / 32) * ((E + 31) / 32) >= 128 ? 2 : 1;
+    int ntt = E >= 32 && (int64_t)((T + 16 * mtt - 1) / (16 * mtt)) * ((E + 31) / 32) >= 128 ? 2 : 1;
+    // The split-weight kernel is bound by what its tiles fetch from L2: each
+    // expert row is three planes, each token row one. Taller token tiles fetch
+    // each plane row for more tokens (mtt and ntt always name the launched
+    // kernel's tile: the grid and the reduction's LDS follow them).
+    if (split3 && ntt == 2 && (int64_t)((T + 16 * kSplitTallM - 1) / (16 * kSplitTallM)) * ((E + 31) / 32) >= 128)
+      mtt = kSplitTallM;
     dim3 grid((T + 16 * mtt - 1) / (16 * mtt), (E + 16 * ntt - 1) / (16 * ntt));
     const int64_t tiles = (int64_t)grid.x * grid.y;
     // waves per workgroup (up to 4), then K splits across workgroups, while the
@@ -522,6 +592,11 @@ hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R,
                    logits, kw, ldr);
     };
     auto with_tile = [&](auto XC) {
+      if (mtt == kSplitTallM) {
+        MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_bf16x3<kSplitTallM, 2>), grid, dim3(64 * nw), lds, s,
+                   static_cast<const uint16_t*>(x), T, H, static_cast<const uint16_t*>(r3), E, logits, kw);
+        return;
+      }
       if (mtt == 2 && ntt == 2) go(XC, std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
       else if (ntt == 2) go(XC, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
       else if (mtt == 2) go(XC, std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});

@@ -100,8 +100,9 @@ def test_route_exact_ties_go_to_lower_ids(E, k):
 # ---------------------------------------------------------------- grouping
 @pytest.mark.parametrize("T,k,E", [(1, 8, 256), (63, 10, 512), (64, 10, 512), (65, 3, 8), (16, 10, 512),
                                    (2048, 8, 256), (300, 16, 1024), (5, 4, 4),
-                                   # chunk masks beyond the one-workgroup form's LDS: three kernels
-                                   (2048, 4, 1024), (520, 2, 1024)])
+                                   # chunk masks beyond the one-workgroup form's LDS: three kernels,
+                                   # the scan splitting each expert's chunks over 1, 4, 3 (unevenly) and 2 threads
+                                   (2048, 4, 1024), (520, 2, 1024), (8192, 8, 256), (2000, 3, 300), (1100, 5, 512)])
 def test_group_bit_exact(T, k, E):
     g = np.random.default_rng(T * 31 + k)
     idx = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
