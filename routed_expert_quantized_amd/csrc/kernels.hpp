@@ -27,7 +27,7 @@ constexpr int kMaxK = 16;
 constexpr int kMfmaLogitsMinT = 16;  // from this many tokens the router logits run on the matrix cores
 constexpr int kMaxLogitSplits = 8;   // split-K partial planes of the batch router, at most
 constexpr int kSplitRouterMinT = 128;  // from this many bf16 tokens the router runs on bf16 MFMA (split weights)
-constexpr int kGroupLdsCells = 8192; // chunk x expert cells of the one-workgroup grouping (96 KiB of LDS)
+constexpr int kGroupLdsCells = 4096; // chunk x expert cells of the one-workgroup grouping (48 KiB of LDS); above, three kernels (measured faster from 8192 cells)
 
 
 // Device buffers of the token-by-expert grouping.
