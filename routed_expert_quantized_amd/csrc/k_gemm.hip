@@ -711,8 +711,10 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
       };
 
       // Every iteration issues one stage and waits for the oldest one, so all
-      // waits are the same constant; past the last chunk a stage is refilled with
-      // the last chunk again (clamped, cache-resident) and never read.
+      // waits are the same constant; past the last chunk a deeper ring refills a
+      // stage with the last chunk again (clamped, cache-resident, never read) to
+      // keep that count. A two-stage ring waits for everything in flight, so it
+      // issues nothing past the last chunk.
       static_for<NS - 1>([&](auto R) { issue(min((int)decltype(R)::value, nchunks - 1), stage(R)); });
       // chunk q lives in stage q % NS; the loop is unrolled NS times so that every
       // stage index is a constant
@@ -723,7 +725,7 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
           if (q < nchunks) {
             wait_vmcnt<(NS - 2) * D::NI>();
             raw_barrier();  // chunk q is in LDS for every wave; chunk q-1's stage is free
-            issue(min(q + NS - 1, nchunks - 1), stage(ICg<(r + NS - 1) % NS>{}));
+            if (NS > 2 || q + 1 < nchunks) issue(min(q + NS - 1, nchunks - 1), stage(ICg<(r + NS - 1) % NS>{}));
             compute(q, stage(R));  // ends with its LDS reads complete
           }
         });
