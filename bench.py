@@ -145,6 +145,41 @@ def miss_policies(w, xs, router, pool, rq, torch) -> dict:
     return out
 
 
+def flag_step(w, xs, nl, pools, routers, ws, K, W, flags, rq, torch) -> dict:
+    """The headline's layers with other flags (the single-token path with fp32
+    h): the same pools, routers and inputs, one HIP graph of the nl layers."""
+    xbuf = torch.empty_like(xs[0])
+    ys = [torch.empty((w.T, w.H), dtype=torch.float32, device="cuda") for _ in range(nl)]
+    nx = xs.shape[0]
+
+    def run():
+        for l in range(nl):
+            rq.moe_layer_forward(xbuf, routers[l], pools[l], w.k, rq.MOE_FLAG_RENORM | flags, ws=ws, out=ys[l],
+                                 return_routing=False)
+
+    xbuf.copy_(xs[0])
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for s in range(W):
+        xbuf.copy_(xs[s % nx])
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(K):
+        xbuf.copy_(xs[(W + s) % nx])
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (K * nl)
+    del g
+    return {"us_per_layer": round(us, 3), "flags": int(flags), "layers": nl, "steps": K}
+
+
 def staged_step(w, xs, nl, pools, routers, ws, K, W, path_flag, rq, torch) -> dict:
     """The layer on resident stacks behind slot tables (moe_layer_forward_staged):
     every layer's E experts copied into a stack in a random slot order, so the
@@ -719,6 +754,9 @@ def run_workload(w, args, K, W, rq, synth, torch, headline: bool) -> dict:
     if headline and w.T <= 64:
         extras["miss_policies"] = miss_policies(w, [xs[i] for i in range(nx)], routers[0], pools[0], rq, torch)
         if w.T == 1:
+            log("fp32 h ...")
+            extras["h_fp32"] = flag_step(w, xs, nl, pools, routers, ws, K, W, path_flag | rq.MOE_FLAG_H_FP32, rq, torch)
+            extras["h_fp32"]["default_us_per_layer"] = round(t_layer_s * 1e6, 3)
             log("staged layer ...")
             st = staged_step(w, xs, nl, pools, routers, ws, K, W, path_flag, rq, torch)
             st["routed_us_per_layer"] = round(t_layer_s * 1e6, 3)

@@ -79,7 +79,13 @@ enum {
    *       power-of-two exponent per tile, so no intermediate overflows; the
    *       per-slot outputs ahead of the combine are fp32. */
   MOE_FLAG_PATH_GATHER = 2u,
-  MOE_FLAG_PATH_GEMM = 4u
+  MOE_FLAG_PATH_GEMM = 4u,
+  /* Single-token path only: keep h = silu(gate) * up in fp32 between the
+   * gate/up and down kernels (by default it is stored in fp16, rounded to
+   * nearest even, when I <= 1024, and the down kernel reads half the bytes).
+   * Ignored by the T > 1 paths; moe_prerouted_layer_forward with this bit runs
+   * its expert and head launches separately (the fused form holds h in fp16). */
+  MOE_FLAG_H_FP32 = 8u
 };
 
 /* Stacked experts [LR "事前ウォームアップとmmapキャッシュを比べる"]:

@@ -567,10 +567,11 @@ constexpr int kDownRows = 2;
 hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int k, int renorm,
                             const float* logits, const int32_t* idx_in, const float* gate_in,
                             int32_t* idx_ws, float* gate_ws, int32_t* idx_user, float* gate_user,
-                            float* h, float* y, hipStream_t s) {
+                            float* h, float* y, bool h32, hipStream_t s) {
   const bool from_logits = logits != nullptr;
   const int nbi = (ex.I / 32 + 15) / 16;
-  const bool slots = nbi <= 2;
+  // fp16 h and the one-wave-per-slot down kernel, unless fp32 h is asked for
+  const bool slots = nbi <= 2 && !h32;
   const int nbj = (ex.H / 32 + 63) / 64;  // 1 (H <= 2048) or 2 (H <= 4096)
   with_scheme(ex.scheme, [&](auto S) {
     with_xtype(xtype, [&](auto X) {

@@ -90,7 +90,7 @@ hipError_t launch_group(const int32_t* idx, int T, int k, int E, const GroupBufs
 hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int k, int renorm,
                             const float* logits, const int32_t* idx_in, const float* gate_in,
                             int32_t* idx_ws, float* gate_ws, int32_t* idx_user, float* gate_user,
-                            float* h, float* y, hipStream_t s);
+                            float* h, float* y, bool h32, hipStream_t s);
 
 // Staged decode: copy experts[i] of pool into slot slots[i] of stack;
 // out = slot_of[idx] for ids in [0, E), -1 for ids outside it.

@@ -110,7 +110,7 @@ moe_status check_shape(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
 moe_status check_path_flags(uint32_t flags, int32_t xtype) {
   if ((flags & MOE_FLAG_PATH_GATHER) && (flags & MOE_FLAG_PATH_GEMM))
     return fail(MOE_ERR_INVALID_ARG, "both path flags are set");
-  if (flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_PATH_GATHER | MOE_FLAG_PATH_GEMM))
+  if (flags & ~(uint32_t)(MOE_FLAG_RENORM | MOE_FLAG_PATH_GATHER | MOE_FLAG_PATH_GEMM | MOE_FLAG_H_FP32))
     return fail(MOE_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
   if ((flags & MOE_FLAG_PATH_GEMM) && xtype == MOE_F32)
     return fail(MOE_ERR_UNSUPPORTED, "the grouped GEMM path takes fp16 or bf16 activations, not fp32");
@@ -157,7 +157,7 @@ moe_status run_experts(const void* x, int32_t xtype, int32_t T, const moe::Exper
   const bool gemm = (flags & MOE_FLAG_PATH_GEMM) || (!(flags & MOE_FLAG_PATH_GATHER) && T > 1 && xtype != MOE_F32);
   if (T == 1 && !gemm)
     return hip_status(moe::launch_decode_t1(x, xtype, d, k, 0, nullptr, idx, gate, nullptr, nullptr, nullptr,
-                                            nullptr, h, y, s),
+                                            nullptr, h, y, (flags & MOE_FLAG_H_FP32) != 0, s),
                       "decode (one token)");
   const moe::GroupBufs g = group_bufs(ws, L);
   hipError_t e = moe::launch_group(idx, T, k, d.E, g, s);
@@ -235,7 +235,8 @@ moe_status layer_from_logits(const void* x, int32_t xtype, int32_t T, const moe:
   float* gate = at<float>(ws, L.gate);
   if (T == 1 && !(flags & MOE_FLAG_PATH_GEMM))
     return hip_status(moe::launch_decode_t1(x, xtype, d, k, renorm, logits, nullptr, nullptr, idx, gate,
-                                            topk_idx_out, topk_gate_out, at<float>(ws, L.h), y, s),
+                                            topk_idx_out, topk_gate_out, at<float>(ws, L.h), y,
+                                            (flags & MOE_FLAG_H_FP32) != 0, s),
                       "decode (one token)");
   hipError_t e = moe::launch_topk(logits, nsplit, T, d.E, k, renorm, idx, gate, topk_idx_out, topk_gate_out, s);
   if (e != hipSuccess) return hip_status(e, "top-k");
@@ -626,7 +627,8 @@ moe_status moe_prerouted_layer_forward(const void* x, int32_t xtype, int32_t T, 
   float* part = at<float>(ws, base + align256((size_t)T * head->F * 4));
   float* raw = at<float>(ws, base + align256((size_t)T * head->F * 4) + 2 * align256((size_t)T * head->E * 4));
   const int renorm = (flags & MOE_FLAG_RENORM) ? 1 : 0;
-  if (T == 1 && !(flags & MOE_FLAG_PATH_GEMM) && moe::prerouted_t1_fusable(d, xtype, hd))
+  // (fp32 h is not a form of the fused launches: the expert and head launches run separately)
+  if (T == 1 && !(flags & (MOE_FLAG_PATH_GEMM | MOE_FLAG_H_FP32)) && moe::prerouted_t1_fusable(d, xtype, hd))
     return hip_status(moe::launch_prerouted_t1(x, xtype, d, k, renorm, logits, at<int32_t>(ws, L.idx),
                                                at<float>(ws, L.gate), topk_idx_out, topk_gate_out,
                                                at<float>(ws, L.h), y, hd, prev_idx, act, part, logits_next, s),

@@ -33,7 +33,7 @@ hipError_t launch_topk(const float*, int, int, int, int, int, int32_t*, float*, 
 }
 hipError_t launch_group(const int32_t*, int, int, int, const GroupBufs&, hipStream_t) { launched("grouping"); }
 hipError_t launch_decode_t1(const void*, int, const ExpertsDev&, int, int, const float*, const int32_t*, const float*,
-                            int32_t*, float*, int32_t*, float*, float*, float*, hipStream_t) {
+                            int32_t*, float*, int32_t*, float*, float*, float*, bool, hipStream_t) {
   launched("single-token decode");
 }
 hipError_t launch_stage_experts(const ExpertsDev&, const ExpertsDev&, const int32_t*, const int32_t*, int,

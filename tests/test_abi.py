@@ -103,6 +103,9 @@ def test_gather_and_layer_validation(L):
     assert gather(y=None) == rq.MOE_ERR_INVALID_ARG
     assert gather(flags=rq.MOE_FLAG_PATH_GATHER | rq.MOE_FLAG_PATH_GEMM) == rq.MOE_ERR_INVALID_ARG
     assert gather(flags=0x100) == rq.MOE_ERR_UNSUPPORTED
+    # fp32 h on the single-token path is a known flag: validation goes on to the workspace
+    assert gather(flags=rq.MOE_FLAG_H_FP32, nws=4096) == rq.MOE_ERR_WORKSPACE
+    assert gather(flags=rq.MOE_FLAG_H_FP32 | 0x100) == rq.MOE_ERR_UNSUPPORTED
     # the grouped GEMM takes 16-bit activations only; fp32 goes to the gathered path
     assert gather(flags=rq.MOE_FLAG_PATH_GEMM, xt=rq.MOE_F32, T=4) == rq.MOE_ERR_UNSUPPORTED
     assert b"fp16 or bf16" in L.moe_last_error()

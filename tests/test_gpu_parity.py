@@ -283,6 +283,29 @@ def test_single_token_paths_agree_with_oracle(name):
             outs.append(y.cpu().numpy())
 
 
+@pytest.mark.parametrize("name", ["decode40", "tiny", "batched_int4"])
+def test_single_token_fp32_h_matches_oracle(name):
+    """MOE_FLAG_H_FP32: the single-token path keeps h in fp32 (the general down
+    kernel); same routing, output within the contract, and no further from the
+    oracle than the default fp16 h by more than rounding noise."""
+    w = synth.WORKLOADS[name]
+    li = enforce_gap(w, synth.draw_layer(w, seed=5, layer=0, T=1, with_experts=False), seed=5, layer=0)
+    bf16 = w.xtype == synth.BF16
+    ridx, rgate = oracle.route(li.x, li.R, w.k, bf16=bf16)
+    ex = device_pool(w, 5, 0, np.unique(ridx))
+    xd, Rd = to_dev_x(li.x, w.xtype), torch.from_numpy(li.R).cuda()
+    y32, idx, _ = rq.moe_layer_forward(xd, Rd, ex, w.k, rq.MOE_FLAG_RENORM | rq.MOE_FLAG_H_FP32)
+    y16 = rq.moe_layer_forward(xd, Rd, ex, w.k, rq.MOE_FLAG_RENORM)[0]
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    rex, m = oracle_compact(w, 5, 0, np.unique(ridx))
+    ref = oracle.gather_forward(li.x, rex, remap(ridx, m), rgate, bf16=bf16)
+    e32, e16 = rel_norm_err(y32.cpu().numpy(), ref), rel_norm_err(y16.cpu().numpy(), ref)
+    say(f"{name}: rel_norm_err fp32 h {e32:.2e}, fp16 h {e16:.2e}")
+    assert e32 <= Y_REL_NORM
+    assert e32 <= e16 + 1e-6
+
+
 def test_stream_read_runs_on_ragged_sizes():
     """The bandwidth reference reads whole buffers and ragged tails without error."""
     buf = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
