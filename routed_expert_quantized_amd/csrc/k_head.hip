@@ -108,16 +108,16 @@ hipError_t launch_prerouter(const void* x, int xtype, int T, const HeadDev& hd, 
     int ns1 = 1, ns2 = 1, ld1 = F, ld2 = E, off2 = 0;
     if (hd.wl == hd.w1 + (int64_t)F * ldx) {
       // the residual path's rows follow fc1's in memory: one launch over F + E rows
-      e = launch_logits(x, xtype, T, H, hd.w1, F + E, raw1, &ns1, nullptr, s, ldx);
+      e = launch_logits(x, xtype, T, H, hd.w1, F + E, raw1, &ns1, false, s, ldx);
       if (e != hipSuccess) return e;
       raw2 = raw1;
       ns2 = ns1;
       ld1 = ld2 = F + E;
       off2 = F;
     } else {
-      e = launch_logits(x, xtype, T, H, hd.w1, F, raw1, &ns1, nullptr, s, ldx);
+      e = launch_logits(x, xtype, T, H, hd.w1, F, raw1, &ns1, false, s, ldx);
       if (e != hipSuccess) return e;
-      e = launch_logits(x, xtype, T, H, hd.wl, E, raw2, &ns2, nullptr, s, ldx);
+      e = launch_logits(x, xtype, T, H, hd.wl, E, raw2, &ns2, false, s, ldx);
       if (e != hipSuccess) return e;
     }
     MOE_LAUNCH(MOE_KERNEL_HEAD, k_head_epilogue, dim3((unsigned)(((F + E + 255) / 256) * T)), dim3(256), 0, s, raw1, ns1,

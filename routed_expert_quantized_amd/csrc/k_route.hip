@@ -405,37 +405,12 @@ __global__ __launch_bounds__(1024) void k_logits_mfma(const void* __restrict__ x
 // accuracy. Each fp32 router weight is split exactly into three bf16 parts
 // (hi: the top 8 significand bits, mid: the next 8 of the remainder, lo: the
 // rest, at most 8 bits), so x * w = x * hi + x * mid + x * lo with every
-// product exact; the MFMA adds them in fp32 like the fp32 kernel. The split
-// runs once per call over the router (k_split_router), the products take three
-// v_mfma_f32_16x16x32_bf16 per 32 K values instead of eight 16x16x4 fp32 MFMAs.
-// Tiles, split-K planes and the output mapping are those of k_logits_mfma; lane
-// (r = l%16, g = l/16) holds A[r][8g..8g+7] (a token row) and B[8g..8g+7][r] (an
-// expert row), D[4g+i][r].
-__global__ __launch_bounds__(256) void k_split_router(const float* __restrict__ R, int64_t n4,
-                                                      uint16_t* __restrict__ r3, int64_t plane) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  const float4 w = reinterpret_cast<const float4*>(R)[i];
-  const float wv[4] = {w.x, w.y, w.z, w.w};
-  uint16_t hi[4], mid[4], lo[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t hb = __builtin_bit_cast(uint32_t, wv[j]) & 0xFFFF0000u;
-    const float r1 = wv[j] - __builtin_bit_cast(float, hb);  // exact: the low 16 significand bits
-    const uint32_t mb = __builtin_bit_cast(uint32_t, r1) & 0xFFFF0000u;
-    const float r2 = r1 - __builtin_bit_cast(float, mb);     // exact, at most 8 significant bits
-    hi[j] = (uint16_t)(hb >> 16);
-    mid[j] = (uint16_t)(mb >> 16);
-    lo[j] = (uint16_t)(__builtin_bit_cast(uint32_t, r2) >> 16);
-  }
-  auto pack = [](const uint16_t (&v)[4]) {
-    return make_uint2((uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16));
-  };
-  reinterpret_cast<uint2*>(r3)[i] = pack(hi);
-  reinterpret_cast<uint2*>(r3 + plane)[i] = pack(mid);
-  reinterpret_cast<uint2*>(r3 + 2 * plane)[i] = pack(lo);
-}
-
+// product exact; the MFMA adds them in fp32 like the fp32 kernel. The split is
+// made in registers from the fp32 weights as they are loaded (4 bytes fetched
+// per weight), and the products take three v_mfma_f32_16x16x32_bf16 per 32 K
+// values instead of eight 16x16x4 fp32 MFMAs. Tiles, split-K planes and the
+// output mapping are those of k_logits_mfma; lane (r = l%16, g = l/16) holds
+// A[r][8g..8g+7] (a token row) and B[8g..8g+7][r] (an expert row), D[4g+i][r].
 typedef __bf16 bf16x8_r __attribute__((ext_vector_type(8)));
 
 template <typename F, int... Is>
@@ -455,21 +430,47 @@ constexpr int kSplitTallM = 8;
 // run while the loads of steps i+1 .. i+kRouterDepth-1 are outstanding.
 constexpr int kRouterDepth = 3;
 
+// The three bf16 parts of 8 fp32 weights, as MFMA operands: hi, mid, lo.
+__device__ __forceinline__ void split_bf16x3(const float4v_r (&w)[2], bf16x8_r (&b)[3]) {
+  uint32_t u[8], m[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = w[i >> 2][i & 3];
+    u[i] = __builtin_bit_cast(uint32_t, v);
+    const float r1 = v - __builtin_bit_cast(float, u[i] & 0xFFFF0000u);  // exact: the low 16 significand bits
+    m[i] = __builtin_bit_cast(uint32_t, r1);
+    const float r2 = r1 - __builtin_bit_cast(float, m[i] & 0xFFFF0000u);  // exact, at most 8 significant bits
+    l[i] = __builtin_bit_cast(uint32_t, r2);
+  }
+  // element 2j in the low half of word j, 2j+1 in the high half: the top
+  // halves of the two fp32 words
+  typedef uint32_t u32x4_r __attribute__((ext_vector_type(4)));
+  u32x4_r h4, m4, l4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h4[j] = __builtin_amdgcn_perm(u[2 * j + 1], u[2 * j], 0x07060302u);
+    m4[j] = __builtin_amdgcn_perm(m[2 * j + 1], m[2 * j], 0x07060302u);
+    l4[j] = __builtin_amdgcn_perm(l[2 * j + 1], l[2 * j], 0x07060302u);
+  }
+  b[0] = __builtin_bit_cast(bf16x8_r, h4);
+  b[1] = __builtin_bit_cast(bf16x8_r, m4);
+  b[2] = __builtin_bit_cast(bf16x8_r, l4);
+}
+
 template <int MTT, int NTT>
 __global__ __launch_bounds__(256) void k_logits_bf16x3(const uint16_t* __restrict__ x, int T, int H,
-                                                       const uint16_t* __restrict__ r3, int E,
+                                                       const float* __restrict__ R, int64_t ldr, int E,
                                                        float* __restrict__ logits, int kw) {
   extern __shared__ float red[];  // [waves][MTT*NTT*4][64]
   logits += (int64_t)blockIdx.z * T * E;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * 16 * MTT, e0 = blockIdx.y * 16 * NTT;
-  const int64_t plane = (int64_t)E * H;
   int64_t xrow[MTT], rrow[NTT];
 #pragma unroll
   for (int mt = 0; mt < MTT; ++mt) xrow[mt] = (int64_t)min(t0 + 16 * mt + r, T - 1) * H;
 #pragma unroll
-  for (int nt = 0; nt < NTT; ++nt) rrow[nt] = (int64_t)min(e0 + 16 * nt + r, E - 1) * H;
+  for (int nt = 0; nt < NTT; ++nt) rrow[nt] = (int64_t)min(e0 + 16 * nt + r, E - 1) * ldr;
   float4v_r acc[MTT][NTT];
 #pragma unroll
   for (int mt = 0; mt < MTT; ++mt)
@@ -479,27 +480,30 @@ __global__ __launch_bounds__(256) void k_logits_bf16x3(const uint16_t* __restric
   const int nsteps = kw / 32;
   // A ring of kRouterDepth register buffers, each one K step's fragments: the
   // loop is unrolled by the ring size so that every buffer index is a constant.
-  bf16x8_r a[kRouterDepth][MTT], b[kRouterDepth][3][NTT];
+  bf16x8_r a[kRouterDepth][MTT];
+  float4v_r wr[kRouterDepth][NTT][2];
   auto load = [&](auto S, int step) {
     constexpr int sl = decltype(S)::value;
     const int k = kb + 32 * step + 8 * g;
 #pragma unroll
     for (int mt = 0; mt < MTT; ++mt) a[sl][mt] = *reinterpret_cast<const bf16x8_r*>(x + xrow[mt] + k);
 #pragma unroll
-    for (int p = 0; p < 3; ++p)
+    for (int nt = 0; nt < NTT; ++nt)
 #pragma unroll
-      for (int nt = 0; nt < NTT; ++nt)
-        b[sl][p][nt] = *reinterpret_cast<const bf16x8_r*>(r3 + p * plane + rrow[nt] + k);
+      for (int h = 0; h < 2; ++h) wr[sl][nt][h] = *reinterpret_cast<const float4v_r*>(R + rrow[nt] + k + 4 * h);
   };
   auto mma = [&](auto S) {
     constexpr int sl = decltype(S)::value;
 #pragma unroll
-    for (int mt = 0; mt < MTT; ++mt)
+    for (int nt = 0; nt < NTT; ++nt) {
+      bf16x8_r b[3];
+      split_bf16x3(wr[sl][nt], b);
 #pragma unroll
-      for (int nt = 0; nt < NTT; ++nt)
+      for (int mt = 0; mt < MTT; ++mt)
 #pragma unroll
         for (int p = 0; p < 3; ++p)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sl][mt], b[sl][p][nt], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sl][mt], b[p], acc[mt][nt], 0, 0, 0);
+    }
   };
   router_static_for<kRouterDepth>([&](auto S) {
     if ((int)decltype(S)::value < nsteps) load(S, decltype(S)::value);
@@ -547,12 +551,12 @@ __global__ __launch_bounds__(256) void k_logits_bf16x3(const uint16_t* __restric
 constexpr int kLogitsWaves = 4;
 
 hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R, int E, float* logits,
-                         int* nsplit, uint16_t* r3, hipStream_t s, int64_t ldr) {
+                         int* nsplit, bool split_ok, hipStream_t s, int64_t ldr) {
   *nsplit = 1;
   if (ldr == 0) ldr = H;
   if (T >= kMfmaLogitsMinT) {
     // bf16 activations of a large batch: the split-weight bf16 kernel
-    const bool split3 = xtype == MOE_BF16 && r3 != nullptr && T >= kSplitRouterMinT;
+    const bool split3 = xtype == MOE_BF16 && split_ok && T >= kSplitRouterMinT;
     const int kstep = split3 ? 32 : 16;
     // tile shape and split-K: aim for about two waves per SIMD (2048 waves)
     int mtt = T >= 32 && (int64_t)((T + 31) / 32) * ((E + 31) / 32) >= 128 ? 2 : 1;
@@ -577,16 +581,11 @@ hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R,
     *nsplit = ns;
     const int kw = H / (nw * ns);
     const size_t lds = nw > 1 ? (size_t)nw * mtt * ntt * 256 * sizeof(float) : 0;
-    if (split3) {
-      const int64_t n4 = (int64_t)E * H / 4;
-      hipLaunchKernelGGL(k_split_router, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, R, n4, r3,
-                         (int64_t)E * H);
-    }
     auto go = [&](auto XC, auto MC, auto NC) {
       constexpr int X_ = decltype(XC)::value, M_ = decltype(MC)::value, N_ = decltype(NC)::value;
       if (split3)
         MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_bf16x3<M_, N_>), grid, dim3(64 * nw), lds, s,
-                   static_cast<const uint16_t*>(x), T, H, static_cast<const uint16_t*>(r3), E, logits, kw);
+                   static_cast<const uint16_t*>(x), T, H, R, ldr, E, logits, kw);
       else
         MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_mfma<X_, M_, N_>), grid, dim3(64 * nw), lds, s, x, T, H, R, E,
                    logits, kw, ldr);
@@ -594,7 +593,7 @@ hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R,
     auto with_tile = [&](auto XC) {
       if (mtt == kSplitTallM) {
         MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_bf16x3<kSplitTallM, 2>), grid, dim3(64 * nw), lds, s,
-                   static_cast<const uint16_t*>(x), T, H, static_cast<const uint16_t*>(r3), E, logits, kw);
+                   static_cast<const uint16_t*>(x), T, H, R, ldr, E, logits, kw);
         return;
       }
       if (mtt == 2 && ntt == 2) go(XC, std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});

@@ -72,12 +72,11 @@ inline int logits_max_splits(int64_t T, int64_t E) {
   return (int)(s < 1 ? 1 : s > kMaxLogitSplits ? kMaxLogitSplits : s);
 }
 // Writes *nsplit partial planes logits[s][T][E] (one for T < kMfmaLogitsMinT).
-// r3: scratch for the router split into three bf16 planes [3][E][H] (used for
-// bf16 activations from kSplitRouterMinT tokens; may be null below that).
-// ldr: row stride of R in elements (0: H); another stride is only for the
-// fp32 matrix-core path (T >= kMfmaLogitsMinT, r3 null).
+// split_ok: bf16 activations from kSplitRouterMinT tokens may take the
+// split-weight bf16 kernel (otherwise the fp32 matrix-core kernel).
+// ldr: row stride of R in elements (0: H).
 hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R, int E, float* logits,
-                         int* nsplit, uint16_t* r3, hipStream_t s, int64_t ldr = 0);
+                         int* nsplit, bool split_ok, hipStream_t s, int64_t ldr = 0);
 hipError_t launch_topk(const float* logits, int nsplit, int T, int E, int k, int renorm, int32_t* idx, float* gate,
                        int32_t* idx2, float* gate2, hipStream_t s);
 hipError_t launch_group(const int32_t* idx, int T, int k, int E, const GroupBufs& g, hipStream_t s);

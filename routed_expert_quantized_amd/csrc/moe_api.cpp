@@ -47,7 +47,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 // Scratch regions inside the caller's workspace, each 256-byte aligned.
 struct Layout {
-  size_t logits, idx, gate, mask, base, counts, offsets, perm, uniq, n_uniq, h, hsig, ys, r3, total;
+  size_t logits, idx, gate, mask, base, counts, offsets, perm, uniq, n_uniq, h, hsig, ys, total;
 };
 
 Layout layout(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
@@ -72,7 +72,6 @@ Layout layout(int64_t T, int64_t E, int64_t H, int64_t I, int64_t k) {
   L.h = take(T * k * I * 4);
   L.hsig = take(T * k * ((I + 63) / 64) * 4);  // the grouped GEMM's tile exponents of h
   L.ys = take(T * k * H * 4);
-  L.r3 = take(T >= moe::kSplitRouterMinT ? 3 * E * H * 2 : 0);  // router split into bf16 planes
   L.total = off;
   return L;
 }
@@ -326,7 +325,7 @@ moe_status moe_route(const void* x, int32_t xtype, int32_t T, int32_t H, const f
   float* logits = at<float>(ws, L.logits);
   int nsplit = 1;
   hipError_t e = moe::launch_logits(x, xtype, T, H, router_w, E, logits, &nsplit,
-                                    T >= moe::kSplitRouterMinT ? at<uint16_t>(ws, L.r3) : nullptr, s);
+                                    true, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
   return hip_status(moe::launch_topk(logits, nsplit, T, E, k, (flags & MOE_FLAG_RENORM) ? 1 : 0, topk_idx, topk_gate,
                                      nullptr, nullptr, s),
@@ -378,7 +377,7 @@ moe_status moe_layer_forward(const void* x, int32_t xtype, int32_t T, const floa
   float* logits = at<float>(ws, L.logits);
   int nsplit = 1;
   hipError_t e = moe::launch_logits(x, xtype, T, d.H, router_w, d.E, logits, &nsplit,
-                                    T >= moe::kSplitRouterMinT ? at<uint16_t>(ws, L.r3) : nullptr, s);
+                                    true, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
   return layer_from_logits(x, xtype, T, d, k, flags, logits, nsplit, y, topk_idx_out, topk_gate_out, ws, L, s);
 }
@@ -405,7 +404,7 @@ moe_status moe_layer_forward_staged(const void* x, int32_t xtype, int32_t T, con
   float* logits = at<float>(ws, L.logits);
   int nsplit = 1;
   hipError_t e = moe::launch_logits(x, xtype, T, d.H, router_w, d.E, logits, &nsplit,
-                                    T >= moe::kSplitRouterMinT ? at<uint16_t>(ws, L.r3) : nullptr, s);
+                                    true, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
   return layer_from_logits(x, xtype, T, d, k, flags, logits, nsplit, y, topk_idx_out, topk_gate_out, ws, L, s);
 }

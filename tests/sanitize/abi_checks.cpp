@@ -26,7 +26,7 @@ namespace moe {
   std::fprintf(stderr, "a host check let %s launch\n", what);
   std::abort();
 }
-hipError_t launch_logits(const void*, int, int, int, const float*, int, float*, int*, uint16_t*, hipStream_t,
+hipError_t launch_logits(const void*, int, int, int, const float*, int, float*, int*, bool, hipStream_t,
                          int64_t) { launched("router logits"); }
 hipError_t launch_topk(const float*, int, int, int, int, int, int32_t*, float*, int32_t*, float*, hipStream_t) {
   launched("top-k");
