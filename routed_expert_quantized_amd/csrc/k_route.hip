@@ -561,12 +561,15 @@ hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R,
     // tile shape and split-K: aim for about two waves per SIMD (2048 waves)
     int mtt = T >= 32 && (int64_t)((T + 31) / 32) * ((E + 31) / 32) >= 128 ? 2 : 1;
     int ntt = E >= 32 && (int64_t)((T + 16 * mtt - 1) / (16 * mtt)) * ((E + 31) / 32) >= 128 ? 2 : 1;
-    // The split-weight kernel is bound by what its tiles fetch from L2: each
-    // expert row is three planes, each token row one. Taller token tiles fetch
-    // each plane row for more tokens (mtt and ntt always name the launched
-    // kernel's tile: the grid and the reduction's LDS follow them).
-    if (split3 && ntt == 2 && (int64_t)((T + 16 * kSplitTallM - 1) / (16 * kSplitTallM)) * ((E + 31) / 32) >= 128)
+    // The split-weight kernel is bound by what its tiles fetch from L2 (each
+    // expert row in fp32, each token row in bf16): taller and wider tiles
+    // fetch each row for more of the other side (mtt and ntt always name the
+    // launched kernel's tile: the grid and the reduction's LDS follow them).
+    if (split3 && ntt == 2 && (int64_t)((T + 16 * kSplitTallM - 1) / (16 * kSplitTallM)) * ((E + 31) / 32) >= 128) {
       mtt = kSplitTallM;
+      // wider expert tiles once there are enough of them
+      if ((int64_t)((T + 16 * kSplitTallM - 1) / (16 * kSplitTallM)) * ((E + 63) / 64) >= 256) ntt = 4;
+    }
     dim3 grid((T + 16 * mtt - 1) / (16 * mtt), (E + 16 * ntt - 1) / (16 * ntt));
     const int64_t tiles = (int64_t)grid.x * grid.y;
     // waves per workgroup (up to 4), then K splits across workgroups, while the
@@ -592,8 +595,12 @@ hipError_t launch_logits(const void* x, int xtype, int T, int H, const float* R,
     };
     auto with_tile = [&](auto XC) {
       if (mtt == kSplitTallM) {
-        MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_bf16x3<kSplitTallM, 2>), grid, dim3(64 * nw), lds, s,
-                   static_cast<const uint16_t*>(x), T, H, R, ldr, E, logits, kw);
+        if (ntt == 4)
+          MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_bf16x3<kSplitTallM, 4>), grid, dim3(64 * nw), lds, s,
+                     static_cast<const uint16_t*>(x), T, H, R, ldr, E, logits, kw);
+        else
+          MOE_LAUNCH(MOE_KERNEL_ROUTE_LOGITS, (k_logits_bf16x3<kSplitTallM, 2>), grid, dim3(64 * nw), lds, s,
+                     static_cast<const uint16_t*>(x), T, H, R, ldr, E, logits, kw);
         return;
       }
       if (mtt == 2 && ntt == 2) go(XC, std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
