@@ -42,14 +42,15 @@ static void with_xtype(int xt, F&& f) {
 // Waves per workgroup of the single-token gate/up kernel (each owns one row pair).
 constexpr int kGateUpWaves = 4;
 
-// Grid: k slots x blocks_per_slot. A wave computes RP (gate row n, up row I+n)
-// pairs of its slot's expert and writes h[slot][n] = silu(gate) * up.
-// ROUTE 0: the routing is given (idx_in, expert ids, mapped through the slot
-// table when there is one). ROUTE 1: wave 0 of each workgroup first picks the
-// top k from the router logits (every workgroup redoes this small step, so no
-// cross-workgroup sync is needed); one workgroup publishes the routing for the
-// down kernel and the caller. ROUTE 2: as 1, with each pick's slot-table entry
-// (the expert's slot in a resident stack) as the weights' index.
+// Grid: k slots x blocks_per_slot (+1 from logits). A wave computes RP (gate
+// row n, up row I+n) pairs of its slot's expert and writes h[slot][n] =
+// silu(gate) * up. ROUTE 0: the routing is given (idx_in, expert ids, mapped
+// through the slot table when there is one). ROUTE 1: wave 0 of each
+// workgroup first picks the top k from the router logits, as far as its slot
+// (every workgroup redoes this small step, so no cross-workgroup sync is
+// needed); one extra workgroup publishes the routing for the down kernel and
+// the caller. ROUTE 2: as 1, with each pick's slot-table entry (the expert's
+// slot in a resident stack) as the weights' index.
 // With H16 the activation is stored as fp16 (round to nearest even) for the
 // slot-parallel down kernel, else as fp32.
 template <int SCHEME, int XT, int NBJ, int RP, int ROUTE, int VPL, bool H16>
@@ -86,33 +87,44 @@ __device__ __forceinline__ void gate_up_t1_body(const void* __restrict__ x, cons
     for (int j = 0; j < NBJ; ++j) load_xreg<SCHEME, XT>(xr[j], x, 0, min(lane + 64 * j, NB - 1));
   }
   int e;
-  // The first workgroup of the last slot publishes the routing for the down
-  // kernel and the caller (lane s < k of its wave 0 holds rank s), after its
-  // weight loads are issued (stores count in the same counter as loads, and a
-  // wait for them would hold the loads back).
-  bool publisher = false;
-  int pub_idx = 0, pub_row = 0;
-  float pub_gate = 0.0f;
   if constexpr (FROM_LOGITS) {
-    // A workgroup of slot s needs only the first s+1 rounds; the publisher
-    // runs all k and computes the gates. Wave 0 picks the routing (with a slot
-    // table, each rank's entry comes along); the other waves store the
-    // activations and wait for it at the barrier.
-    publisher = bid == (k - 1) * blocks_per_slot;
-    const int rounds = publisher ? k : slot + 1;
+    // One extra workgroup, after the k slots' ones, publishes the routing for
+    // the down kernel and the caller: it ranks all k experts and computes
+    // their gates (lane s < k of its wave 0 holds rank s) and reads no
+    // weights, so no weight-reading workgroup waits for the gates.
+    if (bid == k * blocks_per_slot) {
+      if (wave == 0) {
+        int my_idx, my_row;
+        float my_gate;
+        if constexpr (ROUTE == 2) {
+          wave_topk<VPL, true>(logits, ex.E, k, renorm != 0, my_idx, my_gate, k, ex.slot_of, ex.slots, &my_row);
+        } else {
+          wave_topk<VPL>(logits, ex.E, k, renorm != 0, my_idx, my_gate, k);
+          my_row = my_idx;
+        }
+        // the down kernel reads the weights' indices (slots when staged), the caller the expert ids
+        if (lane < k) {
+          idx_ws[lane] = my_row;
+          gate_ws[lane] = my_gate;
+          if (idx_user) idx_user[lane] = my_idx;
+          if (gate_user) gate_user[lane] = my_gate;
+        }
+      }
+      return;
+    }
+    // A workgroup of slot s needs only the first s+1 rounds. Wave 0 picks the
+    // routing (with a slot table, each rank's entry comes along); the other
+    // waves store the activations and wait for it at the barrier.
     __shared__ int e_sh;
     if (wave == 0) {
       int my_idx, my_row;
       float my_gate;
       if constexpr (ROUTE == 2) {
-        wave_topk<VPL, true>(logits, ex.E, k, renorm != 0, my_idx, my_gate, rounds, ex.slot_of, ex.slots, &my_row);
+        wave_topk<VPL, true>(logits, ex.E, k, renorm != 0, my_idx, my_gate, slot + 1, ex.slot_of, ex.slots, &my_row);
       } else {
-        wave_topk<VPL>(logits, ex.E, k, renorm != 0, my_idx, my_gate, rounds);
+        wave_topk<VPL>(logits, ex.E, k, renorm != 0, my_idx, my_gate, slot + 1);
         my_row = my_idx;
       }
-      pub_idx = my_idx;
-      pub_row = my_row;
-      pub_gate = my_gate;
       if (lane == slot) e_sh = my_row;
     }
     if constexpr (kStageX) {
@@ -159,13 +171,6 @@ __device__ __forceinline__ void gate_up_t1_body(const void* __restrict__ x, cons
       sg[r][j] = scale_or_zero(ex.sgu + grow * NB + b, resident);
       su[r][j] = scale_or_zero(ex.sgu + urow * NB + b, resident);
     }
-  }
-  // the down kernel reads the weights' indices (slots when staged), the caller the expert ids
-  if (publisher && wave == 0 && lane < k) {
-    idx_ws[lane] = pub_row;
-    gate_ws[lane] = pub_gate;
-    if (idx_user) idx_user[lane] = pub_idx;
-    if (gate_user) gate_user[lane] = pub_gate;
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -579,7 +584,8 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
       auto go = [&](auto NBJc, auto RPc) {
         constexpr int NBJ = decltype(NBJc)::value, RP = decltype(RPc)::value;
         const int bps = (ex.I + kGateUpWaves * RP - 1) / (kGateUpWaves * RP);
-        dim3 grid(k * bps);
+        // from logits: one more workgroup, which publishes the routing
+        dim3 grid(k * bps + (from_logits ? 1 : 0));
         auto launch = [&](auto RTc, auto VPLc, auto H16c) {
           constexpr bool H16 = decltype(H16c)::value != 0;
           constexpr int RT = decltype(RTc)::value, VPL = decltype(VPLc)::value;
@@ -711,7 +717,7 @@ hipError_t launch_prerouted_t1(const void* x, int xtype, const ExpertsDev& ex, i
       auto go = [&](auto NBJc, auto VPLc, auto HNc) {
         constexpr int NBJ = decltype(NBJc)::value, VPL = decltype(VPLc)::value, HN = decltype(HNc)::value;
         const int bps = (ex.I + kGateUpWaves - 1) / kGateUpWaves;
-        dim3 grid(k * bps + hd.F + hd.E);
+        dim3 grid(k * bps + 1 + hd.F + hd.E);  // the expert grid ends with its routing publisher
         MOE_LAUNCH(MOE_KERNEL_GATE_UP, (k_gate_up_t1_head<SC, XT, NBJ, VPL, HN>), grid, dim3(64 * kGateUpWaves), 0, s,
                    x, ex, k, renorm, logits, idx_ws, gate_ws, idx_user, gate_user, h, bps, hd, prev, act, part);
       };
