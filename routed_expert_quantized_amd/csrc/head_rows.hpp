@@ -6,6 +6,7 @@
 // routing], head = fc2(erf-gelu(fc1(input))) + l(input).
 #pragma once
 #include "common.hpp"
+#include "kernels.hpp"
 
 namespace moe {
 
@@ -91,6 +92,71 @@ __device__ __forceinline__ void head_stage1_body(
       else out2[(int64_t)(tb + lane) * E + r] = z;
     }
     __syncthreads();
+  }
+}
+
+// Stage 1 for one token inside the fused decode launch, which first picks the
+// token's routing from the logits (the k-hot input). The row's reads that do
+// not need it (its hidden part, the activations, the previous token's routed
+// entries) go out first and stay in flight while wave 0 picks the routing;
+// only the current token's k entries are read after it. The sums are
+// head_stage1_body's, in the same order.
+template <int XT, int NCH, int VPL>
+__device__ __forceinline__ void head_stage1_t1_routed(int bx, const void* __restrict__ x, int H, int E, int R1,
+                                                      const float* __restrict__ W1, const float* __restrict__ b1,
+                                                      const float* __restrict__ Wl, const float* __restrict__ b2,
+                                                      const float* __restrict__ logits, int k, int renorm,
+                                                      const int32_t* __restrict__ prev, float* __restrict__ out1,
+                                                      float* __restrict__ out2) {
+  __shared__ float red[kHeadWaves];
+  __shared__ int32_t cur_sh[kMaxK];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const bool fc1 = bx < R1;
+  const int r = fc1 ? bx : bx - R1;
+  const int64_t ldx = (int64_t)H + 2 * E;
+  const float* wx = (fc1 ? W1 : Wl) + (int64_t)r * ldx;
+  const int nx = (H + 255) >> 8;
+  float4 wr[NCH], v[NCH];
+  bool ok[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = w + kHeadWaves * i;
+    const int j = c * 256 + lane * 4;
+    ok[i] = c < nx && j < H;
+    const int col = min(j, H - 4);  // in bounds; masked out of the sums when !ok
+    wr[i] = c < nx ? *reinterpret_cast<const float4*>(wx + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[i] = c < nx ? load_x4<XT>(x, col) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  // lanes k .. 2k-1 of wave 0: the previous token's routed entries
+  const float gp = (w == 0 && lane >= k && lane < 2 * k && prev) ? wx[H + E + prev[lane - k]] : 0.0f;
+  if (w == 0) {
+    int my_idx;
+    float my_gate;
+    wave_topk<VPL>(logits, E, k, renorm != 0, my_idx, my_gate);
+    if (lane < k) cur_sh[lane] = my_idx;
+  }
+  __syncthreads();
+  // lanes 0 .. k-1 of wave 0: the current token's routed entries
+  float acc = (w == 0 && lane < k) ? wx[H + cur_sh[lane]] : gp;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    if (ok[i]) {
+      acc = fmaf(wr[i].x, v[i].x, acc);
+      acc = fmaf(wr[i].y, v[i].y, acc);
+      acc = fmaf(wr[i].z, v[i].z, acc);
+      acc = fmaf(wr[i].w, v[i].w, acc);
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) red[w] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float* bias = fc1 ? b1 : b2;
+    float z = bias ? bias[r] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < kHeadWaves; ++q) z += red[q];
+    if (fc1) out1[r] = gelu_erf(z);
+    else out2[r] = z;
   }
 }
 

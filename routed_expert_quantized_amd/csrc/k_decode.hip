@@ -652,9 +652,9 @@ hipError_t launch_decode_t1(const void* x, int xtype, const ExpertsDev& ex, int 
 
 // F + E head rows (fc1 + GELU, residual path), then the gate/up grid; the head
 // rows come first so their weight reads, which do not wait for the routing,
-// start with the launch. A head workgroup first picks the layer's routing from
-// the same logits, as the gate/up workgroups do, for the current-token k-hot
-// input.
+// start with the launch. A head workgroup picks the layer's routing from the
+// same logits, as the gate/up workgroups do, for the current-token k-hot
+// input, while those reads are in flight.
 template <int SCHEME, int XT, int NBJ, int VPL, int HNCH>
 __global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1_head(
     const void* __restrict__ x, ExpertsDev ex, int k, int renorm, const float* __restrict__ logits,
@@ -668,16 +668,8 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_gate_up_t1_head(
                                                          gate_user, h, blocks_per_slot, (int)blockIdx.x - nhead);
     return;
   }
-  __shared__ int32_t cur_sh[kMaxK];
-  if (threadIdx.x < 64) {
-    int my_idx;
-    float my_gate;
-    wave_topk<VPL>(logits, ex.E, k, renorm != 0, my_idx, my_gate);
-    if ((int)threadIdx.x < k) cur_sh[threadIdx.x] = my_idx;
-  }
-  __syncthreads();
-  head_stage1_body<XT, HNCH, 1, 1>((int)blockIdx.x, 0, x, 1, hd.H, hd.E, hd.F, hd.w1, hd.b1, hd.wl, hd.b2, cur_sh,
-                                   prev, k, act, part);
+  head_stage1_t1_routed<XT, HNCH, VPL>((int)blockIdx.x, x, hd.H, hd.E, hd.F, hd.w1, hd.b1, hd.wl, hd.b2, logits, k,
+                                       renorm, prev, act, part);
 }
 
 // ceil(E / k) workgroups of head stage 2 (one fc2 row per wave), then the down
