@@ -477,17 +477,18 @@ __device__ __forceinline__ void wave_topk_sorted(const float* logits, int E, int
 }
 
 // Top k with gates (lanes s < k hold slot s). With rounds < k only the first
-// `rounds` slots are produced and no gates (the scan form produces all k).
+// `rounds` slots are produced and no gates (the scan form produces all k);
+// gates = false skips them also at rounds == k.
 // With ROWS, lane s also gets the slot-table entry of its expert (as in
 // wave_topk_sorted; the scan form looks it up after the selection).
 template <int VPL, bool ROWS = false>
 __device__ __forceinline__ void wave_topk(const float* logits, int E, int k, bool renorm, int& my_idx,
                                           float& my_gate, int rounds = -1, const int32_t* slot_of = nullptr,
-                                          int nslots = 0, int* my_row = nullptr) {
+                                          int nslots = 0, int* my_row = nullptr, bool gates = true) {
   if (rounds < 0) rounds = k;
   if constexpr (VPL <= 8) {
-    wave_topk_sorted<VPL, ROWS>(logits, E, k, renorm, my_idx, my_gate, rounds, rounds == k, slot_of, nslots,
-                                my_row);
+    wave_topk_sorted<VPL, ROWS>(logits, E, k, renorm, my_idx, my_gate, rounds, gates && rounds == k, slot_of,
+                                nslots, my_row);
   } else {
     wave_topk_scan<VPL>(logits, E, k, renorm, my_idx, my_gate);
     if constexpr (ROWS) {

@@ -132,7 +132,7 @@ __device__ __forceinline__ void head_stage1_t1_routed(int bx, const void* __rest
   if (w == 0) {
     int my_idx;
     float my_gate;
-    wave_topk<VPL>(logits, E, k, renorm != 0, my_idx, my_gate);
+    wave_topk<VPL>(logits, E, k, renorm != 0, my_idx, my_gate, k, nullptr, 0, nullptr, false);  // ids only
     if (lane < k) cur_sh[lane] = my_idx;
   }
   __syncthreads();
