@@ -65,6 +65,22 @@ def test_route_parity(name, T, renorm):
     assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
 
 
+# bf16 batches with at least 256 tiles of 128 tokens x 64 experts take the
+# split-weight router's wide tile; ragged T and E included
+@pytest.mark.parametrize("T,E,H,k", [(8300, 200, 256, 8), (8192, 256, 512, 6)])
+def test_route_split_weight_wide_tiles(T, E, H, k):
+    g = np.random.default_rng(T + E)
+    x32 = g.standard_normal((T, H)).astype(np.float32)
+    R = (g.standard_normal((E, H)) * H ** -0.5).astype(np.float32)
+    w = synth.Workload("adhoc", T=T, H=H, E=E, k=k, I=32, scheme=0, xtype=synth.BF16)
+    li = enforce_gap(w, synth.LayerInputs(x32, synth.encode_x(x32, synth.BF16), R, None, None), seed=5, layer=E)
+    say(f"route wide tiles T={T} E={E} H={H} k={k}")
+    idx, gate = rq.moe_route(to_dev_x(li.x, w.xtype), torch.from_numpy(li.R).cuda(), k, rq.MOE_FLAG_RENORM)
+    ridx, rgate = oracle.route(li.x, li.R, k, flags=oracle.RENORM, bf16=True)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(gate.cpu().numpy() - rgate).max() <= GATE_ATOL
+
+
 def test_route_many_experts_and_max_k():
     g = np.random.default_rng(7)
     for T, H, E, k in [(5, 256, 1000, 16), (2, 64, 1024, 3), (4, 32, 16, 16), (1, 4096, 64, 1)]:
