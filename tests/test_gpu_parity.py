@@ -362,7 +362,7 @@ def test_single_token_layer_exact_ties(E, k):
 # x per thread through LDS); I = 1024 (two blocks per lane in the down kernel);
 # I = 2048 (the fp32-activation down kernel); E = 512 (eight logits per lane)
 T1_EDGE = [(1, 32, 32, 1), (16, 64, 32, 16), (64, 4096, 64, 8), (32, 256, 1024, 10), (512, 64, 32, 10),
-           (8, 256, 2048, 3), (300, 160, 96, 5)]
+           (8, 256, 2048, 3), (300, 160, 96, 5), (320, 256, 96, 8)]
 
 
 @pytest.mark.parametrize("E,H,I,k", T1_EDGE)
