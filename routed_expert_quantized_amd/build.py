@@ -2,6 +2,10 @@
 
 Every source under csrc/ is compiled for gfx950 only, then linked into
 routed_expert_quantized_amd/libmoe.so. Run: python -m routed_expert_quantized_amd.build
+
+With --stamps the same sources are built with -DMOE_STAMPS into
+libmoe_stamps.so instead: the timestamp build that
+`python -m routed_expert_quantized_amd.timeline` loads (csrc/stamps.hpp).
 """
 from __future__ import annotations
 
@@ -17,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+STAMPS_LIB = os.path.join(PKG, "libmoe_stamps.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions stay off: all float math is written as scalar code.
@@ -25,9 +30,9 @@ CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
           "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, stamps: bool = False) -> str:
+    obj = os.path.join(BUILD, ("stamps_" if stamps else "") + os.path.basename(src) + ".o")
+    cmd = [HIPCC, *CFLAGS, *(["-DMOE_STAMPS"] if stamps else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -37,20 +42,21 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, stamps: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     jobs = max(1, min(len(srcs), os.cpu_count() or 4, 16))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, stamps), srcs))
+    lib = STAMPS_LIB if stamps else LIB
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, stamps="--stamps" in sys.argv[1:])

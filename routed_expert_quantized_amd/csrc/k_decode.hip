@@ -18,8 +18,14 @@
 
 #include "head_rows.hpp"
 #include "kernels.hpp"
+#include "stamps.hpp"
 
 namespace moe {
+
+// timestamp build only. Single-token gate/up workgroups: 0 start, 1 routing
+// known, 2 weight loads landed, 3 end; down workgroups: 4 start, 5 routing
+// read, 6 weight loads landed, 7 end.
+MOE_STAMP_TABLE(g_stamps_decode, 8);
 
 template <int V>
 using IC = std::integral_constant<int, V>;
@@ -63,6 +69,7 @@ __device__ __forceinline__ void gate_up_t1_body(const void* __restrict__ x, cons
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int slot = bid / blocks_per_slot, blk = bid % blocks_per_slot;
   const int H = ex.H, I = ex.I, NB = H / 32;
+  MOE_STAMP(g_stamps_decode, 0, bid);
   // Every load below is unconditional (block and row indices are clamped in
   // bounds, surplus lanes get a zero scale) so the scheduler can issue them all
   // before the arithmetic.
@@ -136,6 +143,7 @@ __device__ __forceinline__ void gate_up_t1_body(const void* __restrict__ x, cons
     }
     __syncthreads();
     e = e_sh;
+    MOE_STAMP(g_stamps_decode, 1, bid);
   } else {
     e = expert_index(ex, idx_in[slot]);
   }
@@ -173,6 +181,7 @@ __device__ __forceinline__ void gate_up_t1_body(const void* __restrict__ x, cons
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  MOE_STAMP_LANDED(g_stamps_decode, 2, bid);
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
     float ag = 0.0f, au = 0.0f;
@@ -190,6 +199,7 @@ __device__ __forceinline__ void gate_up_t1_body(const void* __restrict__ x, cons
       else h[(int64_t)slot * I + n0 + r] = hv;
     }
   }
+  MOE_STAMP(g_stamps_decode, 3, bid);
 }
 
 template <int SCHEME, int XT, int NBJ, int RP, int ROUTE, int VPL, bool H16>
@@ -220,6 +230,7 @@ __device__ __forceinline__ void down_t1_slots_body(const ExpertsDev& ex, int k, 
   const int q = tid >> 6, lane = tid & 63, lg = lane >> 4, ll = lane & 15;
   const int H = ex.H, I = ex.I, NBI = I / 32;
   const int mb = (int)bid * 4 * RW, m0 = mb + lg * RW;
+  MOE_STAMP(g_stamps_decode, 4, bid);
   const int64_t rb = row_bytes<SCHEME>(I);
   // idx holds weight indices, or expert ids mapped here through a slot table;
   // an expert without a slot contributes nothing. The index is requested
@@ -231,6 +242,10 @@ __device__ __forceinline__ void down_t1_slots_body(const ExpertsDev& ex, int k, 
   int e = expert_index(ex, iq);
   const bool resident = e >= 0;  // a slot-less expert: zero scales, whatever slot 0 holds
   e = max(e, 0);
+#ifdef MOE_STAMPS
+  asm volatile("" ::"v"(e));  // the routing read is consumed before the stamp
+#endif
+  MOE_STAMP_LANDED(g_stamps_decode, 5, bid);
   Block<SCHEME> c[RW][NBJ];
   float sc[RW][NBJ];
 #pragma unroll
@@ -243,6 +258,7 @@ __device__ __forceinline__ void down_t1_slots_body(const ExpertsDev& ex, int k, 
       sc[r][j] = scale_or_zero(ex.sd + row * NBI + b, resident);
     }
   }
+  MOE_STAMP_LANDED(g_stamps_decode, 6, bid);
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     float part_r = 0.0f;
@@ -262,6 +278,7 @@ __device__ __forceinline__ void down_t1_slots_body(const ExpertsDev& ex, int k, 
     for (int s = 0; s < k; ++s) acc = fmaf(gate[s], part[s][tid], acc);
     y[mb + tid] = acc;
   }
+  MOE_STAMP(g_stamps_decode, 7, bid);
 }
 
 template <int SCHEME, int NBJ, int RW>
@@ -820,3 +837,5 @@ hipError_t launch_combine(int T, int H, int k, const float* gate, const float* y
 }
 
 }  // namespace moe
+
+MOE_STAMP_READER(moe_stamps_read_decode, moe::g_stamps_decode);

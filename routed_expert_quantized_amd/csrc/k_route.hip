@@ -6,8 +6,12 @@
 #include <utility>
 
 #include "kernels.hpp"
+#include "stamps.hpp"
 
 namespace moe {
+
+// timestamp build only: start and end of each row kernel workgroup
+MOE_STAMP_TABLE(g_stamps_route, 2);
 
 // ---------------------------------------------------------------- logits, few tokens
 // WPE waves per expert row: logits[t][e] = R[e] . x[t] in fp32, for every token.
@@ -23,6 +27,7 @@ __global__ __launch_bounds__(64 * WPE) void k_logits_rows(const void* __restrict
   __shared__ float red[WPE][TU];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int e = blockIdx.x;
+  MOE_STAMP(g_stamps_route, 0, blockIdx.x);
   const int c0 = w * NCH;
   const float* row = R + (int64_t)e * H;
   float4 r[NCH];
@@ -70,6 +75,7 @@ __global__ __launch_bounds__(64 * WPE) void k_logits_rows(const void* __restrict
       __syncthreads();
     }
   }
+  MOE_STAMP(g_stamps_route, 1, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- top-k, one wave per token
@@ -670,3 +676,14 @@ hipError_t launch_group(const int32_t* idx, int T, int k, int E, const GroupBufs
 }
 
 }  // namespace moe
+
+MOE_STAMP_READER(moe_stamps_read_route, moe::g_stamps_route);
+#ifdef MOE_STAMPS
+// frequency of the stamps' counter on the current device, in kHz (0 on error)
+extern "C" int moe_stamps_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return 0;
+  return khz;
+}
+#endif

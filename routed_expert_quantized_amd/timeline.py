@@ -1,0 +1,143 @@
+"""Timeline of the single-token chain (router -> gate/up -> down) at decode40.
+
+Loads the timestamp build (libmoe_stamps.so; csrc/stamps.hpp), captures the
+40-layer decode40 step as the bench does (one HIP graph, same layers, same
+inputs), replays it, and prints in Markdown when each phase of the last layer
+happened, relative to the first router workgroup's start: per kernel the
+earliest, median and latest workgroup; for gate/up also per slot (the slot-s
+workgroups run s+1 top-k rounds); and the gaps between kernels. The stamps
+that wait for loads change wave 0's schedule, so the chain under this build
+is somewhat slower than the plain library's; its event time is printed too.
+
+Build on any host with hipcc, then run from the repository root on one GPU:
+    python -m routed_expert_quantized_amd.build --stamps
+    python -m routed_expert_quantized_amd.timeline [--replays N]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import os
+import statistics
+import sys
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+COLS = 1024  # kStampCols
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--replays", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=40)
+    args = ap.parse_args()
+    sys.path.insert(0, ROOT)
+    import torch
+
+    import routed_expert_quantized_amd as rq
+    rq.LIB_PATH = os.path.join(PKG, "libmoe_stamps.so")
+    if not os.path.exists(rq.LIB_PATH):
+        raise SystemExit(f"{rq.LIB_PATH} is missing: python -m routed_expert_quantized_amd.build --stamps")
+    import bench
+    import synth
+    L = rq.lib()
+    for fn in (L.moe_stamps_read_route, L.moe_stamps_read_decode):
+        fn.argtypes = [ctypes.c_void_p]
+        fn.restype = ctypes.c_int
+    L.moe_stamps_clock_khz.restype = ctypes.c_int
+
+    w = synth.WORKLOADS["decode40"]
+    NL = args.layers
+    pools, routers = bench.build_layers(w, NL, 0, rq, synth, torch)
+    xs = [bench.to_dev(synth.draw_step_x(w, 0, s), w.xtype, torch) for s in range(16)]
+    xbuf = torch.empty_like(xs[0])
+    ys = [torch.empty((1, w.H), dtype=torch.float32, device="cuda") for _ in range(NL)]
+    ws = rq.Workspace()
+    ws.get(rq.moe_workspace_bytes(1, w.E, w.H, w.I, w.k, w.scheme))
+
+    def run():
+        for l in range(NL):
+            rq.moe_layer_forward(xbuf, routers[l], pools[l], w.k, rq.MOE_FLAG_RENORM, ws=ws, out=ys[l],
+                                 return_routing=False)
+
+    xbuf.copy_(xs[0])
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    khz = L.moe_stamps_clock_khz()
+    if khz <= 0:
+        raise SystemExit("could not read the stamps' clock rate")
+    us_per_tick = 1000.0 / khz
+
+    r = np.zeros((2, COLS), np.uint64)
+    d = np.zeros((8, COLS), np.uint64)
+    runs = []
+    for rep in range(args.replays + 2):
+        xbuf.copy_(xs[rep % len(xs)])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        if L.moe_stamps_read_route(r.ctypes.data) != 0 or L.moe_stamps_read_decode(d.ctypes.data) != 0:
+            raise SystemExit("reading the stamps failed")
+        if rep >= 2:
+            runs.append((e0.elapsed_time(e1) * 1000.0 / NL, r.copy(), d.copy()))
+
+    # the last layer's stamps: every workgroup of each grid writes its entry
+    nr = int(np.count_nonzero(runs[0][1][0]))
+    ngu = int(np.count_nonzero(runs[0][2][0]))
+    ndn = int(np.count_nonzero(runs[0][2][4]))
+    bps = ngu // w.k
+    phases = {}
+
+    def put(name, vals):
+        phases.setdefault(name, []).append(vals)
+
+    for _, rr, dd in runs:
+        base = int(rr[0, :nr].min())
+        f = lambda a: (a.astype(np.int64) - base) * us_per_tick
+        R = [f(rr[i, :nr]) for i in range(2)]
+        G = [f(dd[i, :ngu]) for i in range(4)]
+        D = [f(dd[4 + i, :ndn]) for i in range(4)]
+        for name, a in (("router: start", R[0]), ("router: end", R[1]),
+                        ("gate/up: start", G[0]), ("gate/up: routing known", G[1]),
+                        ("gate/up: weight loads landed", G[2]), ("gate/up: end", G[3]),
+                        ("down: start", D[0]), ("down: routing read", D[1]),
+                        ("down: weight loads landed", D[2]), ("down: end", D[3])):
+            put(name, (a.min(), float(np.median(a)), a.max()))
+        for s in range(w.k):
+            sl = slice(s * bps, (s + 1) * bps)
+            put(f"slot {s}", (float(np.median(G[1][sl])), float(np.median(G[2][sl])), G[3][sl].max()))
+        put("gaps", (G[0].min() - R[1].max(), D[0].min() - G[3].max(), D[3].max()))
+
+    med = lambda name, i: statistics.median(v[i] for v in phases[name])
+    ev = statistics.median(t for t, _, _ in runs)
+    print(f"# Single-token chain timeline: decode40 (T=1, H={w.H}, E={w.E}, top-{w.k}, I={w.I}, sym8, x fp16)\n")
+    print("Command (from the repository root, on one MI355X):\n")
+    print("```\npython -m routed_expert_quantized_amd.build --stamps\n"
+          f"python -m routed_expert_quantized_amd.timeline --replays {args.replays} --layers {NL}\n```\n")
+    print(f"Timestamp build, {NL}-layer graph, {len(runs)} replays; the last layer of each replay, medians over "
+          f"replays. Counter {khz} kHz. Event time of this build: {ev:.2f} us per layer. Workgroups: router {nr}, "
+          f"gate/up {ngu} ({bps} per slot; the routing publisher is not stamped), down {ndn}.\n")
+    print("| phase (us from the first router start) | earliest workgroup | median | latest |")
+    print("|---|---|---|---|")
+    for name in ("router: start", "router: end", "gate/up: start", "gate/up: routing known",
+                 "gate/up: weight loads landed", "gate/up: end", "down: start", "down: routing read",
+                 "down: weight loads landed", "down: end"):
+        print(f"| {name} | {med(name, 0):.2f} | {med(name, 1):.2f} | {med(name, 2):.2f} |")
+    print("\n| gate/up slot | routing known (median) | loads landed (median) | end (latest) |")
+    print("|---|---|---|---|")
+    for s in range(w.k):
+        print(f"| {s} | {med(f'slot {s}', 0):.2f} | {med(f'slot {s}', 1):.2f} | {med(f'slot {s}', 2):.2f} |")
+    print(f"\nGaps: router end -> gate/up start {med('gaps', 0):.2f} us, gate/up end -> down start "
+          f"{med('gaps', 1):.2f} us; the layer's span {med('gaps', 2):.2f} us.")
+
+
+if __name__ == "__main__":
+    main()
