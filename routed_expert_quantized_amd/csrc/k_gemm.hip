@@ -35,8 +35,18 @@
 #include <utility>
 
 #include "kernels.hpp"
+#include "stamps.hpp"
 
 namespace moe {
+
+#ifdef MOE_STAMPS
+// Timestamp build only. Per kernel mode (0 gate/up, 1 down) of k_gemm_dma, the
+// waves' shader-clock cycles summed by phase: 0 DMA wait, 1 barrier, 2 issue
+// + compute, 3 whole wave, 4 number of waves, 5 pass set-up, 6 prologue
+// issue, 7 trailing wait, 8 epilogue, 9 tiles (from a tile's start to the end
+// of its last pass), 10 tile set-up.
+__device__ unsigned long long g_stamps_gemm[2][16];
+#endif
 
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
@@ -526,6 +536,8 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
   // XCDs, and tile (expert u, column block cb) has id (u/8)*8*ncb + cb*8 + u%8,
   // so all column blocks of an expert (which read the same activation rows)
   // run on one XCD, with the experts alternating over the XCDs.
+  MOE_STAMPS_ONLY(unsigned long long st_ph[11] = {}; const unsigned long long st_t0 = stamp_clock();
+                  unsigned long long st_tile = st_t0, st_x = st_t0;)
   const int nu = *n_uniq;
   const int ntiles = ncb * ((nu + 7) / 8 * 8);
   const int tid = (int)threadIdx.x, lane = tid & 63;
@@ -536,6 +548,7 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
     const int cb = rest % ncb;
     const int u = (rest / ncb) * 8 + (tile & 7);
     if (u >= nu) continue;
+    MOE_STAMPS_ONLY(st_tile = stamp_clock();)
     const int e = uniq[u], cnt = counts[e], beg = offsets[e];
     const int ew = expert_index(ex, e);  // -1: no slot, contributes nothing (index 0, zero scales)
     const bool resident = ew >= 0;  // a slot-less expert: zero scales, whatever slot 0 holds
@@ -579,6 +592,7 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
 
     for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
       const int nm = min(16 * MT, cnt - m0);
+      MOE_STAMPS_ONLY(st_x = stamp_clock(); if (m0 == 0) st_ph[10] += st_x - st_tile;)
       __syncthreads();
       for (int i = tid; i < 16 * MT; i += 256) fs[i] = i < nm ? perm[beg + m0 + i] : -1;
       if (MODE == 1 && tid < nsl) sg[tid] = sig[(int64_t)(beg + m0) * nsl + tid];
@@ -715,7 +729,9 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
       // stage with the last chunk again (clamped, cache-resident, never read) to
       // keep that count. A two-stage ring waits for everything in flight, so it
       // issues nothing past the last chunk.
+      MOE_STAMPS_ONLY(const unsigned long long st_p = stamp_clock(); st_ph[5] += st_p - st_x;)
       static_for<NS - 1>([&](auto R) { issue(min((int)decltype(R)::value, nchunks - 1), stage(R)); });
+      MOE_STAMPS_ONLY(st_ph[6] += stamp_clock() - st_p;)
       // chunk q lives in stage q % NS; the loop is unrolled NS times so that every
       // stage index is a constant
       for (int q0 = 0; q0 < nchunks; q0 += NS) {
@@ -723,14 +739,20 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
           constexpr int r = decltype(R)::value;
           const int q = q0 + r;
           if (q < nchunks) {
+            MOE_STAMPS_ONLY(const unsigned long long st_a = stamp_clock();)
             wait_vmcnt<(NS - 2) * D::NI>();
+            MOE_STAMPS_ONLY(const unsigned long long st_b = stamp_clock();)
             raw_barrier();  // chunk q is in LDS for every wave; chunk q-1's stage is free
+            MOE_STAMPS_ONLY(const unsigned long long st_c = stamp_clock();)
             if (NS > 2 || q + 1 < nchunks) issue(min(q + NS - 1, nchunks - 1), stage(ICg<(r + NS - 1) % NS>{}));
             compute(q, stage(R));  // ends with its LDS reads complete
+            MOE_STAMPS_ONLY(st_ph[0] += st_b - st_a; st_ph[1] += st_c - st_b; st_ph[2] += stamp_clock() - st_c;)
           }
         });
       }
+      MOE_STAMPS_ONLY(const unsigned long long st_w = stamp_clock();)
       wait_vmcnt<0>();  // the trailing refills land before the next pass reuses the stages
+      MOE_STAMPS_ONLY(st_x = stamp_clock(); st_ph[7] += st_x - st_w;)
       // epilogue: lane holds rows m = mt*16 + 4g + i of its two 16-column tiles, column r16
       if constexpr (MODE == 0) {
         // gate tile column n0 + 16*wave + r16 pairs with the same up tile column
@@ -752,6 +774,7 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
             const int m = mt * 16 + 4 * g + i;
             if (m < nm && n < lim) h16[(int64_t)fs[m] * I + n] = to_act16<MOE_F16>(ldexpf(hv[mt][i], -sigma));
           }
+        MOE_STAMPS_ONLY(st_ph[8] += stamp_clock() - st_x;)
       } else {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -767,9 +790,14 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
             }
           }
         }
+        MOE_STAMPS_ONLY(st_ph[8] += stamp_clock() - st_x;)
       }
     }
+    MOE_STAMPS_ONLY(st_ph[9] += stamp_clock() - st_tile;)
   }
+  MOE_STAMPS_ONLY(st_ph[3] = stamp_clock() - st_t0; st_ph[4] = 1; if (lane == 0) {
+    for (int i = 0; i < 11; ++i) atomicAdd(&g_stamps_gemm[MODE][i], st_ph[i]);
+  })
 }
 
 // Workgroups of a kernel that fit on the device at once (a multiple of 8).
@@ -857,3 +885,11 @@ hipError_t launch_gemm_grouped(const void* x, int xtype, int T, const ExpertsDev
 }
 
 }  // namespace moe
+
+#ifdef MOE_STAMPS
+MOE_STAMP_READER(moe_stamps_read_gemm, moe::g_stamps_gemm)
+extern "C" int moe_stamps_zero_gemm(void) {
+  static const unsigned long long zero[2][16] = {};
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(moe::g_stamps_gemm), zero, sizeof(zero));
+}
+#endif

@@ -15,6 +15,13 @@
 // MOE_STAMP_LANDED first waits, in wave 0, for every load that wave has in
 // flight, so it changes that wave's schedule: a timestamp build gives a
 // timeline of the chain, not kernel times.
+//
+// The grouped GEMM uses the same build differently: each wave sums the shader
+// clock (s_memtime, read between scheduling barriers so that no instruction
+// moves across a reading) spent in each phase of its tiles, and adds the sums
+// into a small table per kernel mode (moe_stamps_read_gemm,
+// moe_stamps_zero_gemm). MOE_STAMPS_ONLY(...) keeps its argument only in this
+// build.
 #pragma once
 
 namespace moe {
@@ -41,6 +48,15 @@ constexpr int kStampCols = 1024;
   extern "C" int fn(void* host) {                                                  \
     return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(table), sizeof(table));       \
   }
+#define MOE_STAMPS_ONLY(...) __VA_ARGS__
+namespace moe {
+__device__ __forceinline__ unsigned long long stamp_clock() {
+  __builtin_amdgcn_sched_barrier(0);
+  const unsigned long long t = __builtin_amdgcn_s_memtime();
+  __builtin_amdgcn_sched_barrier(0);
+  return t;
+}
+}  // namespace moe
 #else
 #define MOE_STAMP_TABLE(name, rows) static_assert(true, "")
 #define MOE_STAMP(table, row, bid) \
@@ -50,4 +66,5 @@ constexpr int kStampCols = 1024;
   do {                                    \
   } while (0)
 #define MOE_STAMP_READER(fn, table) static_assert(true, "")
+#define MOE_STAMPS_ONLY(...)
 #endif

@@ -9,9 +9,15 @@ workgroups run s+1 top-k rounds); and the gaps between kernels. The stamps
 that wait for loads change wave 0's schedule, so the chain under this build
 is somewhat slower than the plain library's; its event time is printed too.
 
+With --gemm WORKLOAD... it instead runs each workload's layer eagerly and
+prints how the grouped GEMM's waves spend their shader-clock cycles (DMA
+wait, barrier, issue + compute, pass set-up, ...), summed over every wave of
+the timed launches, for the gate/up and the down kernel.
+
 Build on any host with hipcc, then run from the repository root on one GPU:
     python -m routed_expert_quantized_amd.build --stamps
     python -m routed_expert_quantized_amd.timeline [--replays N]
+    python -m routed_expert_quantized_amd.timeline --gemm prefill8k prefill batched_int4
 """
 from __future__ import annotations
 
@@ -28,10 +34,64 @@ ROOT = os.path.dirname(PKG)
 COLS = 1024  # kStampCols
 
 
+# k_gemm_dma's phase sums (g_stamps_gemm columns)
+GEMM_PHASES = {"dma_wait": 0, "barrier": 1, "issue_compute": 2, "total": 3, "waves": 4, "pass_setup": 5,
+               "prologue": 6, "trailing_wait": 7, "epilogue": 8}
+
+
+def gemm_split(names, runs, rq, bench, synth, torch, L) -> None:
+    L.moe_stamps_read_gemm.argtypes = [ctypes.c_void_p]
+    print("# Grouped GEMM: where the waves' cycles go\n")
+    print("Command (from the repository root, on one MI355X):\n")
+    print("```\npython -m routed_expert_quantized_amd.build --stamps\n"
+          f"python -m routed_expert_quantized_amd.timeline --gemm {' '.join(names)} --runs {runs}\n```\n")
+    print(f"Timestamp build. Per workload: two layers, four warm-up calls, then {runs} calls of the layer whose "
+          "waves' shader-clock cycles are summed by phase over every wave of the gate/up and down launches "
+          "(fractions of the summed wave time). 'other' is the rest: tile set-up, the grid-stride loop and the "
+          "kernel's start and end.\n")
+    print("| workload | kernel | waves per launch | DMA wait | trailing wait | barrier | issue + compute | "
+          "pass set-up | prologue | epilogue | other |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for name in names:
+        w = synth.WORKLOADS[name]
+        pools, routers = bench.build_layers(w, 2, 0, rq, synth, torch)
+        xs = [bench.to_dev(synth.draw_step_x(w, 0, s), w.xtype, torch) for s in range(2)]
+        ws = rq.Workspace()
+        ws.get(rq.moe_workspace_bytes(w.T, w.E, w.H, w.I, w.k, w.scheme))
+        y = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+
+        def run(n):
+            for i in range(n):
+                rq.moe_layer_forward(xs[i % 2], routers[i % 2], pools[i % 2], w.k, rq.MOE_FLAG_RENORM, ws=ws,
+                                     out=y, return_routing=False)
+
+        run(4)
+        torch.cuda.synchronize()
+        if L.moe_stamps_zero_gemm() != 0:
+            raise SystemExit("clearing the GEMM stamps failed")
+        run(runs)
+        torch.cuda.synchronize()
+        g = np.zeros((2, 16), np.uint64)
+        if L.moe_stamps_read_gemm(g.ctypes.data) != 0:
+            raise SystemExit("reading the GEMM stamps failed")
+        for mode, kname in ((0, "gate/up"), (1, "down")):
+            v = {k: int(g[mode][i]) for k, i in GEMM_PHASES.items()}
+            tot = max(v["total"], 1)
+            parts = [v[k] for k in ("dma_wait", "trailing_wait", "barrier", "issue_compute", "pass_setup",
+                                    "prologue", "epilogue")]
+            other = tot - sum(parts)
+            cells = " | ".join(f"{100.0 * p / tot:.1f}%" for p in parts + [other])
+            print(f"| {name} | {kname} | {v['waves'] // runs} | {cells} |")
+        del pools, routers, ws
+        torch.cuda.empty_cache()
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--replays", type=int, default=8)
     ap.add_argument("--layers", type=int, default=40)
+    ap.add_argument("--gemm", nargs="+", default=None, metavar="WORKLOAD")
+    ap.add_argument("--runs", type=int, default=8)
     args = ap.parse_args()
     sys.path.insert(0, ROOT)
     import torch
@@ -43,6 +103,12 @@ def main() -> None:
     import bench
     import synth
     L = rq.lib()
+    if args.gemm:
+        for name in args.gemm:
+            if name not in synth.WORKLOADS or synth.WORKLOADS[name].T == 1:
+                raise SystemExit(f"--gemm takes workloads with more than one token, not {name}")
+        gemm_split(args.gemm, args.runs, rq, bench, synth, torch, L)
+        return
     for fn in (L.moe_stamps_read_route, L.moe_stamps_read_decode):
         fn.argtypes = [ctypes.c_void_p]
         fn.restype = ctypes.c_int
