@@ -181,7 +181,6 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_qlinear_lora_mfma(
   const int per = (nb + kLoraWaves - 1) / kLoraWaves;
   const int b0 = w * per, b1 = min(nb, b0 + per);
   float4_l acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
   for (int b = b0; b < b1; ++b) {
     const int k0 = 32 * b + 8 * g;
     const half8_l a = __builtin_bit_cast(half8_l, *reinterpret_cast<const uint4*>(xrow + k0));

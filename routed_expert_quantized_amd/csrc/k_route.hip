@@ -360,7 +360,6 @@ __global__ __launch_bounds__(1024) void k_logits_mfma(const void* __restrict__ x
 #pragma unroll
     for (int nt = 0; nt < NTT; ++nt) acc[mt][nt] = float4v_r{0.f, 0.f, 0.f, 0.f};
   const int kb = (blockIdx.z * nw + w) * kw;
-#pragma unroll 4
   for (int k = kb; k < kb + kw; k += 16) {
     float4 a[MTT], b[NTT];
 #pragma unroll
