@@ -176,6 +176,38 @@ def test_gather_parity_small(T, E, H, I, k, scheme, xtype, path):
     assert rel_norm_err(ys.cpu().numpy(), rys) <= Y_REL_NORM
 
 
+# One hot expert: slot 0 of every token routes to expert 0 and the other slots
+# spread over the rest, so one expert runs many GEMM passes with a ragged last
+# pass while the others run one short pass each. The three cases land in the
+# six-tile (sym8; int4 takes four-tile), four-tile and one-tile pass regimes.
+HOT = [(1100, 32, 2, 256, 128), (300, 40, 2, 256, 128), (64, 128, 4, 256, 192)]
+
+
+@pytest.mark.parametrize("T,E,k,H,I", HOT)
+@pytest.mark.parametrize("scheme", [rq.MOE_Q_SYM8, rq.MOE_Q_INT4])
+@pytest.mark.parametrize("xtype", [synth.F16, synth.BF16])
+def test_gemm_hot_expert(T, E, k, H, I, scheme, xtype):
+    say(f"hot expert T={T} E={E} k={k} H={H} I={I} scheme={scheme} xtype={xtype}")
+    g = np.random.default_rng(T + E + 3 * k + 10 * scheme + xtype)
+    wgu = (g.standard_normal((E, 2 * I, H)) * 0.02).astype(np.float32)
+    wd = (g.standard_normal((E, H, I)) * 0.02).astype(np.float32)
+    x = synth.encode_x(g.standard_normal((T, H)).astype(np.float32), xtype)
+    idx = np.zeros((T, k), np.int32)
+    for t in range(T):
+        idx[t, 1:] = 1 + (t * (k - 1) + np.arange(k - 1)) % (E - 1)
+    assert np.bincount(idx.ravel(), minlength=E)[0] == T
+    gate = g.random((T, k)).astype(np.float32)
+    ex = rq.quantize_experts(torch.from_numpy(wgu).cuda(), torch.from_numpy(wd).cuda(), scheme)
+    rex = oracle.quantize_experts(wgu, wd, scheme)
+    xd = to_dev_x(x, xtype)
+    bf16 = xtype == synth.BF16
+    fl = rq.MOE_FLAG_PATH_GEMM
+    y = rq.moe_gather_qmm_forward(xd, ex, torch.from_numpy(idx).cuda(), torch.from_numpy(gate).cuda(), flags=fl)
+    assert rel_norm_err(y.cpu().numpy(), oracle.gather_forward(x, rex, idx, gate, bf16=bf16)) <= Y_REL_NORM
+    ys = rq.moe_gather_qmm_forward(xd, ex, torch.from_numpy(idx).cuda(), None, flags=fl)
+    assert rel_norm_err(ys.cpu().numpy(), oracle.gather_forward(x, rex, idx, None, bf16=bf16)) <= Y_REL_NORM
+
+
 # ---------------------------------------------------------------- whole layer at the workloads' sizes
 # Every token is compared with the oracle, except at prefill8k (8192 tokens),
 # where the tokens are a stratified sample ("passes"): for every routed expert,
