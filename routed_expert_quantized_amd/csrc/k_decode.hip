@@ -536,15 +536,16 @@ __global__ __launch_bounds__(256) void k_down_grouped(ExpertsDev ex, int k, cons
 }
 
 // y[t][m] = sum over slots s, in order, of gate[t][s] * ys[t*k+s][m], with the
-// per-slot rows in fp32 (ys) or, with HALF, fp16 (ys16: the grouped GEMM's).
-// Four consecutive outputs of one token per thread; every slot's loads are
-// issued before the fused multiply-adds, which run in slot order (KMAX >= k).
-// With NT the fp32 rows are read non-temporally (rows larger than the cache
-// that would hold them).
+// per-slot rows in fp32 (ys) or, with HALF, as the grouped GEMM stores them:
+// fp16 (ys16) times 2^ysig[t*k+s][m/32], exact powers of two. Four
+// consecutive outputs of one token per thread; every slot's loads are issued
+// before the fused multiply-adds, which run in slot order (KMAX >= k). With NT
+// the fp32 rows are read non-temporally (rows larger than the cache that would
+// hold them).
 template <int KMAX, bool HALF, bool NT>
 __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const float* __restrict__ gate,
                                                  const float* __restrict__ ys, const uint16_t* __restrict__ ys16,
-                                                 float* __restrict__ y) {
+                                                 const int32_t* __restrict__ ysig, float* __restrict__ y) {
   const int nbx = (H / 4 + 255) / 256;
   const int t = blockIdx.x / nbx;
   const int m = ((blockIdx.x % nbx) * 256 + threadIdx.x) * 4;
@@ -557,8 +558,10 @@ __global__ __launch_bounds__(256) void k_combine(int T, int H, int k, const floa
     const int64_t off = ((int64_t)t * k + sc) * H + m;
     if constexpr (HALF) {
       const uint2 u = *reinterpret_cast<const uint2*>(ys16 + off);
+      const int e = ysig[((int64_t)t * k + sc) * (H / 32) + m / 32];
       const half2v lo = as_h2(u.x), hi = as_h2(u.y);
-      v[s] = make_float4((float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]);
+      v[s] = make_float4(ldexpf((float)lo[0], e), ldexpf((float)lo[1], e), ldexpf((float)hi[0], e),
+                         ldexpf((float)hi[1], e));
     } else if constexpr (NT) {
       typedef float f4v __attribute__((ext_vector_type(4)));
       const f4v q = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(ys + off));
@@ -808,17 +811,17 @@ hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsD
     else if (nbi <= 4) go(IC<4>{});
     else go(IC<8>{});
   });
-  if (gate) return launch_combine(T, ex.H, k, gate, ys, nullptr, y, s);
+  if (gate) return launch_combine(T, ex.H, k, gate, ys, nullptr, nullptr, y, s);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(int T, int H, int k, const float* gate, const float* ys, const uint16_t* ys16, float* y,
-                          hipStream_t s) {
+hipError_t launch_combine(int T, int H, int k, const float* gate, const float* ys, const uint16_t* ys16,
+                          const int32_t* ysig, float* y, hipStream_t s) {
   const dim3 cg((unsigned)((int64_t)T * ((H / 4 + 255) / 256)));
   auto go = [&](auto KM, auto HF, auto NTc) {
     constexpr int K_ = decltype(KM)::value;
     constexpr bool H_ = decltype(HF)::value != 0, N_ = decltype(NTc)::value != 0;
-    MOE_LAUNCH(MOE_KERNEL_COMBINE, (k_combine<K_, H_, N_>), cg, dim3(256), 0, s, T, H, k, gate, ys, ys16, y);
+    MOE_LAUNCH(MOE_KERNEL_COMBINE, (k_combine<K_, H_, N_>), cg, dim3(256), 0, s, T, H, k, gate, ys, ys16, ysig, y);
   };
   // Per-slot rows beyond the 256 MB last-level cache are read non-temporally:
   // measured faster there (8192 tokens, 537 MB) and slower below (2048, 134 MB).

@@ -110,11 +110,11 @@ hipError_t launch_decode_grouped(const void* x, int xtype, int T, const ExpertsD
                                  const GroupBufs& g, const float* gate, float* h, float* ys, float* y,
                                  hipStream_t s);
 
-// Gate-weighted combine y[t] = sum_s gate[t][s] * ys[t*k+s] (T > 1 paths).
-// y[t] = sum over slots s (in order) of gate[t][s] * ys[t][s], per-slot rows
-// fp32 (ys) or fp16 (ys16, when non-null).
-hipError_t launch_combine(int T, int H, int k, const float* gate, const float* ys, const uint16_t* ys16, float* y,
-                          hipStream_t s);
+// Gate-weighted combine (T > 1 paths): y[t] = sum over slots s, in order, of
+// gate[t][s] * ys[t*k+s], per-slot rows fp32 (ys) or, when ys16 is non-null,
+// fp16 rows times 2^ysig[t*k+s][m/32] (the grouped GEMM's).
+hipError_t launch_combine(int T, int H, int k, const float* gate, const float* ys, const uint16_t* ys16,
+                          const int32_t* ysig, float* y, hipStream_t s);
 
 // Grouped MFMA GEMM path (after launch_group), for fp16 or bf16 activations:
 // gate/up + SwiGLU into fp16 h [T*k][I] with one power-of-two exponent per tile

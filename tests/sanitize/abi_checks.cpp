@@ -42,7 +42,7 @@ hipError_t launch_remap_ids(const int32_t*, int64_t, const int32_t*, int, int32_
 hipError_t launch_stream_read(const void*, int64_t, hipStream_t) { launched("stream read"); }
 hipError_t launch_decode_grouped(const void*, int, int, const ExpertsDev&, int, const GroupBufs&, const float*, float*,
                                  float*, float*, hipStream_t) { launched("grouped decode"); }
-hipError_t launch_combine(int, int, int, const float*, const float*, const uint16_t*, float*, hipStream_t) {
+hipError_t launch_combine(int, int, int, const float*, const float*, const uint16_t*, const int32_t*, float*, hipStream_t) {
   launched("combine");
 }
 hipError_t launch_gemm_grouped(const void*, int, int, const ExpertsDev&, int, const GroupBufs&, const float*,
