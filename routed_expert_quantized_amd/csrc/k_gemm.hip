@@ -756,75 +756,95 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
       MOE_STAMPS_ONLY(const unsigned long long st_w = stamp_clock();)
       wait_vmcnt<0>();  // the trailing refills land before the next pass reuses the stages
       MOE_STAMPS_ONLY(st_x = stamp_clock(); st_ph[7] += st_x - st_w;)
-      // epilogue: lane holds rows m = mt*16 + 4g + i of its two 16-column tiles, column r16
+      // epilogue: lane holds rows m = mt*16 + 4g + i of its two 16-column tiles, column r16.
+      // A pass with all 16*MT rows and all of the workgroup's columns in range
+      // (the common case in large batches) takes a form without the row and
+      // column tests, which otherwise wrap every store in a branch.
+      const bool full = nm == 16 * MT && n0 + (MODE == 0 ? 64 : 128) <= lim;
       if constexpr (MODE == 0) {
         // gate tile column n0 + 16*wave + r16 pairs with the same up tile column
         const int n = n0 + wave * 16 + r16;
-        float hv[MT][4], amax = 0.0f;
+        auto epilogue = [&](auto FULLc) {
+          constexpr bool FULL = decltype(FULLc)::value;
+          float hv[MT][4], amax = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            hv[mt][i] = silu(acc[mt][0][i]) * acc[mt][1][i];
-            if (mt * 16 + 4 * g + i < nm && n < lim) amax = fmaxf(amax, fabsf(hv[mt][i]));
-          }
-        const int sigma = tile_sigma(workgroup_absmax(amax, red));
-        if (tid == 0) sig[(int64_t)(beg + m0) * nsl + cb] = sigma;
+            for (int i = 0; i < 4; ++i) {
+              hv[mt][i] = silu(acc[mt][0][i]) * acc[mt][1][i];
+              if (FULL || (mt * 16 + 4 * g + i < nm && n < lim)) amax = fmaxf(amax, fabsf(hv[mt][i]));
+            }
+          const int sigma = tile_sigma(workgroup_absmax(amax, red));
+          if (tid == 0) sig[(int64_t)(beg + m0) * nsl + cb] = sigma;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = mt * 16 + 4 * g + i;
-            if (m < nm && n < lim) h16[(int64_t)fs[m] * I + n] = to_act16<MOE_F16>(ldexpf(hv[mt][i], -sigma));
-          }
+            for (int i = 0; i < 4; ++i) {
+              const int m = mt * 16 + 4 * g + i;
+              if (FULL || (m < nm && n < lim))
+                h16[(int64_t)fs[m] * I + n] = to_act16<MOE_F16>(ldexpf(hv[mt][i], -sigma));
+            }
+        };
+        if (full) epilogue(std::true_type{});
+        else epilogue(std::false_type{});
         MOE_STAMPS_ONLY(st_ph[8] += stamp_clock() - st_x;)
       } else if constexpr (!OHALF) {
         // fp32 rows
+        auto epilogue = [&](auto FULLc) {
+          constexpr bool FULL = decltype(FULLc)::value;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+          for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = mt * 16 + 4 * g + i;
-            if (m >= nm) continue;
-            const int f = fs[m];
+            for (int i = 0; i < 4; ++i) {
+              const int m = mt * 16 + 4 * g + i;
+              if (!FULL && m >= nm) continue;
+              const int f = fs[m];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              const int n = n0 + wave * 32 + 16 * c + r16;
-              if (n < lim) ys[(int64_t)f * H + n] = acc[mt][c][i];
+              for (int c = 0; c < 2; ++c) {
+                const int n = n0 + wave * 32 + 16 * c + r16;
+                if (FULL || n < lim) ys[(int64_t)f * H + n] = acc[mt][c][i];
+              }
             }
           }
-        }
+        };
+        if (full) epilogue(std::true_type{});
+        else epilogue(std::false_type{});
         MOE_STAMPS_ONLY(st_ph[8] += stamp_clock() - st_x;)
       } else {
         // per-slot rows ahead of the combine, stored as h is: fp16 of
         // y * 2^-sigma, with the largest |y| of the wave's tile (the pass's
         // rows x its 32 columns) in [2^14, 2^15), and sigma for each of the
         // tile's rows at osig[f][n/32]
-        float amax = 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-              if (mt * 16 + 4 * g + i < nm && n0 + wave * 32 + 16 * c + r16 < lim)
-                amax = fmaxf(amax, fabsf(acc[mt][c][i]));
-        const int sigma = tile_sigma(wave_max(amax));
         const int nsl32 = (H + 31) / 32, sl32 = (n0 + wave * 32) / 32;
+        auto epilogue = [&](auto FULLc) {
+          constexpr bool FULL = decltype(FULLc)::value;
+          float amax = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = mt * 16 + 4 * g + i;
-            if (m >= nm) continue;
-            const int f = fs[m];
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              const int n = n0 + wave * 32 + 16 * c + r16;
-              if (n < lim) o16[(int64_t)f * H + n] = to_act16<MOE_F16>(ldexpf(acc[mt][c][i], -sigma));
+              for (int c = 0; c < 2; ++c)
+                if (FULL || (mt * 16 + 4 * g + i < nm && n0 + wave * 32 + 16 * c + r16 < lim))
+                  amax = fmaxf(amax, fabsf(acc[mt][c][i]));
+          const int sigma = tile_sigma(wave_max(amax));
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int m = mt * 16 + 4 * g + i;
+              if (!FULL && m >= nm) continue;
+              const int f = fs[m];
+#pragma unroll
+              for (int c = 0; c < 2; ++c) {
+                const int n = n0 + wave * 32 + 16 * c + r16;
+                if (FULL || n < lim) o16[(int64_t)f * H + n] = to_act16<MOE_F16>(ldexpf(acc[mt][c][i], -sigma));
+              }
             }
           }
-        }
+          return sigma;
+        };
+        const int sigma = full ? epilogue(std::true_type{}) : epilogue(std::false_type{});
         if (sl32 < nsl32)
           for (int m = lane; m < nm; m += 64) osig[(int64_t)fs[m] * nsl32 + sl32] = sigma;
         MOE_STAMPS_ONLY(st_ph[8] += stamp_clock() - st_x;)
