@@ -205,6 +205,19 @@ __device__ __forceinline__ void scaled_add(float4v& acc, float s, float4v p) {
   for (int i = 0; i < 4; ++i) acc[i] = fmaf(s, p[i], acc[i]);
 }
 
+// The same for the first NR of them (rows 4g + i, i < NR, of lane group g):
+// the others are rows past a one-tile pass's last assignment, never stored.
+// p is an MFMA result: with NR < 4 some of its registers are otherwise unused,
+// and the compiler may hand them to an inline-asm output (whose hazards it
+// does not check) while the MFMA is still writing them. The empty asm keeps
+// all four in use until after the first FMA, which waits for the MFMA.
+template <int NR>
+__device__ __forceinline__ void scaled_add_n(float4v& acc, float s, float4v p) {
+#pragma unroll
+  for (int i = 0; i < NR; ++i) acc[i] = fmaf(s, p[i], acc[i]);
+  if constexpr (NR < 4) asm volatile("" ::"v"(p), "v"(acc[0]));
+}
+
 // ---------------------------------------------------------------------------
 // Register-staged kernel, for rows with an odd number of 32-element blocks
 // (the DMA kernel below moves scales as 4-byte pairs).
@@ -645,7 +658,10 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
       // block is A, and every MFMA's fp32 partial is added times its row's
       // block scale. The next block's activation fragments are read while the
       // current block's MFMAs run.
-      auto compute = [&](int q, const uint8_t* Bst) {
+      // NR: how many of a lane's four rows per tile take the scale FMAs (4 but
+      // in one-tile passes of at most three assignments)
+      auto compute = [&](int q, const uint8_t* Bst, auto NRc) {
+        constexpr int NR = decltype(NRc)::value;
         uint32_t bb = lds_addr(Bst);
         // One-tile passes are bound by bytes in flight, so by occupancy: the
         // stage base is hidden from the optimiser, and each LDS address is
@@ -708,7 +724,8 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
           static_for<2 * MT>([&](auto J) {
             constexpr int j = decltype(J)::value;
             pp[j & 1] = M::run(a_operand<SCHEME, AT>(fa[b & 1][j / 2]), (j & 1) ? bc1 : bc0);
-            if constexpr (j > 0) scaled_add(acc[(j - 1) / 2][(j - 1) & 1], ((j - 1) & 1) ? s1 : s0, pp[(j - 1) & 1]);
+            if constexpr (j > 0)
+              scaled_add_n<NR>(acc[(j - 1) / 2][(j - 1) & 1], ((j - 1) & 1) ? s1 : s0, pp[(j - 1) & 1]);
             if constexpr (j == 0) {
               if (b + 1 < D::BPS) {
                 bn0 = codes8<SCHEME, AT>(cw0[b + 1]);
@@ -716,9 +733,9 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
               }
             }
             sched_group<kSchedMfma, 1>();
-            sched_group<kSchedValu, j == 0 ? 2 : 6>();
+            sched_group<kSchedValu, j == 0 ? 2 : 2 + NR>();
           });
-          scaled_add(acc[MT - 1][1], s1, pp[(2 * MT - 1) & 1]);
+          scaled_add_n<NR>(acc[MT - 1][1], s1, pp[(2 * MT - 1) & 1]);
           if (b + 1 < D::BPS) {
             bc0 = bn0;
             bc1 = bn1;
@@ -737,6 +754,7 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
       MOE_STAMPS_ONLY(st_ph[6] += stamp_clock() - st_p;)
       // chunk q lives in stage q % NS; the loop is unrolled NS times so that every
       // stage index is a constant
+      auto k_loop = [&](auto NRc) {
       for (int q0 = 0; q0 < nchunks; q0 += NS) {
         static_for<NS>([&](auto R) {
           constexpr int r = decltype(R)::value;
@@ -748,10 +766,24 @@ void k_gemm_dma(const uint16_t* __restrict__ act, ExpertsDev ex, int k, const in
             raw_barrier();  // chunk q is in LDS for every wave; chunk q-1's stage is free
             MOE_STAMPS_ONLY(const unsigned long long st_c = stamp_clock();)
             if (NS > 2 || q + 1 < nchunks) issue(min(q + NS - 1, nchunks - 1), stage(ICg<(r + NS - 1) % NS>{}));
-            compute(q, stage(R));  // ends with its LDS reads complete
+            compute(q, stage(R), NRc);  // ends with its LDS reads complete
             MOE_STAMPS_ONLY(st_ph[0] += st_b - st_a; st_ph[1] += st_c - st_b; st_ph[2] += stamp_clock() - st_c;)
           }
         });
+      }
+      };
+      // A one-tile pass of nm <= 3 assignments keeps rows 0 .. nm-1, all in lane
+      // group 0: only the first nm of a lane's four rows need the scale FMAs (a
+      // uniform branch per pass, outside the MFMA chain). Batched decode passes
+      // mostly hold one to three assignments. Gate/up only: the one-tile down
+      // GEMM waits on its loads, and the larger code made it slower.
+      if constexpr (MT == 1 && MODE == 0) {
+        if (nm == 1) k_loop(ICg<1>{});
+        else if (nm == 2) k_loop(ICg<2>{});
+        else if (nm == 3) k_loop(ICg<3>{});
+        else k_loop(ICg<4>{});
+      } else {
+        k_loop(ICg<4>{});
       }
       MOE_STAMPS_ONLY(const unsigned long long st_w = stamp_clock();)
       wait_vmcnt<0>();  // the trailing refills land before the next pass reuses the stages
