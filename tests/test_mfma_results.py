@@ -40,9 +40,12 @@ def mfma_result_writes(asm: str):
     """(function, mfma line, offending line) for every write into an MFMA result
     ahead of the result's first read, and the number of MFMAs checked."""
     bad, checked = [], 0
-    for fn in re.finditer(r"^(\S+):\s*$(.*?)^\.Lfunc_end", asm, re.M | re.S):
-        lines = [l.strip() for l in fn.group(2).splitlines()]
-        ins = [l for l in lines if l and not l.startswith((".", ";"))]
+    for chunk in asm.split(".Lfunc_end"):
+        names = re.findall(r"^([A-Za-z_][\w.$]*):", chunk, re.M)
+        name = names[0] if names else "?"
+        lines = [l.strip() for l in chunk.splitlines()]
+        # instructions only: no directives, comments or labels (which may carry a comment)
+        ins = [l for l in lines if l and not l.startswith((".", ";")) and not re.match(r"^[\w.$]+:", l)]
         for n, line in enumerate(ins):
             if not line.startswith("v_mfma"):
                 continue
@@ -64,7 +67,7 @@ def mfma_result_writes(asm: str):
                 if read & dst:
                     break  # the first use waits for the MFMA: its registers are complete from here
                 if written & dst:
-                    bad.append((fn.group(1), line, nxt))
+                    bad.append((name, line, nxt))
                     break
     return bad, checked
 
