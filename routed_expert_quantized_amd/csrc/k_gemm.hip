@@ -3,8 +3,10 @@
 // After the token-by-expert grouping each routed expert e has n_e assignments.
 // GEMM1: U_e[n_e][2I] = X_e[n_e][H] . W_gu[e]^T, then h = silu(gate) * up
 //        (gate columns n and up columns I + n in the same workgroup).
-// GEMM2: Y_e[n_e][H] = h_e[n_e][I] . W_d[e]^T, stored per assignment in fp32
-//        (ys, ahead of the combine; y itself in per-slot mode).
+// GEMM2: Y_e[n_e][H] = h_e[n_e][I] . W_d[e]^T, stored per assignment (ys,
+//        ahead of the combine) in fp32, or, where fp32 rows would exceed the
+//        256 MB last-level cache, in fp16 with a power of two per row and 32
+//        columns (as h below); in per-slot mode into y itself, in fp32.
 // Each expert's weights are read once per pass over its assignments
 // ("鳴かぬなら、カスタムカーネル、ほととぎす", section 4: only routed experts are read;
 // section 7: each slot's down projection takes that slot's own activation).
