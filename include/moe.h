@@ -77,7 +77,10 @@ enum {
    *       activations are the other operand as given (fp16 or bf16; fp32 x is
    *       MOE_ERR_UNSUPPORTED with this bit); h is held in fp16 with a
    *       power-of-two exponent per tile, so no intermediate overflows; the
-   *       per-slot outputs ahead of the combine are fp32. */
+   *       per-slot outputs ahead of the combine are fp32, or, where those fp32
+   *       rows (T*k*H*4 bytes) would exceed 256 MB, fp16 with a power-of-two
+   *       exponent per row and 32 columns (the per-slot output returned with
+   *       topk_gate == NULL is always fp32). */
   MOE_FLAG_PATH_GATHER = 2u,
   MOE_FLAG_PATH_GEMM = 4u,
   /* Single-token path only: keep h = silu(gate) * up in fp32 between the
